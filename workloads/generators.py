@@ -1,0 +1,211 @@
+"""Synthetic rollout batches shaped like the pages' workloads.
+
+The pages measure on the tau2 / tau^2-bench agent task (Qwen3-8B,
+n_samples 8, responses up to 8192 tokens, 32768 tokens per micro-batch) and
+on GRPO-style groups of samples per prompt.  Neither the data set nor the
+weights exist here, so these generators stand in for their *shapes*: token
+ids are uniform random, which means two rollouts share a prefix exactly
+where the generator makes them share one.
+
+Every generator is seeded and deterministic.  Batches come out in the
+padded tensor-dict form ``ids[B, S]`` int32 plus ``mask[B, S]`` uint8, real
+tokens left-aligned in each row.
+
+Configurations:
+  1  tiny: 2 prompts x 48 tokens, 4 responses each of U[16,64] tokens; in
+     prompt 0, response 3 repeats the first m tokens of response 0
+     (m ~ U[1, min(len0, len3) - 1]) and then differs.  V = 1000.
+     M = 512; 1 head, D = 64, fp32, forward only.
+  2  GRPO: 16 prompts U[256,1024] x 8 responses U[128,2048], V = 151936.
+     M = 8192; 32q/8kv heads, D = 128, bf16.
+  3  multi-turn agentic: one 2048-token system prefix common to every
+     sample; 4 prompt groups of 8 samples; for each of 4 turns a group of
+     two or more samples splits into two halves with probability 0.5 (each
+     half gets its own turn text), else the group shares one turn text;
+     turns are U[256,1024] tokens; then every sample ends with its own
+     response of U[256,8192] tokens.  M = 32768.
+  4a deep-shared: one 16384-token prefix + 64 leaves x 256 tokens, leaf
+     first tokens distinct.  M = 32768.
+  4b no sharing: 16 disjoint sequences x 2048 tokens, distinct first
+     tokens.  M = 32768.
+  5  sweep: the config-2 generator with b samples per prompt and
+     M = L in {8192, 16384, 32768, 65536}; ceil(4L / (640 + 1088 b))
+     prompts, i.e. about four full tries.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+VOCAB_BIG = 151936
+
+CONFIG_NAMES = {
+    "1": "tiny-fwd",
+    "2": "grpo-16x8",
+    "3": "multiturn-agentic",
+    "4a": "deep-shared-16k+64x256",
+    "4b": "no-sharing-16x2048",
+}
+
+
+@dataclass
+class Workload:
+    name: str
+    config: str
+    ids: np.ndarray          # int32 [B, S]
+    mask: np.ndarray         # uint8 [B, S]
+    max_tokens_per_mb: int
+    hq: int
+    hkv: int
+    d: int
+    dtype: str               # "fp32" | "bf16"
+    backward: bool
+    qkv_std: float
+    seed: int
+
+
+def pad_rows(seqs: list[np.ndarray], pad_id: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """Left-aligned padded batch of the given token rows."""
+    S = max(len(s) for s in seqs)
+    ids = np.full((len(seqs), S), pad_id, np.int32)
+    mask = np.zeros((len(seqs), S), np.uint8)
+    for r, s in enumerate(seqs):
+        ids[r, : len(s)] = s
+        mask[r, : len(s)] = 1
+    return ids, mask
+
+
+def _tok(rng, n, vocab):
+    return rng.integers(0, vocab, size=n, dtype=np.int64).astype(np.int32)
+
+
+def _cfg1(seed=1):
+    rng = np.random.default_rng(seed)
+    V = 1000
+    seqs = []
+    for p in range(2):
+        prompt = _tok(rng, 48, V)
+        resps = [_tok(rng, int(rng.integers(16, 65)), V) for _ in range(4)]
+        if p == 0:
+            r0, r3 = resps[0], resps[3]
+            m = int(rng.integers(1, min(len(r0), len(r3))))  # U[1, min-1]
+            r3[:m] = r0[:m]
+            if r3[m] == r0[m]:
+                r3[m] = (r0[m] + 1) % V
+        seqs += [np.concatenate([prompt, r]) for r in resps]
+    ids, mask = pad_rows(seqs)
+    return Workload("tiny-fwd", "1", ids, mask, 512, 1, 1, 64, "fp32", False, 1.0, seed)
+
+
+def _grpo(seed, n_prompts, n_samples, M, name, config):
+    rng = np.random.default_rng(seed)
+    seqs = []
+    for _ in range(n_prompts):
+        prompt = _tok(rng, int(rng.integers(256, 1025)), VOCAB_BIG)
+        for _ in range(n_samples):
+            seqs.append(np.concatenate([prompt, _tok(rng, int(rng.integers(128, 2049)), VOCAB_BIG)]))
+    ids, mask = pad_rows(seqs)
+    return Workload(name, config, ids, mask, M, 32, 8, 128, "bf16", True, 1.0 / math.sqrt(128), seed)
+
+
+def _cfg3(seed=3):
+    rng = np.random.default_rng(seed)
+    system = _tok(rng, 2048, VOCAB_BIG)
+    seqs = []
+    for _ in range(4):
+        # each group: (member sample indices, shared token parts so far)
+        groups = [(list(range(8)), [system])]
+        for _turn in range(4):
+            nxt = []
+            for members, parts in groups:
+                if len(members) >= 2 and rng.random() < 0.5:
+                    h = len(members) // 2
+                    for half in (members[:h], members[h:]):
+                        nxt.append((half, parts + [_tok(rng, int(rng.integers(256, 1025)), VOCAB_BIG)]))
+                else:
+                    nxt.append((members, parts + [_tok(rng, int(rng.integers(256, 1025)), VOCAB_BIG)]))
+            groups = nxt
+        for members, parts in groups:
+            for _m in members:
+                seqs.append(np.concatenate(parts + [_tok(rng, int(rng.integers(256, 8193)), VOCAB_BIG)]))
+    ids, mask = pad_rows(seqs)
+    return Workload("multiturn-agentic", "3", ids, mask, 32768, 32, 8, 128, "bf16", True,
+                    1.0 / math.sqrt(128), seed)
+
+
+def _cfg4a(seed=4):
+    rng = np.random.default_rng(seed)
+    prefix = _tok(rng, 16384, VOCAB_BIG)
+    firsts = rng.choice(VOCAB_BIG, size=64, replace=False).astype(np.int32)
+    seqs = []
+    for f in firsts:
+        leaf = _tok(rng, 256, VOCAB_BIG)
+        leaf[0] = f
+        seqs.append(np.concatenate([prefix, leaf]))
+    ids, mask = pad_rows(seqs)
+    return Workload("deep-shared-16k+64x256", "4a", ids, mask, 32768, 32, 8, 128, "bf16", True,
+                    1.0 / math.sqrt(128), seed)
+
+
+def _cfg4b(seed=41):
+    rng = np.random.default_rng(seed)
+    firsts = rng.choice(VOCAB_BIG, size=16, replace=False).astype(np.int32)
+    seqs = []
+    for f in firsts:
+        s = _tok(rng, 2048, VOCAB_BIG)
+        s[0] = f
+        seqs.append(s)
+    ids, mask = pad_rows(seqs)
+    return Workload("no-sharing-16x2048", "4b", ids, mask, 32768, 32, 8, 128, "bf16", True,
+                    1.0 / math.sqrt(128), seed)
+
+
+def make_workload(config: str) -> Workload:
+    """Token batch of one named configuration ("1", "2", "3", "4a", "4b")."""
+    config = str(config)
+    if config == "1":
+        return _cfg1()
+    if config == "2":
+        return _grpo(2, 16, 8, 8192, "grpo-16x8", "2")
+    if config == "3":
+        return _cfg3()
+    if config == "4a":
+        return _cfg4a()
+    if config == "4b":
+        return _cfg4b()
+    raise ValueError(f"unknown config {config!r}")
+
+
+def sweep_workload(L: int, b: int) -> Workload:
+    """Config-5 point: GRPO generator, b samples per prompt, budget M = L."""
+    n_prompts = math.ceil(4 * L / (640 + 1088 * b))
+    seed = 5_000_000 + L * 10 + b
+    w = _grpo(seed, n_prompts, b, L, f"sweep-L{L}-b{b}", "5")
+    return w
+
+
+def worked_example():
+    """The pages' packing figure: Seq0 [A,B,C,D], Seq1 [A,B,E,F],
+    Seq2 [A,G,H], with A..H encoded as ids 1..8 (0 is the pad id)."""
+    A, B, C, D, E, F, G, H = range(1, 9)
+    return pad_rows([np.array(s, np.int32) for s in ([A, B, C, D], [A, B, E, F], [A, G, H])])
+
+
+def attention_inputs(L: int, hq: int, hkv: int, d: int, dtype: str, std: float, seed: int,
+                     backward: bool = True):
+    """Q, K, V (and dO) for one packed trie of length L, drawn in fp32 from a
+    seeded ``torch.Generator`` on the CPU and rounded to the kernel dtype:
+    Q [L,hq,d], K/V [L,hkv,d] ~ N(0,1)*std, dO [L,hq,d] ~ N(0,1).
+    Returns CPU torch tensors of dtype bf16 or fp32."""
+    import torch
+
+    g = torch.Generator().manual_seed(int(seed))
+    tdt = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
+    q = (torch.randn(L, hq, d, generator=g) * std).to(tdt)
+    k = (torch.randn(L, hkv, d, generator=g) * std).to(tdt)
+    v = (torch.randn(L, hkv, d, generator=g) * std).to(tdt)
+    do = torch.randn(L, hq, d, generator=g).to(tdt) if backward else None
+    return q, k, v, do
