@@ -1,0 +1,189 @@
+/*
+ * tree_attn.h -- C ABI of the MI355X (gfx950) trie-packed tree-attention
+ * library (libtreeattn.so).
+ *
+ * The problem (sources: the AReaL tree-training guide, "AReaL Tree Training
+ * 完全指南" on 2kiu.com, sections 树构建流程 / 核心数据结构 / 打包数据的生成 /
+ * 两种注意力实现; and the AREAL-DTA paper notes, §3 问题形式化):
+ * rollout sequences that share prefixes are packed into compressed prefix
+ * tries, flattened in pre-order, so each shared token is stored and computed
+ * once.  Each token attends to itself and its ancestors only; its position
+ * id is its ancestor count.  Gradients of a shared prefix are the sum over
+ * every sequence through it.
+ *
+ * Conventions for every entry point:
+ *   - Return 0 on success or a negative TREE_E_* code; the message of the
+ *     last failure on the calling thread is in tree_last_error().  No C++
+ *     exception crosses this boundary.
+ *   - Pointers named d_* and the tensors q/k/v/o/lse/dout/dq/dk/dv are DEVICE
+ *     pointers owned by the caller.  The library never allocates device
+ *     memory; it reports workspace sizes and the caller passes workspaces in.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Device work is enqueued on it; no call synchronises.  Faults inside a
+ *     kernel surface at the caller's next synchronisation of that stream.
+ *   - Layouts: one packed trie of L tokens (L a multiple of 128) is a batch
+ *     of one.  Q, O, dQ, dO are [L, Hq, D] contiguous; K, V, dK, dV are
+ *     [L, Hkv, D]; LSE is [Hq, L] float32 (natural log).  dtype is
+ *     TREE_DTYPE_BF16 (bf16 tensors, fp32 accumulation; D = 64 or 128) or
+ *     TREE_DTYPE_FP32 (fp32 tensors, a slow check mode; D <= 128).  Query
+ *     head h reads key/value head h / (Hq / Hkv).
+ */
+#ifndef TREE_ATTN_H
+#define TREE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TREE_ATTN_ABI_VERSION 1
+
+/* status codes */
+#define TREE_OK 0
+#define TREE_E_MAX_TOKENS (-1)   /* max_tokens_per_mb <= 0 */
+#define TREE_E_ALIGN (-2)        /* max_tokens_per_mb not a multiple of block_size */
+#define TREE_E_SEQ_TOO_LONG (-3) /* a sequence longer than max_tokens_per_mb */
+#define TREE_E_EMPTY_SEQ (-4)    /* a row with no real token */
+#define TREE_E_ARG (-5)          /* null pointer, bad size, dims, head ratio or dtype */
+#define TREE_E_WORKSPACE (-6)    /* workspace smaller than the reported size */
+#define TREE_E_HIP (-7)          /* a HIP launch or runtime call failed */
+#define TREE_E_NOMEM (-8)        /* host allocation failed */
+
+#define TREE_DTYPE_BF16 0
+#define TREE_DTYPE_FP32 1
+
+/* Block size of the tile grid and of the padding (the guide's BlockMask
+ * block, section 两种注意力实现). */
+#define TREE_BLOCK 128
+
+/* Version of this ABI (TREE_ATTN_ABI_VERSION). */
+int tree_abi_version(void);
+
+/* Message of the last failed call on this thread ("" if none).  The string
+ * belongs to the library and stays valid until the thread's next call. */
+const char* tree_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Host packer.  Guide, sections 参数背后的源码校验逻辑 (validation),
+ * 树构建流程 steps 1-3 (extraction, first-fit-decreasing insertion, chain
+ * compression) and 核心数据结构 / 打包数据的生成 (pre-order layout with
+ * inclusive node ranges, position ids, tree_token_ratio).
+ * ---------------------------------------------------------------------- */
+typedef struct tree_pack tree_pack_t; /* opaque, owned by the library */
+
+/* Read-only view of one packed trie.  Every pointer belongs to the
+ * tree_pack_t it came from and stays valid until tree_pack_free(). */
+typedef struct {
+    int64_t n_tokens;            /* real (stored) tokens n                      */
+    int64_t L;                   /* padded length, multiple of block_size       */
+    int64_t n_nodes;             /* compressed nodes                            */
+    int64_t n_seqs;              /* sequences in this trie                      */
+    const int32_t* token_ids;    /* [L]  pads = pad_id                          */
+    const int32_t* node_id;      /* [L]  pre-order node index, -1 for pads      */
+    const int32_t* subtree_end;  /* [L]  inclusive last index of the token's
+                                         node's subtree, -1 for pads            */
+    const int32_t* node_start;   /* [n_nodes] first token index                 */
+    const int32_t* node_end;     /* [n_nodes] last token index (inclusive)      */
+    const int32_t* node_parent;  /* [n_nodes] parent node, -1 under the root    */
+    const int32_t* seq_ids;      /* [n_seqs] batch rows, insertion order        */
+    const int32_t* seq_iv_ptr;   /* [n_seqs+1] CSR offsets into seq_iv          */
+    const int32_t* seq_iv;       /* [2*seq_iv_ptr[n_seqs]] (start,end) pairs:
+                                    the nodes each sequence passes, root first  */
+} tree_trie_view;
+
+typedef struct {
+    int64_t n_tries;
+    int64_t original_tokens;     /* sum of the attention mask                   */
+    int64_t tree_tokens;         /* sum of n_tokens over tries                  */
+    double tree_token_ratio;     /* tree_tokens / original_tokens (guide,
+                                    section 指标与监控)                          */
+    int64_t n_pairs;             /* visible (query,key) pairs, all tries        */
+    int64_t unpacked_pairs;      /* sum over sequences of l*(l+1)/2             */
+} tree_pack_stats_t;
+
+/* Pack a padded batch.  ids [B,S] int32 and mask [B,S] uint8 are HOST
+ * row-major arrays; row r's sequence is ids[r][c] for every c with
+ * mask[r][c] != 0, in column order.  Sequences are sorted by length,
+ * longest first (ties keep row order), and each goes into the first trie
+ * (in creation order) whose uncompressed token count plus what it adds
+ * stays <= max_tokens_per_mb; otherwise a new trie is opened.  Single-child
+ * chains carrying the same sequences are merged; nodes are laid out in
+ * pre-order with children in insertion order; each trie is padded to
+ * round_up(n, block_size), or to max_tokens_per_mb if pad_to_maximum != 0,
+ * with pad_id.  block_size must be 128.  On success *out owns the result
+ * (free with tree_pack_free).  Errors: TREE_E_MAX_TOKENS, TREE_E_ALIGN,
+ * TREE_E_EMPTY_SEQ, TREE_E_SEQ_TOO_LONG (rows checked in order, empty
+ * before too long), TREE_E_ARG, TREE_E_NOMEM; *out is then NULL. */
+int tree_pack(const int32_t* ids, const uint8_t* mask, int64_t B, int64_t S,
+              int64_t max_tokens_per_mb, int32_t block_size, int32_t pad_to_maximum,
+              int32_t pad_id, tree_pack_t** out);
+
+/* Number of tries, or -1 if p is NULL. */
+int64_t tree_pack_num_tries(const tree_pack_t* p);
+
+/* Fill *v with a view of trie t (0 <= t < num_tries); TREE_E_ARG otherwise. */
+int tree_pack_trie(const tree_pack_t* p, int64_t t, tree_trie_view* v);
+
+/* Accounting of the whole pack (guide, section 指标与监控). */
+int tree_pack_stats(const tree_pack_t* p, tree_pack_stats_t* s);
+
+/* Release a pack (NULL is a no-op). */
+void tree_pack_free(tree_pack_t* p);
+
+/* ------------------------------------------------------------------------
+ * Metadata (device).  Guide, section 打包数据的生成: a token's position id is
+ * the number of tokens it may attend to, minus one; the block mask of
+ * section 两种注意力实现 is built here as a per-128x128-tile class computed
+ * from subtree intervals: key j is visible to query i iff j <= i <= se[j].
+ * ---------------------------------------------------------------------- */
+
+/* Bytes of device workspace tree_meta needs for a trie of length L. */
+size_t tree_meta_workspace_bytes(int64_t L);
+
+/* From d_se[L] (the trie's subtree_end, copied to the device; real tokens
+ * first, pads -1 after them) compute:
+ *   d_pos[L]          int32 position ids, pads 0;
+ *   d_tile_class[nb*nb] uint8, nb = L/128, row-major [query block][key
+ *                     block]: 0 empty, 1 partial, 2 full;
+ *   d_ws              the attention kernels' tile lists (row- and
+ *                     column-wise nonempty tiles, heaviest-first orders).
+ * d_ws must hold tree_meta_workspace_bytes(L) bytes and stay untouched
+ * until the attention calls that use it have run.  L % 128 != 0 or
+ * L > 2^20 gives TREE_E_ARG. */
+int tree_meta(const int32_t* d_se, int64_t L, int32_t* d_pos, uint8_t* d_tile_class,
+              void* d_ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Attention (device).  Forward: for query head h and token i,
+ *   O_i = softmax_j(scale * q_i . k_j) v_j over j in A(i) = {j : j <= i <= se[j]},
+ *   LSE_i = ln sum_{j in A(i)} exp(scale * q_i . k_j);
+ * rows with no visible key (pads) get O = 0 and LSE = -inf.  Tiles the
+ * metadata marks empty are skipped.  d_se and d_meta_ws are the inputs and
+ * the workspace of the tree_meta call for this trie.
+ * ---------------------------------------------------------------------- */
+int tree_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int32_t* d_se, const void* d_meta_ws, int64_t L, int32_t Hq,
+                  int32_t Hkv, int32_t D, float scale, int32_t dtype, void* stream);
+
+/* Bytes of device workspace tree_attn_bwd needs. */
+size_t tree_attn_bwd_workspace_bytes(int64_t L, int32_t Hq, int32_t D, int32_t dtype);
+
+/* Backward of tree_attn_fwd (AREAL-DTA notes, §3 问题形式化: a shared
+ * prefix's gradient is accumulated over every sequence through it, which
+ * holds here because a shared token is one row of the packed problem).
+ * Inputs q, k, v, o, lse (from tree_attn_fwd) and dout; outputs dq [L,Hq,D],
+ * dk, dv [L,Hkv,D] in the tensor dtype, fully overwritten (pads get 0).
+ * dk/dv of a key/value head sum over its query heads.  d_ws must hold
+ * tree_attn_bwd_workspace_bytes() bytes. */
+int tree_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                  const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                  const int32_t* d_se, const void* d_meta_ws, void* d_ws, size_t ws_bytes,
+                  int64_t L, int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                  int32_t dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TREE_ATTN_H */

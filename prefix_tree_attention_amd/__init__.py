@@ -1,0 +1,22 @@
+"""Trie-packed tree attention for AMD MI355X (gfx950).
+
+Rollout sequences that share prefixes are packed into compressed prefix
+tries (host C++ packer), per-token metadata and 128x128 tile classes are
+derived on the GPU, and forward / backward attention run in hand-written
+HIP kernels with bf16 MFMA.  Everything sits behind the C ABI of
+``include/tree_attn.h`` (libtreeattn.so); this package only marshals
+arguments into it.
+"""
+
+from ._lib import TreeAttnError, lib, library_path, DTYPE_BF16, DTYPE_FP32, BLOCK  # noqa: F401
+from .api import (  # noqa: F401
+    PackedTrie,
+    TreeMeta,
+    pack,
+    tree_meta,
+    meta_workspace_bytes,
+    bwd_workspace_bytes,
+    attn_fwd,
+    attn_bwd,
+    tree_attention,
+)

@@ -1,0 +1,224 @@
+"""Python face of libtreeattn: argument marshalling only.
+
+Every step of the path -- packing, metadata, forward, backward -- runs in the
+library (C++ on the host for the packer, HIP kernels on the GPU for the
+rest).  PyTorch provides device memory and the current stream."""
+
+from __future__ import annotations
+
+import ctypes
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+from ._lib import (BLOCK, DTYPE_BF16, DTYPE_FP32, PackStats, TrieView, TreeAttnError, check, lib)
+
+
+# ---------------------------------------------------------------------------
+# packer (host)
+# ---------------------------------------------------------------------------
+@dataclass
+class PackedTrie:
+    """One packed trie, copied out of the library's pack."""
+    n_tokens: int
+    L: int
+    token_ids: np.ndarray
+    node_id: np.ndarray
+    subtree_end: np.ndarray
+    node_start: np.ndarray
+    node_end: np.ndarray
+    node_parent: np.ndarray
+    seq_ids: np.ndarray
+    seq_iv_ptr: np.ndarray
+    seq_iv: np.ndarray  # [k, 2]
+
+    @property
+    def n_nodes(self) -> int:
+        return int(self.node_start.shape[0])
+
+    def sequence_indices(self, k: int) -> np.ndarray:
+        a, b = int(self.seq_iv_ptr[k]), int(self.seq_iv_ptr[k + 1])
+        return np.concatenate([np.arange(s, e + 1) for s, e in self.seq_iv[a:b]])
+
+
+def _arr(ptr, n) -> np.ndarray:
+    if n == 0:
+        return np.zeros(0, np.int32)
+    return np.ctypeslib.as_array(ptr, shape=(int(n),)).copy()
+
+
+def pack(ids, mask, max_tokens_per_mb: int, block_size: int = BLOCK, pad_to_maximum: bool = False,
+         pad_id: int = 0):
+    """Pack a padded [B, S] batch into tries (``tree_pack``).  Returns
+    ``(tries, stats)`` with ``stats`` a dict of the pack's accounting."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    if ids.ndim != 2 or ids.shape != mask.shape:
+        raise TreeAttnError(-5, "ids and mask must both be [B, S]")
+    L = lib()
+    h = ctypes.c_void_p()
+    check(L.tree_pack(ids.ctypes.data, mask.ctypes.data, ids.shape[0], ids.shape[1], int(max_tokens_per_mb),
+                      int(block_size), int(bool(pad_to_maximum)), int(pad_id), ctypes.byref(h)))
+    try:
+        tries = []
+        for t in range(L.tree_pack_num_tries(h)):
+            v = TrieView()
+            check(L.tree_pack_trie(h, t, ctypes.byref(v)))
+            n_iv = int(_arr(v.seq_iv_ptr, v.n_seqs + 1)[-1])
+            tries.append(PackedTrie(
+                n_tokens=int(v.n_tokens), L=int(v.L),
+                token_ids=_arr(v.token_ids, v.L), node_id=_arr(v.node_id, v.L),
+                subtree_end=_arr(v.subtree_end, v.L), node_start=_arr(v.node_start, v.n_nodes),
+                node_end=_arr(v.node_end, v.n_nodes), node_parent=_arr(v.node_parent, v.n_nodes),
+                seq_ids=_arr(v.seq_ids, v.n_seqs), seq_iv_ptr=_arr(v.seq_iv_ptr, v.n_seqs + 1),
+                seq_iv=_arr(v.seq_iv, 2 * n_iv).reshape(-1, 2)))
+        s = PackStats()
+        check(L.tree_pack_stats(h, ctypes.byref(s)))
+        stats = {k: getattr(s, k) for k, _ in PackStats._fields_}
+    finally:
+        L.tree_pack_free(h)
+    return tries, stats
+
+
+# ---------------------------------------------------------------------------
+# device side
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def meta_workspace_bytes(L: int) -> int:
+    return int(lib().tree_meta_workspace_bytes(int(L)))
+
+
+def bwd_workspace_bytes(L: int, hq: int, d: int, dtype: int = DTYPE_BF16) -> int:
+    return int(lib().tree_attn_bwd_workspace_bytes(int(L), int(hq), int(d), int(dtype)))
+
+
+@dataclass
+class TreeMeta:
+    """Device metadata of one trie (the library's analogue of the guide's
+    TreeAttentionMeta.from_trie): subtree ends, position ids, tile classes
+    and the attention kernels' tile lists."""
+    L: int
+    se: "object"          # int32 [L] device
+    pos: "object"         # int32 [L] device
+    tile_class: "object"  # uint8 [nb, nb] device
+    ws: "object"          # uint8 workspace device
+
+
+def tree_meta(subtree_end, device=None) -> TreeMeta:
+    """Run ``tree_meta`` on a trie's subtree ends (numpy array or device
+    tensor)."""
+    torch = _torch()
+    device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    se = torch.as_tensor(np.asarray(subtree_end, np.int32) if not torch.is_tensor(subtree_end) else subtree_end)
+    se = se.to(device=device, dtype=torch.int32).contiguous()
+    L = int(se.numel())
+    nb = L // BLOCK
+    pos = torch.empty(L, dtype=torch.int32, device=device)
+    tc = torch.empty((nb, nb), dtype=torch.uint8, device=device)
+    nbytes = meta_workspace_bytes(L)
+    if nbytes == 0:
+        raise TreeAttnError(-5, f"bad packed length {L}")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    check(lib().tree_meta(_ptr(se), L, _ptr(pos), _ptr(tc), _ptr(ws), nbytes, _stream(device)))
+    return TreeMeta(L, se, pos, tc, ws)
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_FP32
+    raise TreeAttnError(-5, f"unsupported dtype {t.dtype}")
+
+
+def _check_qkv(q, k, v, meta):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise TreeAttnError(-5, f"{name} must be a contiguous device tensor")
+        if t.dim() != 3 or t.shape[0] != meta.L:
+            raise TreeAttnError(-5, f"{name} must be [L={meta.L}, H, D], got {tuple(t.shape)}")
+    if k.shape != v.shape or q.shape[2] != k.shape[2] or q.dtype != k.dtype or q.dtype != v.dtype:
+        raise TreeAttnError(-5, "q/k/v shapes or dtypes disagree")
+
+
+def attn_fwd(q, k, v, meta: TreeMeta, scale: float | None = None):
+    """``tree_attn_fwd``: returns (o [L,Hq,D], lse [Hq,L] fp32)."""
+    torch = _torch()
+    _check_qkv(q, k, v, meta)
+    L, hq, d = q.shape
+    hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q)
+    lse = torch.empty((hq, L), dtype=torch.float32, device=q.device)
+    check(lib().tree_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(meta.se), _ptr(meta.ws), L, hq,
+                              hkv, d, scale, _dtype_code(q), _stream(q.device)))
+    return o, lse
+
+
+def attn_bwd(q, k, v, o, lse, do, meta: TreeMeta, scale: float | None = None, workspace=None):
+    """``tree_attn_bwd``: returns (dq, dk, dv)."""
+    torch = _torch()
+    _check_qkv(q, k, v, meta)
+    for name, t in (("o", o), ("do", do)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise TreeAttnError(-5, f"{name} must match q")
+    L, hq, d = q.shape
+    hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    code = _dtype_code(q)
+    nbytes = bwd_workspace_bytes(L, hq, d, code)
+    ws = workspace if workspace is not None else torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    check(lib().tree_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse.contiguous()), _ptr(do), _ptr(dq),
+                              _ptr(dk), _ptr(dv), _ptr(meta.se), _ptr(meta.ws), _ptr(ws), ws.numel(), L, hq, hkv,
+                              d, scale, code, _stream(q.device)))
+    return dq, dk, dv
+
+
+def _autograd_fn():
+    torch = _torch()
+
+    class TreeAttentionFn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, meta, scale):
+            o, lse = attn_fwd(q, k, v, meta, scale)
+            ctx.save_for_backward(q, k, v, o, lse)
+            ctx.meta, ctx.scale = meta, scale
+            return o
+
+        @staticmethod
+        def backward(ctx, do):
+            q, k, v, o, lse = ctx.saved_tensors
+            dq, dk, dv = attn_bwd(q, k, v, o, lse, do.contiguous(), ctx.meta, ctx.scale)
+            return dq, dk, dv, None, None
+
+    return TreeAttentionFn
+
+
+_FN = None
+
+
+def tree_attention(q, k, v, meta: TreeMeta, scale: float | None = None):
+    """Differentiable tree attention over one packed trie (batch 1):
+    q [L,Hq,D], k/v [L,Hkv,D] -> o [L,Hq,D]."""
+    global _FN
+    if _FN is None:
+        _FN = _autograd_fn()
+    return _FN.apply(q, k, v, meta, scale)

@@ -1,0 +1,152 @@
+// C ABI of libtreeattn: error state, argument validation and dispatch to the
+// device launchers.  See include/tree_attn.h for the contract.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "device.h"
+#include "status.h"
+
+namespace treeattn {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+int set_error(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_L(int64_t L, const char* fn) {
+    if (L <= 0 || L % kBlock != 0 || L > kMaxL)
+        return set_error(TREE_E_ARG, "%s: L=%lld must be a positive multiple of %d and <= %lld", fn,
+                         (long long)L, kBlock, (long long)kMaxL);
+    return TREE_OK;
+}
+
+int check_attn(const char* fn, int64_t L, int32_t Hq, int32_t Hkv, int32_t D, float scale, int32_t dtype) {
+    if (int rc = check_L(L, fn)) return rc;
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Hq > 4096)
+        return set_error(TREE_E_ARG, "%s: bad head counts Hq=%d Hkv=%d (need Hq %% Hkv == 0)", fn, Hq, Hkv);
+    if (dtype == TREE_DTYPE_BF16) {
+        if (D != 64 && D != 128) return set_error(TREE_E_ARG, "%s: bf16 path supports D in {64,128}, got %d", fn, D);
+    } else if (dtype == TREE_DTYPE_FP32) {
+        if (D != 32 && D != 64 && D != 128)
+            return set_error(TREE_E_ARG, "%s: fp32 path supports D in {32,64,128}, got %d", fn, D);
+    } else {
+        return set_error(TREE_E_ARG, "%s: unknown dtype %d", fn, dtype);
+    }
+    if (!std::isfinite(scale)) return set_error(TREE_E_ARG, "%s: scale must be finite", fn);
+    return TREE_OK;
+}
+
+int hip_status(hipError_t e, const char* fn) {
+    if (e != hipSuccess) return set_error(TREE_E_HIP, "%s: HIP error %d (%s)", fn, int(e), hipGetErrorString(e));
+    clear_error();
+    return TREE_OK;
+}
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+}  // namespace
+}  // namespace treeattn
+
+using namespace treeattn;
+
+extern "C" {
+
+int tree_abi_version(void) { return TREE_ATTN_ABI_VERSION; }
+
+const char* tree_last_error(void) { return g_last_error.c_str(); }
+
+size_t tree_meta_workspace_bytes(int64_t L) {
+    if (L <= 0 || L % kBlock != 0 || L > kMaxL) return 0;
+    return size_t(meta_layout(L).words) * sizeof(int32_t);
+}
+
+int tree_meta(const int32_t* d_se, int64_t L, int32_t* d_pos, uint8_t* d_tile_class, void* d_ws,
+              size_t ws_bytes, void* stream) {
+    if (int rc = check_L(L, "tree_meta")) return rc;
+    if (!d_se || !d_pos || !d_tile_class || !d_ws) return set_error(TREE_E_ARG, "tree_meta: NULL device pointer");
+    if (!aligned16(d_se) || !aligned16(d_ws))
+        return set_error(TREE_E_ARG, "tree_meta: d_se and d_ws must be 16-byte aligned");
+    if (ws_bytes < tree_meta_workspace_bytes(L))
+        return set_error(TREE_E_WORKSPACE, "tree_meta: workspace %zu < %zu bytes", ws_bytes,
+                         tree_meta_workspace_bytes(L));
+    return hip_status(launch_meta(d_se, L, d_pos, d_tile_class, d_ws, static_cast<hipStream_t>(stream)),
+                      "tree_meta");
+}
+
+int tree_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* d_se,
+                  const void* d_meta_ws, int64_t L, int32_t Hq, int32_t Hkv, int32_t D, float scale, int32_t dtype,
+                  void* stream) {
+    if (int rc = check_attn("tree_attn_fwd", L, Hq, Hkv, D, scale, dtype)) return rc;
+    if (!q || !k || !v || !o || !lse || !d_se || !d_meta_ws)
+        return set_error(TREE_E_ARG, "tree_attn_fwd: NULL device pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(d_se) ||
+        !aligned16(d_meta_ws))
+        return set_error(TREE_E_ARG, "tree_attn_fwd: tensors must be 16-byte aligned");
+    const AttnShape sh{L, int(L / kBlock), Hq, Hkv, D, scale};
+    const MetaPtrs mp = meta_ptrs(d_meta_ws, L);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (dtype == TREE_DTYPE_BF16)
+        e = launch_fwd_bf16(q, k, v, o, lse, d_se, mp, sh, s);
+    else
+        e = launch_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+                           static_cast<float*>(o), lse, d_se, mp, sh, s);
+    return hip_status(e, "tree_attn_fwd");
+}
+
+size_t tree_attn_bwd_workspace_bytes(int64_t L, int32_t Hq, int32_t D, int32_t dtype) {
+    (void)D;
+    (void)dtype;
+    if (L <= 0 || Hq <= 0) return 0;
+    return round256(size_t(L) * size_t(Hq) * sizeof(float));  // delta [Hq, L]
+}
+
+int tree_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, const int32_t* d_se, const void* d_meta_ws, void* d_ws,
+                  size_t ws_bytes, int64_t L, int32_t Hq, int32_t Hkv, int32_t D, float scale, int32_t dtype,
+                  void* stream) {
+    if (int rc = check_attn("tree_attn_bwd", L, Hq, Hkv, D, scale, dtype)) return rc;
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !d_se || !d_meta_ws || !d_ws)
+        return set_error(TREE_E_ARG, "tree_attn_bwd: NULL device pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+        !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(lse) || !aligned16(d_se) ||
+        !aligned16(d_meta_ws) || !aligned16(d_ws))
+        return set_error(TREE_E_ARG, "tree_attn_bwd: tensors must be 16-byte aligned");
+    const size_t need = tree_attn_bwd_workspace_bytes(L, Hq, D, dtype);
+    if (ws_bytes < need)
+        return set_error(TREE_E_WORKSPACE, "tree_attn_bwd: workspace %zu < %zu bytes", ws_bytes, need);
+    const AttnShape sh{L, int(L / kBlock), Hq, Hkv, D, scale};
+    const MetaPtrs mp = meta_ptrs(d_meta_ws, L);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    float* delta = static_cast<float*>(d_ws);
+    hipError_t e;
+    if (dtype == TREE_DTYPE_BF16)
+        e = launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, d_se, mp, delta, sh, s);
+    else
+        e = launch_bwd_f32(static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+                           static_cast<const float*>(o), lse, static_cast<const float*>(dout),
+                           static_cast<float*>(dq), static_cast<float*>(dk), static_cast<float*>(dv), d_se, mp,
+                           delta, sh, s);
+    return hip_status(e, "tree_attn_bwd");
+}
+
+}  // extern "C"

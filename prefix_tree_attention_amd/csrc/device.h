@@ -1,0 +1,102 @@
+// Internal: device-side types, the metadata workspace layout and the kernel
+// launchers of libtreeattn.  Included by the .hip translation units and by
+// the C ABI shim.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace treeattn {
+
+constexpr int kBlock = 128;          // tile edge = padding unit
+constexpr int64_t kMaxL = 1 << 20;   // largest packed length accepted
+
+// Layout of the tree_meta workspace, in int32 words.  Segments are padded to
+// 64 words (256 bytes).  nb = L / 128, T = nb (nb + 1) / 2 bounds the number
+// of nonempty tiles (only key block <= query block can be nonempty).
+//   hdr      [64]     hdr[0] = L, hdr[1] = nb, hdr[2] = real tokens
+//   blk_min  [nb]     min subtree end over each key block (pads: -1)
+//   blk_max  [nb]     max subtree end over each key block
+//   hist     [L+1]    number of tokens whose subtree ends at each index
+//   row_cnt  [nb]     nonempty tiles per query block
+//   row_ptr  [nb+1]   CSR offsets into row_ent
+//   row_ent  [T]      (key block << 1) | partial, ascending key block
+//   col_cnt  [nb]     nonempty tiles per key block
+//   col_ptr  [nb+1]
+//   col_ent  [T]      (query block << 1) | partial, ascending query block
+//   q_order  [nb]     query blocks, most nonempty tiles first (ties: index)
+//   k_order  [nb]     key blocks, most nonempty tiles first (ties: index)
+struct MetaLayout {
+    int64_t L, nb, T;
+    int64_t hdr, blk_min, blk_max, hist, row_cnt, row_ptr, row_ent, col_cnt, col_ptr, col_ent,
+        q_order, k_order, words;
+};
+
+inline int64_t pad64(int64_t w) { return (w + 63) / 64 * 64; }
+
+inline MetaLayout meta_layout(int64_t L) {
+    MetaLayout m{};
+    m.L = L;
+    m.nb = L / kBlock;
+    m.T = m.nb * (m.nb + 1) / 2;
+    int64_t o = 0;
+    m.hdr = o;     o += 64;
+    m.blk_min = o; o += pad64(m.nb);
+    m.blk_max = o; o += pad64(m.nb);
+    m.hist = o;    o += pad64(L + 1);
+    m.row_cnt = o; o += pad64(m.nb);
+    m.row_ptr = o; o += pad64(m.nb + 1);
+    m.row_ent = o; o += pad64(m.T);
+    m.col_cnt = o; o += pad64(m.nb);
+    m.col_ptr = o; o += pad64(m.nb + 1);
+    m.col_ent = o; o += pad64(m.T);
+    m.q_order = o; o += pad64(m.nb);
+    m.k_order = o; o += pad64(m.nb);
+    m.words = o;
+    return m;
+}
+
+// Device pointers into a metadata workspace.
+struct MetaPtrs {
+    const int32_t* row_ptr;
+    const int32_t* row_ent;
+    const int32_t* col_ptr;
+    const int32_t* col_ent;
+    const int32_t* q_order;
+    const int32_t* k_order;
+};
+
+inline MetaPtrs meta_ptrs(const void* ws, int64_t L) {
+    const MetaLayout m = meta_layout(L);
+    const int32_t* w = static_cast<const int32_t*>(ws);
+    return {w + m.row_ptr, w + m.row_ent, w + m.col_ptr, w + m.col_ent, w + m.q_order, w + m.k_order};
+}
+
+// Problem shape shared by the attention launchers.
+struct AttnShape {
+    int64_t L;
+    int nb, Hq, Hkv, D;
+    float scale;
+};
+
+hipError_t launch_meta(const int32_t* se, int64_t L, int32_t* pos, uint8_t* tile_class, void* ws,
+                       hipStream_t stream);
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                           const int32_t* se, const MetaPtrs& mp, const AttnShape& sh,
+                           hipStream_t stream);
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           const int32_t* se, const MetaPtrs& mp, float* delta,
+                           const AttnShape& sh, hipStream_t stream);
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                          const int32_t* se, const MetaPtrs& mp, const AttnShape& sh,
+                          hipStream_t stream);
+hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* o,
+                          const float* lse, const float* dout, float* dq, float* dk, float* dv,
+                          const int32_t* se, const MetaPtrs& mp, float* delta,
+                          const AttnShape& sh, hipStream_t stream);
+
+}  // namespace treeattn

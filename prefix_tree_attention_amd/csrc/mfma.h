@@ -1,0 +1,74 @@
+// Internal: CDNA4 (gfx950) MFMA fragment types and helpers for the bf16
+// attention kernels.
+//
+// v_mfma_f32_16x16x32_bf16, D = A * B + C with A 16x32, B 32x16, C/D 16x16:
+//   A operand: lane l holds row (l % 16), k = 8 (l / 16) + 0..7
+//   B operand: lane l holds column (l % 16), k = 8 (l / 16) + 0..7
+//   C/D:       lane l holds column (l % 16), rows 4 (l / 16) + 0..3
+// So a C fragment read "by column" has the same per-lane shape as an A or B
+// operand whose row/column index is that column and whose k index runs over
+// C's rows -- which lets a score tile feed the next product without a
+// shuffle, provided the k order is permuted consistently on both operands.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace treeattn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Round-to-nearest-even float -> bf16 bits (inputs here are finite).
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return bf16_bits(lo) | (bf16_bits(hi) << 16);
+}
+
+// Eight floats -> one bf16x8 operand.
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x4& lo, const f32x4& hi) {
+    u32x4 w;
+    w[0] = pack_bf16x2(lo[0], lo[1]);
+    w[1] = pack_bf16x2(lo[2], lo[3]);
+    w[2] = pack_bf16x2(hi[0], hi[1]);
+    w[3] = pack_bf16x2(hi[2], hi[3]);
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+__device__ __forceinline__ float bf16_to_float(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ void st8(void* p, const u32x2& v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+// Transpose a 4 (rows) x 8 (bf16 columns) register block: rows[r] holds 8
+// consecutive bf16 of row r; returns, for column j, the 4 values of that
+// column packed into 8 bytes (row 0 in the low half of word 0).
+__device__ __forceinline__ void transpose4x8(const u32x4 rows[4], u32x2 cols[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int w = j >> 1, sh = (j & 1) * 16;
+        const uint32_t a = (rows[0][w] >> sh) & 0xffffu, b = (rows[1][w] >> sh) & 0xffffu;
+        const uint32_t c = (rows[2][w] >> sh) & 0xffffu, d = (rows[3][w] >> sh) & 0xffffu;
+        cols[j][0] = a | (b << 16);
+        cols[j][1] = c | (d << 16);
+    }
+}
+
+}  // namespace treeattn

@@ -1,0 +1,155 @@
+"""Host-side tests of libtreeattn: the library loads and exports every symbol
+include/tree_attn.h declares, the C++ packer matches the oracle bit for bit
+on every generator and on random batches, and argument errors carry the
+codes the header documents.  No device compute is issued here."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+import prefix_tree_attention_amd as pta
+from prefix_tree_attention_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "tree_attn.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(pta.library_path()):
+        from prefix_tree_attention_amd import build
+        build.build()
+    return pta.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    text = open(HEADER).read()
+    names = set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(tree_[a-z_0-9]+)\s*\(", text, re.M))
+    assert {"tree_pack", "tree_meta", "tree_attn_fwd", "tree_attn_bwd", "tree_last_error"} <= names
+    for n in sorted(names):
+        assert hasattr(L, n), n
+    assert set(_lib.SIGNATURES) == names
+    assert L.tree_abi_version() == 1
+
+
+def _compare(tries_lib, tries_or):
+    assert len(tries_lib) == len(tries_or)
+    for a, b in zip(tries_lib, tries_or):
+        assert a.n_tokens == b.n_tokens and a.L == b.L
+        for f in ("token_ids", "node_id", "subtree_end", "node_start", "node_end", "node_parent", "seq_ids",
+                  "seq_iv_ptr", "seq_iv"):
+            x, y = getattr(a, f), getattr(b, f)
+            assert x.shape == y.shape and (x == y).all(), f
+
+
+def _stats_vs_oracle(stats, tries_or, w_mask):
+    lens = np.asarray(w_mask).astype(bool).sum(1)
+    assert stats["n_tries"] == len(tries_or)
+    assert stats["original_tokens"] == int(lens.sum())
+    assert stats["tree_tokens"] == sum(p.n_tokens for p in tries_or)
+    assert stats["unpacked_pairs"] == int((lens.astype(np.int64) * (lens + 1) // 2).sum())
+
+
+def test_worked_example(L):
+    ids, mask = workloads.worked_example()
+    tl, st = pta.pack(ids, mask, 128)
+    to = oracle.pack(ids, mask, 128)
+    _compare(tl, to)
+    assert st["n_pairs"] == 22 and st["unpacked_pairs"] == 26
+    assert st["tree_token_ratio"] == pytest.approx(8 / 11)
+
+
+@pytest.mark.parametrize("config", ["1", "2", "3", "4a", "4b"])
+def test_configs_bit_exact(L, config):
+    w = workloads.make_workload(config)
+    tl, st = pta.pack(w.ids, w.mask, w.max_tokens_per_mb)
+    to = oracle.pack(w.ids, w.mask, w.max_tokens_per_mb)
+    _compare(tl, to)
+    _stats_vs_oracle(st, to, w.mask)
+    if config == "4a":
+        assert st["n_pairs"] == 404_766_720
+    if config == "4b":
+        assert st["n_pairs"] == 33_570_816
+
+
+@pytest.mark.parametrize("L_,b", [(8192, 1), (8192, 8), (16384, 2), (16384, 4)])
+def test_sweep_points_bit_exact(L, L_, b):
+    w = workloads.sweep_workload(L_, b)
+    tl, _ = pta.pack(w.ids, w.mask, w.max_tokens_per_mb)
+    _compare(tl, oracle.pack(w.ids, w.mask, w.max_tokens_per_mb))
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_random_batches_bit_exact(L, seed):
+    rng = np.random.default_rng(1000 + seed)
+    n_seq = int(rng.integers(1, 30))
+    vocab = int(rng.choice([2, 3, 5, 50]))
+    seqs = []
+    for _ in range(n_seq):
+        if seqs and rng.random() < 0.6:
+            base = seqs[int(rng.integers(len(seqs)))]
+            cut = int(rng.integers(0, len(base) + 1))
+            tail = rng.integers(0, vocab, int(rng.integers(0 if cut else 1, 90)))
+            s = np.concatenate([base[:cut], tail]).astype(np.int32)
+        else:
+            s = rng.integers(0, vocab, int(rng.integers(1, 120))).astype(np.int32)
+        seqs.append(s if len(s) else np.array([0], np.int32))
+    ids, mask = workloads.pad_rows(seqs)
+    M = int(rng.choice([128, 256, 512]))
+    M = max(M, -(-max(len(s) for s in seqs) // 128) * 128)
+    pad_max = bool(seed % 3 == 0)
+    tl, st = pta.pack(ids, mask, M, pad_to_maximum=pad_max, pad_id=seed % 7)
+    to = oracle.pack(ids, mask, M, pad_to_maximum=pad_max, pad_id=seed % 7)
+    _compare(tl, to)
+    masks = [oracle.dense_ancestor_mask(p) for p in to]
+    acc = oracle.accounting(to, masks, mask.sum(1))
+    assert st["n_pairs"] == acc["n_pairs"]
+
+
+def test_error_codes_match_oracle(L):
+    ids, mask = workloads.worked_example()
+    cases = [(0, "max_tokens", -1), (-128, "max_tokens", -1), (100, "align", -2)]
+    for M, ocode, lcode in cases:
+        with pytest.raises(oracle.PackError) as eo:
+            oracle.pack(ids, mask, M)
+        assert eo.value.code == ocode
+        with pytest.raises(pta.TreeAttnError) as el:
+            pta.pack(ids, mask, M)
+        assert el.value.code == lcode and pta.lib().tree_last_error()
+    long_ids, long_mask = workloads.pad_rows([np.arange(1, 200, dtype=np.int32)])
+    with pytest.raises(pta.TreeAttnError) as el:
+        pta.pack(long_ids, long_mask, 128)
+    assert el.value.code == -3
+    m2 = mask.copy()
+    m2[2] = 0
+    with pytest.raises(pta.TreeAttnError) as el:
+        pta.pack(ids, m2, 128)
+    assert el.value.code == -4
+    with pytest.raises(pta.TreeAttnError) as el:
+        pta.pack(ids, mask, 128, block_size=64)
+    assert el.value.code == -5
+
+
+def test_device_entry_points_validate_before_launch(L):
+    # bad arguments are rejected on the host, before any device work
+    assert L.tree_meta_workspace_bytes(100) == 0 and L.tree_meta_workspace_bytes(0) == 0
+    assert L.tree_meta_workspace_bytes(1024) > 0
+    assert L.tree_meta(None, 1024, None, None, None, 0, None) == -5
+    assert L.tree_meta(None, 1000, None, None, None, 0, None) == -5
+    p = ctypes.c_void_p(256)
+    ws = L.tree_meta_workspace_bytes(1024)
+    assert L.tree_meta(p, 1024, p, p, p, ws - 1, None) == -6
+    args = [p] * 7
+    assert L.tree_attn_fwd(*args, 1024, 6, 4, 128, 0.1, 0, None) == -5   # Hq % Hkv
+    assert L.tree_attn_fwd(*args, 1024, 8, 2, 96, 0.1, 0, None) == -5    # D
+    assert L.tree_attn_fwd(*args, 1024, 8, 2, 128, 0.1, 7, None) == -5   # dtype
+    assert L.tree_attn_fwd(*args, 1000, 8, 2, 128, 0.1, 0, None) == -5   # L % 128
+    assert L.tree_attn_fwd(ctypes.c_void_p(257), *args[1:], 1024, 8, 2, 128, 0.1, 0, None) == -5  # alignment
+    need = L.tree_attn_bwd_workspace_bytes(1024, 8, 128, 0)
+    assert need >= 1024 * 8 * 4
+    assert L.tree_attn_bwd(*([p] * 12), need - 1, 1024, 8, 2, 128, 0.1, 0, None) == -6
+    assert b"workspace" in L.tree_last_error()

@@ -10,4 +10,6 @@ from .generators import (  # noqa: F401
     worked_example,
     attention_inputs,
     pad_rows,
+    small_workload,
+    SMALL_KINDS,
 )

@@ -209,3 +209,57 @@ def attention_inputs(L: int, hq: int, hkv: int, d: int, dtype: str, std: float, 
     v = (torch.randn(L, hkv, d, generator=g) * std).to(tdt)
     do = torch.randn(L, hq, d, generator=g).to(tdt) if backward else None
     return q, k, v, do
+
+
+SMALL_KINDS = ("grpo-small", "deep-small", "nested", "disjoint-small", "multiturn-small")
+
+
+def small_workload(kind: str, seed: int = 0):
+    """Scaled-down batches (a few hundred to a few thousand tokens) whose
+    node boundaries fall inside 128-token tiles, for elementwise parity.
+    Returns (ids, mask, max_tokens_per_mb)."""
+    rng = np.random.default_rng(10_000 + 97 * SMALL_KINDS.index(kind) + seed)
+    V = 50_000
+    seqs = []
+    if kind == "grpo-small":
+        for _ in range(4):
+            p = _tok(rng, int(rng.integers(64, 301)), V)
+            seqs += [np.concatenate([p, _tok(rng, int(rng.integers(20, 401)), V)]) for _ in range(4)]
+        M = 2048
+    elif kind == "deep-small":
+        prefix = _tok(rng, 300, V)
+        leaves = [_tok(rng, int(rng.integers(50, 201)), V) for _ in range(6)]
+        leaves.append(np.concatenate([leaves[0][:30], _tok(rng, 70, V)]))  # a branch inside a leaf
+        seqs = [np.concatenate([prefix, lf]) for lf in leaves]
+        M = 2048
+    elif kind == "nested":
+        base = _tok(rng, 90, V)
+        seqs = [base[:40], base[:90], np.concatenate([base, _tok(rng, 150, V)]), base[:41],
+                np.concatenate([base[:60], _tok(rng, 200, V)]), base[:90]]  # includes a duplicate
+        M = 1024
+    elif kind == "disjoint-small":
+        seqs = [_tok(rng, int(n), V) for n in (37, 300, 129, 1, 255, 200)]
+        for i, s in enumerate(seqs):
+            s[0] = V + i  # distinct first tokens
+        M = 1280
+    elif kind == "multiturn-small":
+        system = _tok(rng, 160, V)
+        groups = [(list(range(4)), [system]) for _ in range(2)]
+        for _turn in range(3):
+            nxt = []
+            for members, parts in groups:
+                if len(members) >= 2 and rng.random() < 0.5:
+                    h = len(members) // 2
+                    for half in (members[:h], members[h:]):
+                        nxt.append((half, parts + [_tok(rng, int(rng.integers(20, 81)), V)]))
+                else:
+                    nxt.append((members, parts + [_tok(rng, int(rng.integers(20, 81)), V)]))
+            groups = nxt
+        for members, parts in groups:
+            for _m in members:
+                seqs.append(np.concatenate(parts + [_tok(rng, int(rng.integers(20, 301)), V)]))
+        M = 4096
+    else:
+        raise ValueError(kind)
+    ids, mask = pad_rows(seqs)
+    return ids, mask, M
