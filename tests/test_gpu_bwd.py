@@ -1,0 +1,148 @@
+"""Backward tree attention on the GPU vs the oracle.
+
+Elementwise dQ / dK / dV on scaled-down tries (bf16 MFMA path and fp32
+check mode).  At full size: sampled dQ rows, sampled dK / dV keys whose
+descendant sets are small enough for the one-column oracle, and two exact
+identities over all keys -- sum_j dK_j = 0 (each softmax-gradient row sums
+to zero) and sum_j dV_j = sum_i dO_i over real rows (each P row sums to
+one), per key/value head with its query heads summed."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+import prefix_tree_attention_amd as pta
+from gpu_common import (BF16_ATOL, BF16_RTOL, F32_ATOL, F32_RTOL, announce, assert_close, bf16_ref,
+                        sample_rows, small_cases, torch_cuda)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(torch, p_lib, hq, hkv, d, dtype, std, seed):
+    q, k, v, do = workloads.attention_inputs(p_lib.L, hq, hkv, d, dtype, std, seed)
+    meta = pta.tree_meta(p_lib.subtree_end)
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    o, lse = pta.attn_fwd(qd, kd, vd, meta)
+    dq, dk, dv = pta.attn_bwd(qd, kd, vd, o, lse, dod, meta)
+    torch.cuda.synchronize()
+    return q, k, v, do, o.cpu(), lse.cpu(), dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def _full_check(torch, name, ids, mask, M, hq, hkv, d, dtype, seed):
+    tl, _ = pta.pack(ids, mask, M)
+    to = oracle.pack(ids, mask, M)
+    std = 1.0 if dtype == "fp32" else 1.0 / math.sqrt(d)
+    atol, rtol = (F32_ATOL, F32_RTOL) if dtype == "fp32" else (BF16_ATOL, BF16_RTOL)
+    for t, (pl, po) in enumerate(zip(tl, to)):
+        announce(f"bwd {name}[{t}] L={pl.L} {dtype} hq={hq} hkv={hkv} d={d}")
+        q, k, v, do, o, lse, dq, dk, dv = _run(torch, pl, hq, hkv, d, dtype, std, seed + t)
+        m = oracle.dense_ancestor_mask(po)
+        Q, K, V, G = (bf16_ref(x) for x in (q, k, v, do))
+        o_ref, lse_ref = oracle.attention_forward(Q, K, V, m, 1.0 / math.sqrt(d))
+        dq_ref, dk_ref, dv_ref = oracle.attention_backward(Q, K, V, o_ref, lse_ref, G, m, 1.0 / math.sqrt(d))
+        for nm, x in (("dQ", dq), ("dK", dk), ("dV", dv)):
+            assert np.isfinite(x.float().numpy()).all(), nm
+        assert_close(bf16_ref(dq), dq_ref, atol, rtol, f"{name}[{t}] dQ")
+        assert_close(bf16_ref(dk), dk_ref, atol, rtol, f"{name}[{t}] dK")
+        assert_close(bf16_ref(dv), dv_ref, atol, rtol, f"{name}[{t}] dV")
+        n = po.n_tokens
+        assert (dq[n:].float() == 0).all() and (dk[n:].float() == 0).all() and (dv[n:].float() == 0).all()
+
+
+@pytest.mark.parametrize("case", list(range(6)))
+@pytest.mark.parametrize("shape", [(8, 2, 128), (4, 1, 64), (2, 2, 128)])
+def test_bwd_bf16_small(case, shape):
+    torch = torch_cuda()
+    name, ids, mask, M = list(small_cases())[case]
+    _full_check(torch, name, ids, mask, M, *shape, "bf16", 300 + case)
+
+
+@pytest.mark.parametrize("case", list(range(6)))
+@pytest.mark.parametrize("shape", [(1, 1, 64), (4, 2, 32), (2, 1, 128)])
+def test_bwd_fp32_small(case, shape):
+    torch = torch_cuda()
+    name, ids, mask, M = list(small_cases())[case]
+    _full_check(torch, name, ids, mask, M, *shape, "fp32", 400 + case)
+
+
+def test_bwd_deep_shared_medium():
+    # a scaled deep-shared trie: 1024-token prefix, 12 leaves of 100 tokens
+    torch = torch_cuda()
+    rng = np.random.default_rng(77)
+    prefix = rng.integers(0, 1000, 1024).astype(np.int32)
+    seqs = [np.concatenate([prefix, np.concatenate([[2000 + i], rng.integers(0, 1000, 99)]).astype(np.int32)])
+            for i in range(12)]
+    ids, mask = workloads.pad_rows(seqs)
+    _full_check(torch, "deep-medium", ids, mask, 4096, 8, 2, 128, "bf16", 500)
+
+
+def _pick_keys(po, rng, n_keys, max_desc):
+    """Keys whose descendant sets have at most max_desc rows."""
+    keys = []
+    cand = rng.permutation(po.n_tokens)
+    for j in cand:
+        dsc = oracle.descendants_of(po, int(j))
+        if len(dsc) <= max_desc:
+            keys.append((int(j), dsc))
+        if len(keys) == n_keys:
+            break
+    return keys
+
+
+@pytest.mark.parametrize("config", ["4a", "4b", "2", "3"])
+def test_bwd_full_size_sampled(config):
+    torch = torch_cuda()
+    w = workloads.make_workload(config)
+    tl, _ = pta.pack(w.ids, w.mask, w.max_tokens_per_mb)
+    to = oracle.pack(w.ids, w.mask, w.max_tokens_per_mb)
+    pl, po = tl[0], to[0]
+    announce(f"bwd full config{config}[0] L={pl.L}")
+    q, k, v, do, o, lse, dq, dk, dv = _run(torch, pl, w.hq, w.hkv, w.d, "bf16", w.qkv_std, 7000 + len(config))
+    for nm, x in (("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert np.isfinite(x.float().numpy()).all(), nm
+    Q, K, V, G = (bf16_ref(x) for x in (q, k, v, do))
+    scale = 1.0 / math.sqrt(w.d)
+    rows = sample_rows(po, 12, seed=11)
+    anc = [oracle.ancestors_of(po, i) for i in rows]
+    dq_ref = oracle.attention_dq_rows(Q, K, V, G, rows, anc, scale, dtype=np.float32)
+    assert_close(bf16_ref(dq[rows]), dq_ref, BF16_ATOL, BF16_RTOL, f"config{config} dQ rows")
+    rng = np.random.default_rng(3)
+    picked = _pick_keys(po, rng, 6, 24)
+    cols = [j for j, _ in picked]
+    desc = [dsc for _, dsc in picked]
+    dk_ref, dv_ref = oracle.attention_dkdv_cols(Q, K, V, G, cols, desc, lambda i: oracle.ancestors_of(po, i),
+                                                scale, dtype=np.float32)
+    assert_close(bf16_ref(dk[cols]), dk_ref, BF16_ATOL, BF16_RTOL, f"config{config} dK cols")
+    assert_close(bf16_ref(dv[cols]), dv_ref, BF16_ATOL, BF16_RTOL, f"config{config} dV cols")
+    # identities over every key, per key/value head
+    n = po.n_tokens
+    grp = w.hq // w.hkv
+    dk_sum = bf16_ref(dk[:n]).sum(axis=0)
+    dv_sum = bf16_ref(dv[:n]).sum(axis=0)
+    do_sum = G[:n].reshape(n, w.hkv, grp, w.d).sum(axis=(0, 2))
+    scale_dk = np.abs(bf16_ref(dk[:n])).sum(axis=0).max()
+    scale_dv = np.abs(bf16_ref(dv[:n])).sum(axis=0).max()
+    print(f"  sum dK max {np.abs(dk_sum).max():.3e} (abs-sum {scale_dk:.3e}); "
+          f"sum dV - sum dO max {np.abs(dv_sum - do_sum).max():.3e} (abs-sum {scale_dv:.3e})", flush=True)
+    assert np.abs(dk_sum).max() <= 1e-2 * scale_dk
+    assert np.abs(dv_sum - do_sum).max() <= 1e-2 * scale_dv
+    assert (dq[n:].float() == 0).all() and (dk[n:].float() == 0).all() and (dv[n:].float() == 0).all()
+
+
+def test_autograd_function_matches_entry_points():
+    torch = torch_cuda()
+    ids, mask, M = workloads.small_workload("deep-small")
+    (pl,), _ = pta.pack(ids, mask, M)
+    q, k, v, do = workloads.attention_inputs(pl.L, 4, 2, 128, "bf16", 0.09, 9)
+    meta = pta.tree_meta(pl.subtree_end)
+    qd, kd, vd = (t.cuda().requires_grad_(True) for t in (q, k, v))
+    o = pta.tree_attention(qd, kd, vd, meta)
+    o.backward(do.cuda())
+    o2, lse2 = pta.attn_fwd(qd.detach(), kd.detach(), vd.detach(), meta)
+    dq, dk, dv = pta.attn_bwd(qd.detach(), kd.detach(), vd.detach(), o2, lse2, do.cuda(), meta)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    assert torch.equal(qd.grad, dq) and torch.equal(kd.grad, dk) and torch.equal(vd.grad, dv)
