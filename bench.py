@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Throughput of the trie-packed tree-attention hot path on one MI355X.
+
+One step is one pass of the whole path over one synthetic rollout batch:
+  host   tree_pack (C++ FFD trie build, compression, pre-order layout)
+  H2D    subtree ends of every trie (pinned, async)
+  device tree_meta, tree_attn_fwd, tree_attn_bwd (delta, dK/dV, dQ)
+Q, K, V and dO are resident in HBM before the timed region.  Steps are
+enqueued back to back, so the host packing of step k+1 overlaps the GPU work
+of step k (the trie-count all-reduce of a data-parallel run would sit at the
+same point).  Each kernel phase is bracketed by HIP events on the stream
+the library launches on.
+
+Prints ONE JSON line.  ``value`` is real packed tokens per second through
+fwd+bwd; useful TFLOP/s counts 14 * D * Hq per visible (query, key) pair
+(forward 4D, backward 10D including the score recompute, the FlashAttention
+convention) and is compared with MI355X's dense bf16 MFMA peak.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--config 4a]
+                    [--sweep L,b] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PHASES = ("meta", "fwd", "delta", "dkdv", "dq")
+PHASE_KERNEL = {"meta": "meta_finish", "fwd": "fwd_bf16_kernel", "delta": "delta_bf16_kernel",
+                "dkdv": "dkdv_bf16_kernel", "dq": "dq_bf16_kernel"}
+PHASE_SOURCE = {"meta": "meta.hip", "fwd": "fwd_bf16.hip", "delta": "bwd_bf16.hip", "dkdv": "bwd_bf16.hip",
+                "dq": "bwd_bf16.hip"}
+# algorithmic FLOPs per visible pair and query head, in units of D
+PHASE_FLOPS_PER_PAIR_D = {"fwd": 4, "dkdv": 8, "dq": 6}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="4a", help="workload: 2, 3, 4a, 4b")
+    ap.add_argument("--sweep", default=None, help="L,b of a sweep point (overrides --config)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=1, help="query heads in the oracle sample")
+    return ap.parse_args(argv)
+
+
+def source_sha(name: str) -> str:
+    with open(os.path.join(ROOT, "prefix_tree_attention_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload: str, phase: str):
+    """HBM bytes per launch of a kernel from a committed rocprofv3 PMC
+    summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{PHASE_KERNEL[phase]}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha") != source_sha(PHASE_SOURCE[phase]):
+        return None
+    return float(t["bytes_per_launch"])
+
+
+def cpu_baseline(w, p_oracle_input, n_heads: int):
+    """The oracle (dense ancestor mask, naive fp32 attention and closed-form
+    gradients) on trie 0 of the workload, restricted to `n_heads` query heads
+    of key/value head 0; scaled to all heads."""
+    import numpy as np
+    import torch
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    ids, mask, M = p_oracle_input
+    t0 = time.perf_counter()
+    po = oracle.pack(ids, mask, M)[0]
+    m = oracle.dense_ancestor_mask(po)
+    t_pack = time.perf_counter() - t0
+    q, k, v, do = workloads.attention_inputs(po.L, w.hq, w.hkv, w.d, "bf16", w.qkv_std, 4242)
+    Q = q[:, :n_heads].float().numpy()
+    K = k[:, :1].float().numpy()
+    V = v[:, :1].float().numpy()
+    G = do[:, :n_heads].float().numpy()
+    scale = 1.0 / math.sqrt(w.d)
+    t1 = time.perf_counter()
+    o, lse = oracle.attention_forward(Q, K, V, m, scale, dtype=np.float32)
+    oracle.attention_backward(Q, K, V, o, lse, G, m, scale, dtype=np.float32)
+    t_attn = time.perf_counter() - t1
+    per_trie = t_pack + t_attn * (w.hq / n_heads)
+    del torch
+    return {
+        "value": po.n_tokens / per_trie,
+        "unit": "tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"trie 0 ({po.n_tokens} tokens, L={po.L}): oracle pack + dense mask "
+                   f"({t_pack:.1f} s) and fp32 fwd+bwd of {n_heads} of {w.hq} query heads "
+                   f"({t_attn:.1f} s), attention time scaled x{w.hq // n_heads}"),
+    }
+
+
+def main(argv=None):
+    a = parse(argv)
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": a.gpus}), flush=True)
+        log("bench.py: multi-GPU runs are not part of this build (one trie per GPU; see the sharding design).")
+        return 2
+    import numpy as np
+    import torch
+    import workloads
+    import prefix_tree_attention_amd as pta
+
+    if a.sweep:
+        L_, b = (int(x) for x in a.sweep.split(","))
+        w = workloads.sweep_workload(L_, b)
+    else:
+        w = workloads.make_workload(a.config)
+    if w.dtype != "bf16" or not w.backward:
+        raise SystemExit("bench.py times the bf16 forward+backward path; config 1 is a parity case")
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # ---------------- untimed setup ----------------
+    tries, stats = pta.pack(w.ids, w.mask, w.max_tokens_per_mb)
+    log(f"workload {w.name}: {len(tries)} tries, L={[t.L for t in tries]}, tree tokens {stats['tree_tokens']}, "
+        f"pairs {stats['n_pairs']}, unpacked pairs {stats['unpacked_pairs']}")
+    bufs = []
+    pairs_per_trie = []
+    for i, tr in enumerate(tries):
+        q, k, v, do = workloads.attention_inputs(tr.L, w.hq, w.hkv, w.d, "bf16", w.qkv_std, 1_000_000 + i)
+        L = tr.L
+        nb = L // 128
+        se_i64 = tr.subtree_end.astype(np.int64)
+        real = se_i64 >= 0
+        pairs_per_trie.append(int((se_i64[real] - np.arange(L)[real] + 1).sum()))
+        bufs.append({
+            "L": L,
+            "q": q.to(dev), "k": k.to(dev), "v": v.to(dev), "do": do.to(dev),
+            "o": torch.empty((L, w.hq, w.d), dtype=torch.bfloat16, device=dev),
+            "lse": torch.empty((w.hq, L), dtype=torch.float32, device=dev),
+            "dq": torch.empty((L, w.hq, w.d), dtype=torch.bfloat16, device=dev),
+            "dk": torch.empty((L, w.hkv, w.d), dtype=torch.bfloat16, device=dev),
+            "dv": torch.empty((L, w.hkv, w.d), dtype=torch.bfloat16, device=dev),
+            "se": torch.empty(L, dtype=torch.int32, device=dev),
+            "pos": torch.empty(L, dtype=torch.int32, device=dev),
+            "tc": torch.empty((nb, nb), dtype=torch.uint8, device=dev),
+            "mws": torch.empty(pta.meta_workspace_bytes(L), dtype=torch.uint8, device=dev),
+            "bws": torch.empty(pta.bwd_workspace_bytes(L, w.hq, w.d), dtype=torch.uint8, device=dev),
+            "pinned": [torch.empty(L, dtype=torch.int32).pin_memory() for _ in range(2)],
+            "copied": [None, None],
+        })
+    assert sum(pairs_per_trie) == stats["n_pairs"]
+    torch.cuda.synchronize()
+    lib = pta.lib()
+    from prefix_tree_attention_amd.api import _ptr  # argument marshalling helper
+    import ctypes
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    scale = 1.0 / math.sqrt(w.d)
+
+    def step(k_step, events):
+        cur, _ = pta.pack(w.ids, w.mask, w.max_tokens_per_mb)
+        assert len(cur) == len(bufs)
+        slot = k_step % 2
+        for i, tr in enumerate(cur):
+            b = bufs[i]
+            assert tr.L == b["L"]
+            if b["copied"][slot] is not None:
+                b["copied"][slot].synchronize()  # the copy that last read this pinned buffer is done
+            b["pinned"][slot].numpy()[:] = tr.subtree_end
+            b["se"].copy_(b["pinned"][slot], non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record(stream)
+            b["copied"][slot] = ev
+            L = b["L"]
+            E = [torch.cuda.Event(enable_timing=True) for _ in range(len(PHASES) + 1)] if events is not None else None
+            if E:
+                E[0].record(stream)
+            pta._lib.check(lib.tree_meta(_ptr(b["se"]), L, _ptr(b["pos"]), _ptr(b["tc"]), _ptr(b["mws"]),
+                                         b["mws"].numel(), sptr))
+            if E:
+                E[1].record(stream)
+            pta._lib.check(lib.tree_attn_fwd(_ptr(b["q"]), _ptr(b["k"]), _ptr(b["v"]), _ptr(b["o"]), _ptr(b["lse"]),
+                                             _ptr(b["se"]), _ptr(b["mws"]), L, w.hq, w.hkv, w.d, scale, 0, sptr))
+            if E:
+                E[2].record(stream)
+            for j, ph in enumerate((pta.BWD_DELTA, pta.BWD_DKDV, pta.BWD_DQ)):
+                pta._lib.check(lib.tree_attn_bwd_phase(
+                    ph, _ptr(b["q"]), _ptr(b["k"]), _ptr(b["v"]), _ptr(b["o"]), _ptr(b["lse"]), _ptr(b["do"]),
+                    _ptr(b["dq"]), _ptr(b["dk"]), _ptr(b["dv"]), _ptr(b["se"]), _ptr(b["mws"]), _ptr(b["bws"]),
+                    b["bws"].numel(), L, w.hq, w.hkv, w.d, scale, 0, sptr))
+                if E:
+                    E[3 + j].record(stream)
+            if events is not None:
+                events.append((i, E))
+
+    for k_step in range(a.warmup):
+        step(k_step, None)
+    torch.cuda.synchronize()
+    log(f"warmup done ({a.warmup} steps)")
+
+    events = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k_step in range(a.steps):
+        step(a.warmup + k_step, events)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sec_per_step = (t1 - t0) / a.steps
+
+    # per-phase kernel time (ms per launch) from the events
+    tot = {p: 0.0 for p in PHASES}
+    for i, E in events:
+        for j, p in enumerate(PHASES):
+            tot[p] += E[j].elapsed_time(E[j + 1])
+    n_launch = len(events)
+    avg = {p: tot[p] / n_launch for p in PHASES}
+    gpu_ms_per_step = sum(tot.values()) / a.steps
+    log("per-launch ms: " + ", ".join(f"{p} {avg[p]:.3f}" for p in PHASES)
+        + f" | gpu ms/step {gpu_ms_per_step:.3f} | wall ms/step {sec_per_step * 1e3:.3f}")
+
+    n_pairs = stats["n_pairs"]
+    tokens = stats["tree_tokens"]
+    useful_flop = 14.0 * w.d * w.hq * n_pairs
+    useful_tflops = useful_flop / sec_per_step / 1e12
+    dom = max(PHASES, key=lambda p: avg[p])
+    if dom in PHASE_FLOPS_PER_PAIR_D:
+        alg = PHASE_FLOPS_PER_PAIR_D[dom] * w.d * w.hq * n_pairs / n_launch * a.steps  # per launch
+        achieved = alg / (avg[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    else:  # HBM-bound phase
+        per = 2 * sum(b["L"] for b in bufs) * w.hq * w.d * 2 / len(bufs)
+        achieved = per / (avg[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["kernel"] = PHASE_KERNEL[dom]
+    roof["traffic"] = load_traffic(w.name, dom)
+
+    result = {
+        "metric": "tree-attn fwd+bwd tokens/s + useful TFLOP/s (% of bf16 MFMA peak), 1 GPU",
+        "value": round(tokens / sec_per_step, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(sec_per_step * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "useful_tflops": round(useful_tflops, 2),
+        "pct_of_bf16_peak": round(100.0 * useful_tflops / PEAK_BF16_TFLOPS, 2),
+        "effective_tokens_per_s": round(stats["original_tokens"] / sec_per_step, 1),
+        "flop_reduction_vs_unpacked": round(stats["unpacked_pairs"] / n_pairs, 3),
+        "tree_token_ratio": round(stats["tree_token_ratio"], 4),
+        "gpu_ms_per_step": round(gpu_ms_per_step, 3),
+        "kernel_ms_per_launch": {p: round(avg[p], 4) for p in PHASES},
+        "config": {"workload": w.name, "tries": len(bufs), "L": [b["L"] for b in bufs], "hq": w.hq,
+                   "hkv": w.hkv, "head_dim": w.d, "max_tokens_per_mb": w.max_tokens_per_mb,
+                   "tree_tokens": tokens, "pairs": n_pairs, "parallelism": "single-gpu"},
+        "roofline": roof,
+    }
+    if not a.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        sub = _first_trie_rows(w, tries[0])
+        result["cpu_baseline"] = cpu_baseline(w, sub, a.cpu_heads)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def _first_trie_rows(w, tr0):
+    """The batch rows packed into trie 0, as an input the oracle packs into
+    exactly that trie."""
+    rows = sorted(int(r) for r in tr0.seq_ids)
+    return w.ids[rows], w.mask[rows], w.max_tokens_per_mb
+
+
+if __name__ == "__main__":
+    sys.exit(main())

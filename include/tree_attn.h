@@ -183,6 +183,23 @@ int tree_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                   int64_t L, int32_t Hq, int32_t Hkv, int32_t D, float scale,
                   int32_t dtype, void* stream);
 
+/* One phase of tree_attn_bwd, for callers that time or schedule the
+ * backward's kernels separately: TREE_BWD_DELTA computes Delta_i =
+ * dO_i . O_i into d_ws; TREE_BWD_DKDV writes dk and dv; TREE_BWD_DQ writes
+ * dq; TREE_BWD_ALL runs all three in that order (same as tree_attn_bwd).
+ * DKDV and DQ read the Delta that a DELTA phase left in the same d_ws, so
+ * a DELTA phase must precede them on the stream.  Other arguments and
+ * errors as tree_attn_bwd; an unknown phase gives TREE_E_ARG. */
+#define TREE_BWD_ALL 0
+#define TREE_BWD_DELTA 1
+#define TREE_BWD_DKDV 2
+#define TREE_BWD_DQ 3
+int tree_attn_bwd_phase(int32_t phase, const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        const int32_t* d_se, const void* d_meta_ws, void* d_ws, size_t ws_bytes,
+                        int64_t L, int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                        int32_t dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

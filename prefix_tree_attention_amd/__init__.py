@@ -8,7 +8,8 @@ HIP kernels with bf16 MFMA.  Everything sits behind the C ABI of
 arguments into it.
 """
 
-from ._lib import TreeAttnError, lib, library_path, DTYPE_BF16, DTYPE_FP32, BLOCK  # noqa: F401
+from ._lib import (TreeAttnError, lib, library_path, DTYPE_BF16, DTYPE_FP32, BLOCK,  # noqa: F401
+                   BWD_ALL, BWD_DELTA, BWD_DKDV, BWD_DQ)
 from .api import (  # noqa: F401
     PackedTrie,
     TreeMeta,
@@ -18,5 +19,6 @@ from .api import (  # noqa: F401
     bwd_workspace_bytes,
     attn_fwd,
     attn_bwd,
+    attn_bwd_phase,
     tree_attention,
 )

@@ -71,7 +71,10 @@ SIGNATURES = {
     "tree_attn_bwd_workspace_bytes": (c_sz, [c_i64, c_i32, c_i32, c_i32]),
     "tree_attn_bwd": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                      c_sz, c_i64, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp]),
+    "tree_attn_bwd_phase": (ctypes.c_int, [c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                           c_vp, c_sz, c_i64, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp]),
 }
+BWD_ALL, BWD_DELTA, BWD_DKDV, BWD_DQ = 0, 1, 2, 3
 
 _lock = threading.Lock()
 _lib = None

@@ -192,6 +192,18 @@ def attn_bwd(q, k, v, o, lse, do, meta: TreeMeta, scale: float | None = None, wo
     return dq, dk, dv
 
 
+def attn_bwd_phase(phase: int, q, k, v, o, lse, do, dq, dk, dv, meta: TreeMeta, workspace, scale=None):
+    """``tree_attn_bwd_phase`` into caller-provided outputs and workspace
+    (BWD_DELTA, BWD_DKDV, BWD_DQ or BWD_ALL); used to time the backward's
+    kernels separately."""
+    L, hq, d = q.shape
+    hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    check(lib().tree_attn_bwd_phase(int(phase), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
+                                    _ptr(dk), _ptr(dv), _ptr(meta.se), _ptr(meta.ws), _ptr(workspace),
+                                    workspace.numel(), L, hq, hkv, d, scale, _dtype_code(q), _stream(q.device)))
+
+
 def _autograd_fn():
     torch = _torch()
 

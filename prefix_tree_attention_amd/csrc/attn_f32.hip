@@ -195,16 +195,20 @@ __global__ __launch_bounds__(256) void delta_f32_kernel(const float* __restrict_
 }
 
 template <int D>
-void launch_f32_bwd_d(const float* q, const float* k, const float* v, const float* dout, const float* lse,
+void launch_f32_bwd_d(int phase, const float* q, const float* k, const float* v, const float* dout, const float* lse,
                       const float* delta, float* dq, float* dk, float* dv, const int32_t* se,
                       const MetaPtrs& mp, const AttnShape& sh, hipStream_t stream) {
     const int L = int(sh.L);
-    dq_f32_kernel<D><<<dim3(2 * sh.nb, sh.Hq), kRows, 0, stream>>>(q, k, v, dout, lse, delta, dq, se, mp.row_ptr,
-                                                                     mp.row_ent, L, sh.Hq, sh.Hkv, sh.scale);
-    dkv_f32_kernel<D, true><<<dim3(2 * sh.nb, sh.Hkv), kRows, 0, stream>>>(
-        q, k, v, dout, lse, delta, dk, se, mp.col_ptr, mp.col_ent, L, sh.Hq, sh.Hkv, sh.scale);
-    dkv_f32_kernel<D, false><<<dim3(2 * sh.nb, sh.Hkv), kRows, 0, stream>>>(
-        q, k, v, dout, lse, delta, dv, se, mp.col_ptr, mp.col_ent, L, sh.Hq, sh.Hkv, sh.scale);
+    if (phase == kPhaseAll || phase == kPhaseDkdv) {
+        dkv_f32_kernel<D, true><<<dim3(2 * sh.nb, sh.Hkv), kRows, 0, stream>>>(
+            q, k, v, dout, lse, delta, dk, se, mp.col_ptr, mp.col_ent, L, sh.Hq, sh.Hkv, sh.scale);
+        dkv_f32_kernel<D, false><<<dim3(2 * sh.nb, sh.Hkv), kRows, 0, stream>>>(
+            q, k, v, dout, lse, delta, dv, se, mp.col_ptr, mp.col_ent, L, sh.Hq, sh.Hkv, sh.scale);
+    }
+    if (phase == kPhaseAll || phase == kPhaseDq)
+        dq_f32_kernel<D><<<dim3(2 * sh.nb, sh.Hq), kRows, 0, stream>>>(q, k, v, dout, lse, delta, dq, se,
+                                                                         mp.row_ptr, mp.row_ent, L, sh.Hq, sh.Hkv,
+                                                                         sh.scale);
 }
 
 }  // namespace
@@ -232,15 +236,17 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,
+hipError_t launch_bwd_f32(int phase, const float* q, const float* k, const float* v, const float* o, const float* lse,
                           const float* dout, float* dq, float* dk, float* dv, const int32_t* se,
                           const MetaPtrs& mp, float* delta, const AttnShape& sh, hipStream_t stream) {
     const int rows = int(sh.L) * sh.Hq;
-    delta_f32_kernel<<<(rows + 3) / 4, 256, 0, stream>>>(o, dout, delta, int(sh.L), sh.Hq, sh.D);
+    if (phase == kPhaseAll || phase == kPhaseDelta)
+        delta_f32_kernel<<<(rows + 3) / 4, 256, 0, stream>>>(o, dout, delta, int(sh.L), sh.Hq, sh.D);
+    if (phase == kPhaseDelta) return hipGetLastError();
     switch (sh.D) {
-        case 32: launch_f32_bwd_d<32>(q, k, v, dout, lse, delta, dq, dk, dv, se, mp, sh, stream); break;
-        case 64: launch_f32_bwd_d<64>(q, k, v, dout, lse, delta, dq, dk, dv, se, mp, sh, stream); break;
-        case 128: launch_f32_bwd_d<128>(q, k, v, dout, lse, delta, dq, dk, dv, se, mp, sh, stream); break;
+        case 32: launch_f32_bwd_d<32>(phase, q, k, v, dout, lse, delta, dq, dk, dv, se, mp, sh, stream); break;
+        case 64: launch_f32_bwd_d<64>(phase, q, k, v, dout, lse, delta, dq, dk, dv, se, mp, sh, stream); break;
+        case 128: launch_f32_bwd_d<128>(phase, q, k, v, dout, lse, delta, dq, dk, dv, se, mp, sh, stream); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -445,23 +445,27 @@ __global__ __launch_bounds__(kThreads, 1) void dq_bf16_kernel(
 }
 
 template <int D>
-hipError_t launch_bwd_d(const bf16* Q, const bf16* K, const bf16* V, const bf16* O, const float* lse,
+hipError_t launch_bwd_d(int phase, const bf16* Q, const bf16* K, const bf16* V, const bf16* O, const float* lse,
                         const bf16* dO, bf16* dQ, bf16* dK, bf16* dV, const int32_t* se, const MetaPtrs& mp,
                         float* delta, const AttnShape& sh, hipStream_t stream) {
     const int L = int(sh.L);
     const int64_t rows = int64_t(L) * sh.Hq;
     const float sl2 = sh.scale * kLog2e;
-    delta_bf16_kernel<D><<<unsigned((rows + 255) / 256), 256, 0, stream>>>(O, dO, delta, L, sh.Hq);
-    dkdv_bf16_kernel<D><<<unsigned(sh.nb) * unsigned(sh.Hkv), kThreads, 0, stream>>>(
-        Q, K, V, dO, lse, delta, dK, dV, se, mp.k_order, mp.col_ptr, mp.col_ent, L, sh.Hq, sh.Hkv, sl2, sh.scale);
-    dq_bf16_kernel<D><<<unsigned(sh.nb) * unsigned(sh.Hq), kThreads, 0, stream>>>(
-        Q, K, V, dO, lse, delta, dQ, se, mp.q_order, mp.row_ptr, mp.row_ent, L, sh.Hq, sh.Hkv, sl2, sh.scale);
+    if (phase == kPhaseAll || phase == kPhaseDelta)
+        delta_bf16_kernel<D><<<unsigned((rows + 255) / 256), 256, 0, stream>>>(O, dO, delta, L, sh.Hq);
+    if (phase == kPhaseAll || phase == kPhaseDkdv)
+        dkdv_bf16_kernel<D><<<unsigned(sh.nb) * unsigned(sh.Hkv), kThreads, 0, stream>>>(
+            Q, K, V, dO, lse, delta, dK, dV, se, mp.k_order, mp.col_ptr, mp.col_ent, L, sh.Hq, sh.Hkv, sl2,
+            sh.scale);
+    if (phase == kPhaseAll || phase == kPhaseDq)
+        dq_bf16_kernel<D><<<unsigned(sh.nb) * unsigned(sh.Hq), kThreads, 0, stream>>>(
+            Q, K, V, dO, lse, delta, dQ, se, mp.q_order, mp.row_ptr, mp.row_ent, L, sh.Hq, sh.Hkv, sl2, sh.scale);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+hipError_t launch_bwd_bf16(int phase, const void* q, const void* k, const void* v, const void* o, const float* lse,
                            const void* dout, void* dq, void* dk, void* dv, const int32_t* se, const MetaPtrs& mp,
                            float* delta, const AttnShape& sh, hipStream_t stream) {
     const auto* Q = static_cast<const bf16*>(q);
@@ -472,8 +476,8 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
     auto* dQ = static_cast<bf16*>(dq);
     auto* dK = static_cast<bf16*>(dk);
     auto* dV = static_cast<bf16*>(dv);
-    if (sh.D == 128) return launch_bwd_d<128>(Q, K, V, O, lse, G, dQ, dK, dV, se, mp, delta, sh, stream);
-    if (sh.D == 64) return launch_bwd_d<64>(Q, K, V, O, lse, G, dQ, dK, dV, se, mp, delta, sh, stream);
+    if (sh.D == 128) return launch_bwd_d<128>(phase, Q, K, V, O, lse, G, dQ, dK, dV, se, mp, delta, sh, stream);
+    if (sh.D == 64) return launch_bwd_d<64>(phase, Q, K, V, O, lse, G, dQ, dK, dV, se, mp, delta, sh, stream);
     return hipErrorInvalidValue;
 }
 

@@ -124,6 +124,16 @@ int tree_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
                   void* dq, void* dk, void* dv, const int32_t* d_se, const void* d_meta_ws, void* d_ws,
                   size_t ws_bytes, int64_t L, int32_t Hq, int32_t Hkv, int32_t D, float scale, int32_t dtype,
                   void* stream) {
+    return tree_attn_bwd_phase(TREE_BWD_ALL, q, k, v, o, lse, dout, dq, dk, dv, d_se, d_meta_ws, d_ws, ws_bytes, L,
+                               Hq, Hkv, D, scale, dtype, stream);
+}
+
+int tree_attn_bwd_phase(int32_t phase, const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv, const int32_t* d_se,
+                        const void* d_meta_ws, void* d_ws, size_t ws_bytes, int64_t L, int32_t Hq, int32_t Hkv,
+                        int32_t D, float scale, int32_t dtype, void* stream) {
+    if (phase < TREE_BWD_ALL || phase > TREE_BWD_DQ)
+        return set_error(TREE_E_ARG, "tree_attn_bwd: unknown phase %d", phase);
     if (int rc = check_attn("tree_attn_bwd", L, Hq, Hkv, D, scale, dtype)) return rc;
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !d_se || !d_meta_ws || !d_ws)
         return set_error(TREE_E_ARG, "tree_attn_bwd: NULL device pointer");
@@ -140,12 +150,12 @@ int tree_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
     float* delta = static_cast<float*>(d_ws);
     hipError_t e;
     if (dtype == TREE_DTYPE_BF16)
-        e = launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, d_se, mp, delta, sh, s);
+        e = launch_bwd_bf16(phase, q, k, v, o, lse, dout, dq, dk, dv, d_se, mp, delta, sh, s);
     else
-        e = launch_bwd_f32(static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
-                           static_cast<const float*>(o), lse, static_cast<const float*>(dout),
-                           static_cast<float*>(dq), static_cast<float*>(dk), static_cast<float*>(dv), d_se, mp,
-                           delta, sh, s);
+        e = launch_bwd_f32(phase, static_cast<const float*>(q), static_cast<const float*>(k),
+                           static_cast<const float*>(v), static_cast<const float*>(o), lse,
+                           static_cast<const float*>(dout), static_cast<float*>(dq), static_cast<float*>(dk),
+                           static_cast<float*>(dv), d_se, mp, delta, sh, s);
     return hip_status(e, "tree_attn_bwd");
 }
 

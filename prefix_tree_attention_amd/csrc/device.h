@@ -74,6 +74,9 @@ inline MetaPtrs meta_ptrs(const void* ws, int64_t L) {
     return {w + m.row_ptr, w + m.row_ent, w + m.col_ptr, w + m.col_ent, w + m.q_order, w + m.k_order};
 }
 
+// Backward phases (TREE_BWD_* of the public header).
+constexpr int kPhaseAll = 0, kPhaseDelta = 1, kPhaseDkdv = 2, kPhaseDq = 3;
+
 // Problem shape shared by the attention launchers.
 struct AttnShape {
     int64_t L;
@@ -87,14 +90,14 @@ hipError_t launch_meta(const int32_t* se, int64_t L, int32_t* pos, uint8_t* tile
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            const int32_t* se, const MetaPtrs& mp, const AttnShape& sh,
                            hipStream_t stream);
-hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+hipError_t launch_bwd_bf16(int phase, const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
                            const int32_t* se, const MetaPtrs& mp, float* delta,
                            const AttnShape& sh, hipStream_t stream);
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                           const int32_t* se, const MetaPtrs& mp, const AttnShape& sh,
                           hipStream_t stream);
-hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* o,
+hipError_t launch_bwd_f32(int phase, const float* q, const float* k, const float* v, const float* o,
                           const float* lse, const float* dout, float* dq, float* dk, float* dv,
                           const int32_t* se, const MetaPtrs& mp, float* delta,
                           const AttnShape& sh, hipStream_t stream);

@@ -31,24 +31,19 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Round-to-nearest-even float -> bf16 bits (inputs here are finite).
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// Two floats -> packed bf16 (round to nearest even; one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return bf16_bits(lo) | (bf16_bits(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 // Eight floats -> one bf16x8 operand.
 __device__ __forceinline__ bf16x8 to_bf16x8(const f32x4& lo, const f32x4& hi) {
-    u32x4 w;
-    w[0] = pack_bf16x2(lo[0], lo[1]);
-    w[1] = pack_bf16x2(lo[2], lo[3]);
-    w[2] = pack_bf16x2(hi[0], hi[1]);
-    w[3] = pack_bf16x2(hi[2], hi[3]);
-    return __builtin_bit_cast(bf16x8, w);
+    const f32x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_convertvector(v, bf16x8);
 }
 
 __device__ __forceinline__ float bf16_to_float(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
