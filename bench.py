@@ -5,11 +5,12 @@ One step is one pass of the whole path over one synthetic rollout batch:
   host   tree_pack (C++ FFD trie build, compression, pre-order layout)
   H2D    subtree ends of every trie (pinned, async)
   device tree_meta, tree_attn_fwd, tree_attn_bwd (delta, dK/dV, dQ)
-Q, K, V and dO are resident in HBM before the timed region.  Steps are
-enqueued back to back, so the host packing of step k+1 overlaps the GPU work
-of step k (the trie-count all-reduce of a data-parallel run would sit at the
-same point).  Each kernel phase is bracketed by HIP events on the stream
-the library launches on.
+Q, K, V and dO are resident in HBM before the timed region.  The loop is a
+steady-state pipeline: step k's device work is enqueued, then the host packs
+step k+1 while the GPU runs (the trie-count all-reduce of a data-parallel
+run would sit at the same point); each timed iteration holds one step's
+device work and one pack.  Each kernel phase is bracketed by HIP events on
+the stream the library launches on.
 
 Prints ONE JSON line.  ``value`` is real packed tokens per second through
 fwd+bwd; useful TFLOP/s counts 14 * D * Hq per visible (query, key) pair
@@ -179,8 +180,8 @@ def main(argv=None):
     sptr = ctypes.c_void_p(stream.cuda_stream)
     scale = 1.0 / math.sqrt(w.d)
 
-    def step(k_step, events):
-        cur, _ = pta.pack(w.ids, w.mask, w.max_tokens_per_mb)
+    def launch(k_step, cur, events):
+        """Enqueue one step's device work for the pack `cur`."""
         assert len(cur) == len(bufs)
         slot = k_step % 2
         for i, tr in enumerate(cur):
@@ -215,16 +216,29 @@ def main(argv=None):
             if events is not None:
                 events.append((i, E))
 
+    def pack_host():
+        cur, _ = pta.pack(w.ids, w.mask, w.max_tokens_per_mb)
+        return cur
+
+    # Steady-state pipeline: the device work of step k is enqueued, then the
+    # host packs step k+1 while the GPU runs.  Each timed iteration holds one
+    # step's device work and one pack.
+    pending = pack_host()
     for k_step in range(a.warmup):
-        step(k_step, None)
+        launch(k_step, pending, None)
+        pending = pack_host()
     torch.cuda.synchronize()
     log(f"warmup done ({a.warmup} steps)")
 
     events = []
+    t_pack = 0.0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k_step in range(a.steps):
-        step(a.warmup + k_step, events)
+        launch(a.warmup + k_step, pending, events)
+        tp = time.perf_counter()
+        pending = pack_host()
+        t_pack += time.perf_counter() - tp
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     sec_per_step = (t1 - t0) / a.steps
@@ -277,6 +291,7 @@ def main(argv=None):
         "flop_reduction_vs_unpacked": round(stats["unpacked_pairs"] / n_pairs, 3),
         "tree_token_ratio": round(stats["tree_token_ratio"], 4),
         "gpu_ms_per_step": round(gpu_ms_per_step, 3),
+        "host_pack_ms_per_step": round(t_pack / a.steps * 1e3, 3),
         "kernel_ms_per_launch": {p: round(avg[p], 4) for p in PHASES},
         "config": {"workload": w.name, "tries": len(bufs), "L": [b["L"] for b in bufs], "hq": w.hq,
                    "hkv": w.hkv, "head_dim": w.d, "max_tokens_per_mb": w.max_tokens_per_mb,

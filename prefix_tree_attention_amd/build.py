@@ -34,7 +34,8 @@ CXX_SOURCES = ["capi.cpp", "pack.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC]
 HIP_FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
-             "-packed-fp32-ops", "-ffast-math", "-fno-finite-math-only", "-munsafe-fp-atomics"]
+             "-packed-fp32-ops", "-ffast-math", "-fno-finite-math-only", "-munsafe-fp-atomics",
+             "-mllvm", "-amdgpu-mfma-vgpr-form"]
 CXX_FLAGS = ["-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"), "-Wall", "-Wextra"]
 
 

@@ -12,102 +12,36 @@
 // Three kernels:
 //   delta: Delta for every (token, query head).
 //   dkdv:  one workgroup per (128-key block, key/value head); wave w owns
-//          keys 32w..32w+31 and keeps K, V, dK^T, dV^T in registers.  It
-//          walks the nonempty tiles of its key block (column list) for each
-//          query head of the group, 64 queries per step, with Q, dO (rows
-//          permuted for the score products) and Q^T, dO^T (for the
-//          gradient products) staged in double-buffered LDS.
-//            S = Q K^T, dP = dO V^T   (A = Q / dO rows, B = K^T / V^T regs)
-//            dV^T += dO^T P, dK^T += Q^T dS   (A = dO^T / Q^T rows, B = P / dS
-//            straight from the score accumulators)
+//          keys 32w..32w+31 and keeps K^T, V^T operands and the dK^T, dV^T
+//          accumulators in registers.  It walks the nonempty tiles of its
+//          key block (column list) for each query head of the group, 64
+//          queries per step; Q and dO (and LSE, Delta) of a step go HBM ->
+//          LDS by direct loads into double-buffered swizzled tiles.
+//            S = Q K^T, dP = dO V^T      (A = Q / dO rows of the tiles)
+//            dV^T += dO^T P, dK^T += Q^T dS
+//          (A = dO^T / Q^T by transposing LDS reads of the same tiles,
+//          B = P / dS straight from the score accumulators).
 //   dq:    one workgroup per (128-query block, query head) like the forward:
-//            S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
-// The row permutation that lets a score accumulator serve directly as the
-// next product's operand is the forward's: MFMA row 16b + m of a 64-row
-// step holds token 32c + 8(m/4) + 4e + (m%4), b = 2c + e.
+//            S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T,
+//          K^T again by transposing reads of the K tile.
+// Score block b of a 64-row step covers rows 16b..16b+15; the gradient
+// products' k-step c pairs blocks 2c and 2c+1, whose accumulator lanes hold
+// rows 32c + 4g + 0..3 and 32c + 16 + 4g + 0..3 -- exactly the rows the
+// transposing reads fetch.
 
 #include <cmath>
+#include <type_traits>
 
 #include "device.h"
 #include "mfma.h"
+#include "tile.h"
 
 namespace treeattn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kStep = 64;
+constexpr int kStep = kTileRows;
 constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ int perm_row(int tok) {
-    const int c = tok >> 5, w = tok & 31;
-    return 16 * (2 * c + ((w >> 2) & 1)) + 4 * (w >> 3) + (w & 3);
-}
-
-// ---------------------------------------------------------------------------
-// staging helpers: a 64-row x D tile of a [token][head][D] tensor
-// ---------------------------------------------------------------------------
-// "Quad" pattern: thread (qg = tid % 16, ch = tid / 16) loads rows 4qg..4qg+3
-// at d-chunk ch; it can write the rows (permuted) and the transpose.
-template <int D>
-struct Quad {
-    u32x4 r[4];
-};
-
-template <int D>
-__device__ __forceinline__ void quad_load(Quad<D>& x, const bf16* __restrict__ base, int64_t tok_stride, int row0,
-                                          int tid) {
-    if (tid < 2 * D) {
-        const int qg = tid & 15, ch = tid >> 4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) x.r[r] = ld16(base + int64_t(row0 + 4 * qg + r) * tok_stride + 8 * ch);
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void quad_store_rows(const Quad<D>& x, bf16 (*rows)[D + 8], int tid) {
-    if (tid < 2 * D) {
-        const int qg = tid & 15, ch = tid >> 4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st16(&rows[perm_row(4 * qg + r)][8 * ch], x.r[r]);
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void quad_store_t(const Quad<D>& x, bf16 (*cols)[kStep + 8], int tid) {
-    if (tid < 2 * D) {
-        const int qg = tid & 15, ch = tid >> 4;
-        u32x2 t[8];
-        transpose4x8(x.r, t);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) st8(&cols[8 * ch + j][4 * qg], t[j]);
-    }
-}
-
-// "Flat" pattern: 16-byte chunks, consecutive threads along a row.
-template <int D>
-struct Flat {
-    static constexpr int kItems = kStep * (D / 8) / kThreads;
-    u32x4 r[kItems];
-};
-
-template <int D>
-__device__ __forceinline__ void flat_load(Flat<D>& x, const bf16* __restrict__ base, int64_t tok_stride, int row0,
-                                          int tid) {
-#pragma unroll
-    for (int i = 0; i < Flat<D>::kItems; ++i) {
-        const int it = tid + kThreads * i;
-        x.r[i] = ld16(base + int64_t(row0 + it / (D / 8)) * tok_stride + 8 * (it % (D / 8)));
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void flat_store_rows(const Flat<D>& x, bf16 (*rows)[D + 8], int tid) {
-#pragma unroll
-    for (int i = 0; i < Flat<D>::kItems; ++i) {
-        const int it = tid + kThreads * i;
-        st16(&rows[perm_row(it / (D / 8))][8 * (it % (D / 8))], x.r[i]);
-    }
-}
 
 // ---------------------------------------------------------------------------
 // Delta = rowsum(dO * O)
@@ -130,19 +64,15 @@ __global__ __launch_bounds__(256) void delta_bf16_kernel(const bf16* __restrict_
     delta[int64_t(r % Hq) * L + r / Hq] = acc;
 }
 
+// direct load of 64 consecutive floats (one wave)
+__device__ __forceinline__ void load_row64_async(lds_char* dst, const float* __restrict__ src, int lane) {
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + lane), reinterpret_cast<lds_void*>(dst), 4, 0,
+                                     0);
+}
+
 // ---------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------
-template <int D>
-struct DkvSmem {
-    bf16 q[2][kStep][D + 8];
-    bf16 g[2][kStep][D + 8];
-    bf16 qt[2][D][kStep + 8];
-    bf16 gt[2][D][kStep + 8];
-    float lse2[2][kStep];
-    float dl[2][kStep];
-};
-
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
@@ -150,9 +80,14 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
     bf16* __restrict__ dK, bf16* __restrict__ dV, const int32_t* __restrict__ se,
     const int32_t* __restrict__ k_order, const int32_t* __restrict__ col_ptr,
     const int32_t* __restrict__ col_ent, int L, int Hq, int Hkv, float scale_log2, float scale) {
+    using T = Tile<D>;
     constexpr int NS = D / 32, NT = D / 16;
-    __shared__ DkvSmem<D> sm;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int kStage = 2 * T::kBytes + 512;  // Q tile, dO tile, LSE[64], Delta[64]
+    __shared__ __attribute__((aligned(1024))) char smem_raw[2 * kStage];
+    lds_char* const smem = (lds_char*)smem_raw;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, g = lane >> 4;
     const int rank = blockIdx.x / Hkv, hkv = blockIdx.x % Hkv;
     const int kb = k_order[rank];
@@ -180,34 +115,24 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
         for (int t = 0; t < NT; ++t) dk[ks][t] = dv[ks][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int beg = col_ptr[kb], nsteps = (col_ptr[kb + 1] - beg) * 2 * G;
+    const int qs32 = int(q_stride);
+    auto qtile = [&](int buf) { return smem + buf * kStage; };
+    auto gtile = [&](int buf) { return smem + buf * kStage + T::kBytes; };
+    auto lsev = [&](int buf) { return smem + buf * kStage + 2 * T::kBytes; };
+    auto dlv = [&](int buf) { return smem + buf * kStage + 2 * T::kBytes + 256; };
     // step st: tile col_ent[beg + st / 2G], query half (st / G) % 2, head hkv G + st % G
-    Quad<D> pq, pg;
-    float plse = 0.f, pdl = 0.f;
-    auto load = [&](int st) {
+    auto issue = [&](int st, int buf) {
         const int ent = col_ent[beg + st / (2 * G)];
         const int qbase = (ent >> 1) * kBlock + kStep * ((st / G) & 1);
         const int h = hkv * G + st % G;
-        quad_load<D>(pq, Q + int64_t(h) * D, q_stride, qbase, tid);
-        quad_load<D>(pg, dO + int64_t(h) * D, q_stride, qbase, tid);
-        if (tid < kStep) {
-            plse = LSE[int64_t(h) * L + qbase + tid] * kLog2e;
-            pdl = Delta[int64_t(h) * L + qbase + tid];
-        }
+        const int64_t off = int64_t(qbase) * q_stride + int64_t(h) * D;
+        T::load_async(qtile(buf), Q + off, qs32, wave, lane);
+        T::load_async(gtile(buf), dO + off, qs32, wave, lane);
+        if (wave == 0) load_row64_async(lsev(buf), LSE + int64_t(h) * L + qbase, lane);
+        if (wave == 1) load_row64_async(dlv(buf), Delta + int64_t(h) * L + qbase, lane);
     };
-    auto store = [&](int buf) {
-        quad_store_rows<D>(pq, sm.q[buf], tid);
-        quad_store_rows<D>(pg, sm.g[buf], tid);
-        quad_store_t<D>(pq, sm.qt[buf], tid);
-        quad_store_t<D>(pg, sm.gt[buf], tid);
-        if (tid < kStep) {
-            sm.lse2[buf][tid] = plse;
-            sm.dl[buf][tid] = pdl;
-        }
-    };
-    if (nsteps > 0) {
-        load(0);
-        store(0);
-    }
+    if (nsteps > 0) issue(0, 0);
+    wait_vm_all();
     __syncthreads();
 
     for (int st = 0; st < nsteps; ++st) {
@@ -215,76 +140,89 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
         const int ent = col_ent[beg + st / (2 * G)];
         const int qbase = (ent >> 1) * kBlock + kStep * ((st / G) & 1);
         const bool partial = ent & 1;
-        if (st + 1 < nsteps) load(st + 1);
+        if (st + 1 < nsteps) issue(st + 1, buf ^ 1);
+        const lds_char* qt = qtile(buf);
+        const lds_char* gt = gtile(buf);
+        const lds_char* lsp = lsev(buf);
+        const lds_char* dlp = dlv(buf);
 
-        f32x4 s[2][4], dp[2][4];
+        // two halves of 32 queries: blocks b = 2c, 2c+1 feed k-step c of the
+        // gradient products
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            bf16x8 aq[NS], ag[NS];
-#pragma unroll
-            for (int x = 0; x < NS; ++x) {
-                aq[x] = *reinterpret_cast<const bf16x8*>(&sm.q[buf][16 * b + n][32 * x + 8 * g]);
-                ag[x] = *reinterpret_cast<const bf16x8*>(&sm.g[buf][16 * b + n][32 * x + 8 * g]);
-            }
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                f32x4 cs = {0.f, 0.f, 0.f, 0.f}, cd = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int x = 0; x < NS; ++x) {
-                    cs = mfma16x16x32(aq[x], kf[ks][x], cs);
-                    cd = mfma16x16x32(ag[x], vf[ks][x], cd);
-                }
-                s[ks][b] = cs;
-                dp[ks][b] = cd;
-            }
-        }
-        // lane's queries for block b = 2c + e: qbase + 32c + 8g + 4e + 0..3
-        f32x4 l2[2][2], dl[2][2];
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < 2; ++c) {
+            f32x4 s[2][2], dp[2][2];  // [ks][e]: lane = key column, queries 32c + 16e + 4g + 0..3
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                l2[c][e] = *reinterpret_cast<const f32x4*>(&sm.lse2[buf][32 * c + 8 * g + 4 * e]);
-                dl[c][e] = *reinterpret_cast<const f32x4*>(&sm.dl[buf][32 * c + 8 * g + 4 * e]);
-            }
+                const int b = 2 * c + e;
+                bf16x8 aq[NS], ag[NS];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int key = kw0 + 16 * ks + n;
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float p = fast_exp2(s[ks][b][r] * scale_log2 - l2[b >> 1][b & 1][r]);
-                    if (partial) {
-                        const int qi = qbase + 32 * (b >> 1) + 8 * g + 4 * (b & 1) + r;
-                        p = (key <= qi && qi <= sek[ks]) ? p : 0.f;
-                    }
-                    s[ks][b][r] = p;
-                    dp[ks][b][r] = p * (dp[ks][b][r] - dl[b >> 1][b & 1][r]);
+                for (int x = 0; x < NS; ++x) {
+                    aq[x] = T::row_frag(qt, 16 * b + n, 4 * x + g);
+                    ag[x] = T::row_frag(gt, 16 * b + n, 4 * x + g);
                 }
-        }
-        bf16x8 pb[2][2], db[2][2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                pb[ks][c] = to_bf16x8(s[ks][2 * c], s[ks][2 * c + 1]);
-                db[ks][c] = to_bf16x8(dp[ks][2 * c], dp[ks][2 * c + 1]);
-            }
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const bf16x8 ag = *reinterpret_cast<const bf16x8*>(&sm.gt[buf][16 * t + n][32 * c + 8 * g]);
-                const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sm.qt[buf][16 * t + n][32 * c + 8 * g]);
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    dv[ks][t] = mfma16x16x32(ag, pb[ks][c], dv[ks][t]);
-                    dk[ks][t] = mfma16x16x32(aq, db[ks][c], dk[ks][t]);
+                    f32x4 cs = {0.f, 0.f, 0.f, 0.f}, cd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int x = 0; x < NS; ++x) {
+                        cs = mfma16x16x32(aq[x], kf[ks][x], cs);
+                        cd = mfma16x16x32(ag[x], vf[ks][x], cd);
+                    }
+                    s[ks][e] = cs;
+                    dp[ks][e] = cd;
                 }
             }
+            f32x4 l2[2], dl[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                l2[e] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+                            lsp + 4 * (32 * c + 16 * e + 4 * g)) * kLog2e;
+                dl[e] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+                    dlp + 4 * (32 * c + 16 * e + 4 * g));
+            }
+            bf16x8 pb[2], db[2];
+            // P = exp2(scale log2e S - LSE log2e), dS = P (dP - Delta); the
+            // subtree-interval predicate only in partial tiles (separate code
+            // path so full tiles carry no mask arithmetic)
+            auto elementwise = [&](auto masked) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int key = kw0 + 16 * ks + n;
+#pragma unroll
+                    for (int e = 0; e < 2; ++e)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            float p = fast_exp2(__builtin_fmaf(s[ks][e][r], scale_log2, -l2[e][r]));
+                            if constexpr (decltype(masked)::value) {
+                                const int qi = qbase + 32 * c + 16 * e + 4 * g + r;
+                                p = (key <= qi && qi <= sek[ks]) ? p : 0.f;
+                            }
+                            s[ks][e][r] = p;
+                            dp[ks][e][r] = p * (dp[ks][e][r] - dl[e][r]);
+                        }
+                    pb[ks] = to_bf16x8(s[ks][0], s[ks][1]);
+                    db[ks] = to_bf16x8(dp[ks][0], dp[ks][1]);
+                }
+            };
+            if (partial)
+                elementwise(std::true_type{});
+            else
+                elementwise(std::false_type{});
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const bf16x8 ag = join_tr(T::tr_frag(gt, 32 * c + 4 * g, 16 * t, n),
+                                          T::tr_frag(gt, 32 * c + 16 + 4 * g, 16 * t, n));
+                const bf16x8 aq = join_tr(T::tr_frag(qt, 32 * c + 4 * g, 16 * t, n),
+                                          T::tr_frag(qt, 32 * c + 16 + 4 * g, 16 * t, n));
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    dv[ks][t] = mfma16x16x32(ag, pb[ks], dv[ks][t]);
+                    dk[ks][t] = mfma16x16x32(aq, db[ks], dk[ks][t]);
+                }
+            }
+        }
 
-        if (st + 1 < nsteps) store(buf ^ 1);
+        wait_vm_all();
         __syncthreads();
     }
 
@@ -305,22 +243,19 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
 // dQ
 // ---------------------------------------------------------------------------
 template <int D>
-struct DqSmem {
-    bf16 k[2][kStep][D + 8];
-    bf16 v[2][kStep][D + 8];
-    bf16 kt[2][D][kStep + 8];
-};
-
-template <int D>
-__global__ __launch_bounds__(kThreads, 1) void dq_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 2) void dq_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     bf16* __restrict__ dQ, const int32_t* __restrict__ se, const int32_t* __restrict__ q_order,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ row_ent, int L, int Hq, int Hkv,
     float scale_log2, float scale) {
+    using T = Tile<D>;
     constexpr int NS = D / 32, NT = D / 16;
-    __shared__ DqSmem<D> sm;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[4 * T::kBytes];
+    lds_char* const smem = (lds_char*)smem_raw;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, g = lane >> 4;
     const int rank = blockIdx.x / Hq, h = blockIdx.x % Hq;
     const int qb = q_order[rank];
@@ -348,22 +283,17 @@ __global__ __launch_bounds__(kThreads, 1) void dq_bf16_kernel(
         for (int t = 0; t < NT; ++t) dq[qs][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int beg = row_ptr[qb], nsteps = 2 * (row_ptr[qb + 1] - beg);
-    Quad<D> pk;
-    Flat<D> pv;
-    auto load = [&](int st) {
+    const int kvs = int(kv_stride);
+    auto ktile = [&](int buf) { return smem + (2 * buf) * T::kBytes; };
+    auto vtile = [&](int buf) { return smem + (2 * buf + 1) * T::kBytes; };
+    auto issue = [&](int st, int buf) {
         const int kbase = (row_ent[beg + (st >> 1)] >> 1) * kBlock + kStep * (st & 1);
-        quad_load<D>(pk, K + hkv * D, kv_stride, kbase, tid);
-        flat_load<D>(pv, V + hkv * D, kv_stride, kbase, tid);
+        const int64_t off = int64_t(kbase) * kv_stride + int64_t(hkv) * D;
+        T::load_async(ktile(buf), K + off, kvs, wave, lane);
+        T::load_async(vtile(buf), V + off, kvs, wave, lane);
     };
-    auto store = [&](int buf) {
-        quad_store_rows<D>(pk, sm.k[buf], tid);
-        quad_store_t<D>(pk, sm.kt[buf], tid);
-        flat_store_rows<D>(pv, sm.v[buf], tid);
-    };
-    if (nsteps > 0) {
-        load(0);
-        store(0);
-    }
+    if (nsteps > 0) issue(0, 0);
+    wait_vm_all();
     __syncthreads();
 
     for (int st = 0; st < nsteps; ++st) {
@@ -371,65 +301,74 @@ __global__ __launch_bounds__(kThreads, 1) void dq_bf16_kernel(
         const int ent = row_ent[beg + (st >> 1)];
         const int kbase = (ent >> 1) * kBlock + kStep * (st & 1);
         const bool partial = ent & 1;
-        if (st + 1 < nsteps) load(st + 1);
+        if (st + 1 < nsteps) issue(st + 1, buf ^ 1);
+        const lds_char* kt = ktile(buf);
+        const lds_char* vt = vtile(buf);
 
-        f32x4 s[2][4], dp[2][4];
+        // two halves of 32 keys: blocks b = 2c, 2c+1 feed k-step c of dQ^T
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            bf16x8 ak[NS], av[NS];
+        for (int c = 0; c < 2; ++c) {
+            f32x4 s[2][2], dp[2][2];  // [qs][e]: lane = query column, keys 32c + 16e + 4g + 0..3
 #pragma unroll
-            for (int x = 0; x < NS; ++x) {
-                ak[x] = *reinterpret_cast<const bf16x8*>(&sm.k[buf][16 * b + n][32 * x + 8 * g]);
-                av[x] = *reinterpret_cast<const bf16x8*>(&sm.v[buf][16 * b + n][32 * x + 8 * g]);
-            }
-#pragma unroll
-            for (int qs = 0; qs < 2; ++qs) {
-                f32x4 cs = {0.f, 0.f, 0.f, 0.f}, cd = {0.f, 0.f, 0.f, 0.f};
+            for (int e = 0; e < 2; ++e) {
+                const int b = 2 * c + e;
+                bf16x8 ak[NS], av[NS];
 #pragma unroll
                 for (int x = 0; x < NS; ++x) {
-                    cs = mfma16x16x32(ak[x], qf[qs][x], cs);
-                    cd = mfma16x16x32(av[x], gf[qs][x], cd);
+                    ak[x] = T::row_frag(kt, 16 * b + n, 4 * x + g);
+                    av[x] = T::row_frag(vt, 16 * b + n, 4 * x + g);
                 }
-                s[qs][b] = cs;
-                dp[qs][b] = cd;
-            }
-        }
-        i32x4 sek[2][2];
-        if (partial) {
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                sek[c][0] = *reinterpret_cast<const i32x4*>(se + kbase + 32 * c + 8 * g);
-                sek[c][1] = *reinterpret_cast<const i32x4*>(se + kbase + 32 * c + 8 * g + 4);
-            }
-        }
-        bf16x8 db[2][2];
+                for (int qs = 0; qs < 2; ++qs) {
+                    f32x4 cs = {0.f, 0.f, 0.f, 0.f}, cd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
-            const int qi = qrow0 + 16 * qs + n;
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float p = fast_exp2(s[qs][b][r] * scale_log2 - lse2[qs]);
-                    if (partial) {
-                        const int key = kbase + 32 * (b >> 1) + 8 * g + 4 * (b & 1) + r;
-                        p = (key <= qi && qi <= sek[b >> 1][b & 1][r]) ? p : 0.f;
+                    for (int x = 0; x < NS; ++x) {
+                        cs = mfma16x16x32(ak[x], qf[qs][x], cs);
+                        cd = mfma16x16x32(av[x], gf[qs][x], cd);
                     }
-                    dp[qs][b][r] = p * (dp[qs][b][r] - dlt[qs]);
+                    s[qs][e] = cs;
+                    dp[qs][e] = cd;
                 }
-            db[qs][0] = to_bf16x8(dp[qs][0], dp[qs][1]);
-            db[qs][1] = to_bf16x8(dp[qs][2], dp[qs][3]);
-        }
+            }
+            bf16x8 db[2];
+            auto elementwise = [&](auto masked) {
+                i32x4 sek[2];
+                if constexpr (decltype(masked)::value) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+                    for (int e = 0; e < 2; ++e)
+                        sek[e] = *reinterpret_cast<const i32x4*>(se + kbase + 32 * c + 16 * e + 4 * g);
+                }
+#pragma unroll
+                for (int qs = 0; qs < 2; ++qs) {
+                    const int qi = qrow0 + 16 * qs + n;
+#pragma unroll
+                    for (int e = 0; e < 2; ++e)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            float p = fast_exp2(__builtin_fmaf(s[qs][e][r], scale_log2, -lse2[qs]));
+                            if constexpr (decltype(masked)::value) {
+                                const int key = kbase + 32 * c + 16 * e + 4 * g + r;
+                                p = (key <= qi && qi <= sek[e][r]) ? p : 0.f;
+                            }
+                            dp[qs][e][r] = p * (dp[qs][e][r] - dlt[qs]);
+                        }
+                    db[qs] = to_bf16x8(dp[qs][0], dp[qs][1]);
+                }
+            };
+            if (partial)
+                elementwise(std::true_type{});
+            else
+                elementwise(std::false_type{});
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.kt[buf][16 * t + n][32 * c + 8 * g]);
+                const bf16x8 a = join_tr(T::tr_frag(kt, 32 * c + 4 * g, 16 * t, n),
+                                         T::tr_frag(kt, 32 * c + 16 + 4 * g, 16 * t, n));
 #pragma unroll
-                for (int qs = 0; qs < 2; ++qs) dq[qs][t] = mfma16x16x32(a, db[qs][c], dq[qs][t]);
+                for (int qs = 0; qs < 2; ++qs) dq[qs][t] = mfma16x16x32(a, db[qs], dq[qs][t]);
             }
+        }
 
-        if (st + 1 < nsteps) store(buf ^ 1);
+        wait_vm_all();
         __syncthreads();
     }
 

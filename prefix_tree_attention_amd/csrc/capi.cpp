@@ -51,7 +51,8 @@ int check_attn(const char* fn, int64_t L, int32_t Hq, int32_t Hkv, int32_t D, fl
     } else {
         return set_error(TREE_E_ARG, "%s: unknown dtype %d", fn, dtype);
     }
-    if (!std::isfinite(scale)) return set_error(TREE_E_ARG, "%s: scale must be finite", fn);
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return set_error(TREE_E_ARG, "%s: scale must be finite and positive", fn);
     return TREE_OK;
 }
 

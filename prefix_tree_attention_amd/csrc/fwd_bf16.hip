@@ -9,83 +9,32 @@
 // Work decomposition: one workgroup (4 waves) per (128-query block, query
 // head); wave w owns queries 32w..32w+31 of the block as two 16-column MFMA
 // groups.  The workgroup walks only the nonempty key tiles of its query
-// block (row list of the metadata), 64 keys per pipeline step, with K and
-// V^T staged through double-buffered LDS.  Partial tiles apply the
+// block (row list of the metadata), 64 keys per pipeline step.  K and V of a
+// step go HBM -> LDS by direct loads into double-buffered swizzled tiles
+// (tile.h) while the previous step computes.  Partial tiles apply the
 // subtree-interval predicate; full tiles skip it.
 //
 // Products are computed transposed: S^T = K Q^T (A = K rows from LDS, B =
-// Q^T held in registers), O^T = V^T P^T (A = V^T rows from LDS, B = P^T
-// taken straight from the S^T accumulators).  Each lane thus owns one query
-// column, so softmax statistics need only an in-lane reduction plus two
-// cross-lane steps, and the rescaling of O^T is per lane.  For the S^T
-// accumulators to be usable as the P^T operand, MFMA row (16b + m) of a
-// 64-key step holds key 32c + 8(m/4) + 4e + (m%4) with b = 2c + e; K is
-// written to LDS in that row order.  Softmax runs in base 2 with
-// scale*log2(e) folded into the scores.
+// Q^T held in registers), O^T = V^T P^T (A = V^T read from the row-major V
+// tile by transposing LDS loads, B = P^T taken straight from the S^T
+// accumulators).  Each lane thus owns one query column, so softmax
+// statistics need only an in-lane reduction plus two cross-lane steps, and
+// the rescaling of O^T is per lane.  S^T block b covers keys 16b..16b+15;
+// k-step c of the PV product pairs blocks 2c and 2c+1, and the transposing
+// reads of V take exactly the key rows those accumulator lanes hold.
+// Softmax runs in base 2 with scale*log2(e) folded into one FMA.
 
 #include <cmath>
 
 #include "device.h"
 #include "mfma.h"
+#include "tile.h"
 
 namespace treeattn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kStep = 64;  // keys per pipeline step
-
-// LDS row of key (0..63) within a step, see the file comment.
-__device__ __forceinline__ int k_lds_row(int key) {
-    const int c = key >> 5, w = key & 31;
-    return 16 * (2 * c + ((w >> 2) & 1)) + 4 * (w >> 3) + (w & 3);
-}
-
-template <int D>
-struct FwdSmem {
-    bf16 k[2][kStep][D + 8];   // +16 B per row: conflict-free 16-byte row reads
-    bf16 vt[2][D][kStep + 8];  // V transposed: [d][key]
-};
-
-template <int D>
-struct FwdPrefetch {
-    static constexpr int kItems = kStep * (D / 8) / kThreads;  // 16-byte K chunks per thread
-    u32x4 k[kItems];
-    u32x4 v[4];  // 4 consecutive keys x 8 d of V
-};
-
-template <int D>
-__device__ __forceinline__ void fwd_load(FwdPrefetch<D>& pf, const bf16* __restrict__ K,
-                                         const bf16* __restrict__ V, int64_t tok_stride, int hoff,
-                                         int kbase, int tid) {
-#pragma unroll
-    for (int i = 0; i < FwdPrefetch<D>::kItems; ++i) {
-        const int it = tid + kThreads * i;
-        const int key = it / (D / 8), ch = it % (D / 8);
-        pf.k[i] = ld16(K + int64_t(kbase + key) * tok_stride + hoff + 8 * ch);
-    }
-    if (tid < 2 * D) {
-        const int kg = tid & 15, ch = tid >> 4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pf.v[r] = ld16(V + int64_t(kbase + 4 * kg + r) * tok_stride + hoff + 8 * ch);
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void fwd_store(const FwdPrefetch<D>& pf, FwdSmem<D>& sm, int buf, int tid) {
-#pragma unroll
-    for (int i = 0; i < FwdPrefetch<D>::kItems; ++i) {
-        const int it = tid + kThreads * i;
-        const int key = it / (D / 8), ch = it % (D / 8);
-        st16(&sm.k[buf][k_lds_row(key)][8 * ch], pf.k[i]);
-    }
-    if (tid < 2 * D) {
-        const int kg = tid & 15, ch = tid >> 4;
-        u32x2 cols[8];
-        transpose4x8(pf.v, cols);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) st8(&sm.vt[buf][8 * ch + j][4 * kg], cols[j]);
-    }
-}
+constexpr int kStep = kTileRows;  // keys per pipeline step
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
@@ -93,17 +42,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     bf16* __restrict__ O, float* __restrict__ LSE, const int32_t* __restrict__ se,
     const int32_t* __restrict__ q_order, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ row_ent, int L, int Hq, int Hkv, float scale_log2) {
+    using T = Tile<D>;
     constexpr int NS = D / 32;  // k-steps of QK^T
     constexpr int NT = D / 16;  // d-blocks of O^T
-    __shared__ FwdSmem<D> sm;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[4 * T::kBytes];
+    lds_char* const smem = (lds_char*)smem_raw;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, g = lane >> 4;
     const int rank = blockIdx.x / Hq, h = blockIdx.x % Hq;
     const int qb = q_order[rank];
     const int hkv = h / (Hq / Hkv);
     const int64_t q_stride = int64_t(Hq) * D, kv_stride = int64_t(Hkv) * D;
-    const int hoff = hkv * D;
     const int qrow0 = qb * kBlock + 32 * wave;  // first query of this wave
 
     // Q^T operand: lane holds query (qrow0 + 16 qs + n), d = 32 s + 8 g .. +7
@@ -123,11 +74,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
 
     const int beg = row_ptr[qb], nsteps = 2 * (row_ptr[qb + 1] - beg);
-    FwdPrefetch<D> pf;
-    if (nsteps > 0) {
-        fwd_load<D>(pf, K, V, kv_stride, hoff, (row_ent[beg] >> 1) * kBlock, tid);
-        fwd_store<D>(pf, sm, 0, tid);
-    }
+    const int kvs = int(kv_stride);
+    auto ktile = [&](int buf) { return smem + (2 * buf) * T::kBytes; };
+    auto vtile = [&](int buf) { return smem + (2 * buf + 1) * T::kBytes; };
+    auto issue = [&](int st, int buf) {
+        const int kbase = (row_ent[beg + (st >> 1)] >> 1) * kBlock + kStep * (st & 1);
+        const int64_t off = int64_t(kbase) * kv_stride + int64_t(hkv) * D;
+        T::load_async(ktile(buf), K + off, kvs, wave, lane);
+        T::load_async(vtile(buf), V + off, kvs, wave, lane);
+    };
+    if (nsteps > 0) issue(0, 0);
+    wait_vm_all();
     __syncthreads();
 
     for (int st = 0; st < nsteps; ++st) {
@@ -135,36 +92,31 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         const int ent = row_ent[beg + (st >> 1)];
         const int kbase = (ent >> 1) * kBlock + kStep * (st & 1);
         const bool partial = ent & 1;
-        if (st + 1 < nsteps) {
-            const int ent1 = row_ent[beg + ((st + 1) >> 1)];
-            fwd_load<D>(pf, K, V, kv_stride, hoff, (ent1 >> 1) * kBlock + kStep * ((st + 1) & 1), tid);
-        }
+        if (st + 1 < nsteps) issue(st + 1, buf ^ 1);
+        const lds_char* kt = ktile(buf);
+        const lds_char* vt = vtile(buf);
 
-        // S^T = K Q^T, 4 key blocks of 16 x 2 query groups of 16
+        // S^T = K Q^T (unscaled): block b = keys 16b..16b+15; lane holds
+        // query column n of group qs, keys 16b + 4g + 0..3
         f32x4 sc[2][4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             bf16x8 a[NS];
 #pragma unroll
-            for (int s = 0; s < NS; ++s)
-                a[s] = *reinterpret_cast<const bf16x8*>(&sm.k[buf][16 * b + n][32 * s + 8 * g]);
+            for (int s = 0; s < NS; ++s) a[s] = T::row_frag(kt, 16 * b + n, 4 * s + g);
 #pragma unroll
             for (int qs = 0; qs < 2; ++qs) {
                 f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < NS; ++s) c = mfma16x16x32(a[s], qf[qs][s], c);
-                sc[qs][b] = c * scale_log2;
+                sc[qs][b] = c;
             }
         }
 
         if (partial) {
-            // lane's keys: kbase + 32 c + 8 g + 0..7 for c = 0, 1
-            i32x4 sek[2][2];
+            i32x4 sek[4];
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                sek[c][0] = *reinterpret_cast<const i32x4*>(se + kbase + 32 * c + 8 * g);
-                sek[c][1] = *reinterpret_cast<const i32x4*>(se + kbase + 32 * c + 8 * g + 4);
-            }
+            for (int b = 0; b < 4; ++b) sek[b] = *reinterpret_cast<const i32x4*>(se + kbase + 16 * b + 4 * g);
 #pragma unroll
             for (int qs = 0; qs < 2; ++qs) {
                 const int qi = qrow0 + 16 * qs + n;
@@ -172,55 +124,61 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
                 for (int b = 0; b < 4; ++b)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int key = kbase + 32 * (b >> 1) + 8 * g + 4 * (b & 1) + r;
-                        const int sej = sek[b >> 1][b & 1][r];
-                        if (!(key <= qi && qi <= sej)) sc[qs][b][r] = -INFINITY;
+                        const int key = kbase + 16 * b + 4 * g + r;
+                        if (!(key <= qi && qi <= sek[b][r])) sc[qs][b][r] = -INFINITY;
                     }
             }
         }
 
-        // online softmax (base 2), one query column per lane
+        // online softmax in base 2, one query column per lane; the running
+        // max is kept in scaled units and the scale is folded into the FMA
+        // that forms the exp2 argument.
         bf16x8 pb[2][2];
 #pragma unroll
         for (int qs = 0; qs < 2; ++qs) {
             float mx = -INFINITY;
 #pragma unroll
             for (int b = 0; b < 4; ++b)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[qs][b][r]);
+                mx = fmaxf(fmaxf(mx, fmaxf(sc[qs][b][0], sc[qs][b][1])), fmaxf(sc[qs][b][2], sc[qs][b][3]));
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mnew = fmaxf(m_run[qs], mx);
+            const float mnew = fmaxf(m_run[qs], mx * scale_log2);
             const float muse = mnew == -INFINITY ? 0.f : mnew;
-            const float alpha = fast_exp2(m_run[qs] - muse);
             float rs = 0.f;
 #pragma unroll
             for (int b = 0; b < 4; ++b)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float p = fast_exp2(sc[qs][b][r] - muse);
+                    const float p = fast_exp2(__builtin_fmaf(sc[qs][b][r], scale_log2, -muse));
                     sc[qs][b][r] = p;
                     rs += p;
                 }
-            l_run[qs] = l_run[qs] * alpha + rs;
-            m_run[qs] = mnew;
+            // rescale only when some lane's running max moved (exact skip)
+            if (__any(mnew != m_run[qs])) {
+                const float alpha = fast_exp2(m_run[qs] - muse);
+                l_run[qs] *= alpha;
 #pragma unroll
-            for (int t = 0; t < NT; ++t) oacc[qs][t] *= alpha;
+                for (int t = 0; t < NT; ++t) oacc[qs][t] *= alpha;
+            }
+            l_run[qs] += rs;
+            m_run[qs] = mnew;
             pb[qs][0] = to_bf16x8(sc[qs][0], sc[qs][1]);
             pb[qs][1] = to_bf16x8(sc[qs][2], sc[qs][3]);
         }
 
-        // O^T += V^T P^T, 2 key steps of 32 x NT d blocks of 16
+        // O^T += V^T P^T: k-step c pairs key rows 32c + 4g + 0..3 and
+        // 32c + 16 + 4g + 0..3 (blocks 2c and 2c+1)
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.vt[buf][16 * t + n][32 * c + 8 * g]);
+                const bf16x8 a = join_tr(T::tr_frag(vt, 32 * c + 4 * g, 16 * t, n),
+                                         T::tr_frag(vt, 32 * c + 16 + 4 * g, 16 * t, n));
 #pragma unroll
                 for (int qs = 0; qs < 2; ++qs) oacc[qs][t] = mfma16x16x32(a, pb[qs][c], oacc[qs][t]);
             }
 
-        if (st + 1 < nsteps) fwd_store<D>(pf, sm, buf ^ 1, tid);
+        wait_vm_all();
         __syncthreads();
     }
 

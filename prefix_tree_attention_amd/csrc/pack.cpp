@@ -11,8 +11,13 @@
 // exactly when no sequence ends at it (which is when both carry the same
 // sequences), empty rows are an error, pads get node -1 / subtree end -1.
 //
-// Token tries are flat arrays; child lookup goes through one open-addressing
-// hash table per trie keyed by (parent node, token).
+// The tries are built directly in compressed (radix) form: a node's tokens
+// are a run of one source sequence, referenced by (sequence, start, length),
+// and matching walks whole runs with a vectorisable compare instead of one
+// lookup per token.  A node is split only where a later sequence branches
+// off or ends inside it, so node boundaries are exactly the branch points
+// and sequence ends -- the guide's compressed nodes.  Child lookup by first
+// token goes through one open-addressing hash table per trie.
 
 #include <algorithm>
 #include <cstdint>
@@ -27,11 +32,11 @@
 namespace {
 
 // ---------------------------------------------------------------------------
-// open-addressing map (parent node, token) -> child node
+// open-addressing map (parent node, first token) -> child node
 // ---------------------------------------------------------------------------
 class ChildMap {
   public:
-    ChildMap() { rehash(1024); }
+    ChildMap() { rehash(256); }
 
     int32_t find(int32_t parent, int32_t token) const {
         const uint64_t key = pack_key(parent, token);
@@ -41,9 +46,18 @@ class ChildMap {
         }
     }
 
-    void insert(int32_t parent, int32_t token, int32_t child) {
+    // insert or overwrite
+    void set(int32_t parent, int32_t token, int32_t child) {
+        const uint64_t key = pack_key(parent, token);
+        for (size_t i = slot(key);; i = (i + 1) & mask_) {
+            if (keys_[i] == key) {
+                vals_[i] = child;
+                return;
+            }
+            if (keys_[i] == kEmpty) break;
+        }
         if ((size_ + 1) * 2 > keys_.size()) rehash(keys_.size() * 2);
-        put(pack_key(parent, token), child);
+        put(key, child);
         ++size_;
     }
 
@@ -52,10 +66,7 @@ class ChildMap {
     static uint64_t pack_key(int32_t parent, int32_t token) {
         return (uint64_t(uint32_t(parent)) << 32) | uint32_t(token);
     }
-    size_t slot(uint64_t key) const {
-        uint64_t h = key * 0x9E3779B97F4A7C15ull;
-        return size_t(h >> 20) & mask_;
-    }
+    size_t slot(uint64_t key) const { return size_t((key * 0x9E3779B97F4A7C15ull) >> 20) & mask_; }
     void put(uint64_t key, int32_t v) {
         size_t i = slot(key);
         while (keys_[i] != kEmpty) i = (i + 1) & mask_;
@@ -78,60 +89,92 @@ class ChildMap {
     size_t mask_ = 0, size_ = 0;
 };
 
-// Uncompressed token trie.  Node 0 is the root (no token).
-struct TokenTrie {
-    std::vector<int32_t> token, first_child, last_child, next_sibling;
-    std::vector<int32_t> n_children, n_end;  // children count; sequences ending here
+// Extracted sequences, concatenated.
+struct Seqs {
+    std::vector<int32_t> tok;
+    std::vector<int64_t> off;  // [B + 1]
+    const int32_t* at(int32_t r) const { return tok.data() + off[size_t(r)]; }
+    int64_t len(int32_t r) const { return off[size_t(r) + 1] - off[size_t(r)]; }
+};
+
+// Number of leading equal elements of a[0..n) and b[0..n).
+int64_t common_prefix(const int32_t* a, const int32_t* b, int64_t n) {
+    int64_t i = 0;
+    while (i + 16 <= n && std::memcmp(a + i, b + i, 16 * sizeof(int32_t)) == 0) i += 16;
+    while (i < n && a[i] == b[i]) ++i;
+    return i;
+}
+
+// Compressed trie.  Node 0 is the root (no tokens).
+struct RadixTrie {
+    struct Node {
+        int32_t row, start, len;    // tokens: seqs.at(row)[start .. start + len)
+        int32_t parent;
+        int32_t n_end;              // sequences ending at this node's last token
+        std::vector<int32_t> kids;  // insertion order
+    };
+    std::vector<Node> nodes;
     ChildMap map;
-    std::vector<int32_t> seqs;  // batch rows, insertion order
+    std::vector<int32_t> seq_rows, seq_end;  // insertion order; node holding each sequence's last token
     int64_t tokens = 0;
 
-    TokenTrie() { add_node(-1, -1); }
+    RadixTrie() { nodes.push_back({-1, 0, 0, -1, 0, {}}); }
 
-    int32_t add_node(int32_t parent, int32_t tok) {
-        const int32_t id = int32_t(token.size());
-        token.push_back(tok);
-        first_child.push_back(-1);
-        last_child.push_back(-1);
-        next_sibling.push_back(-1);
-        n_children.push_back(0);
-        n_end.push_back(0);
-        if (parent >= 0) {
-            if (last_child[parent] < 0)
-                first_child[parent] = id;
-            else
-                next_sibling[last_child[parent]] = id;
-            last_child[parent] = id;
-            ++n_children[parent];
-            map.insert(parent, tok, id);
-        }
-        return id;
-    }
+    // Where a walk of s stops: at the end of `node` (mid == -1) or inside
+    // child `mid` after `midlen` of its tokens; `matched` tokens of s agree.
+    struct Walk {
+        int32_t node, mid, midlen;
+        int64_t matched;
+    };
 
-    // tokens an insertion would add = length minus the longest present prefix
-    int64_t added(const int32_t* s, int64_t n) const {
-        int32_t cur = 0;
+    Walk walk(const Seqs& S, const int32_t* s, int64_t n) const {
+        int32_t node = 0;
         int64_t i = 0;
-        for (; i < n; ++i) {
-            const int32_t c = map.find(cur, s[i]);
-            if (c < 0) break;
-            cur = c;
+        for (;;) {
+            if (i == n) return {node, -1, 0, i};
+            const int32_t c = map.find(node, s[i]);
+            if (c < 0) return {node, -1, 0, i};
+            const Node& x = nodes[size_t(c)];
+            const int64_t lim = std::min<int64_t>(x.len, n - i);
+            const int64_t m = 1 + common_prefix(s + i + 1, S.at(x.row) + x.start + 1, lim - 1);
+            if (m < x.len) return {node, c, int32_t(m), i + m};
+            i += x.len;
+            node = c;
         }
-        return n - i;
     }
 
-    void insert(const int32_t* s, int64_t n, int32_t row) {
-        int32_t cur = 0;
-        for (int64_t i = 0; i < n; ++i) {
-            int32_t c = map.find(cur, s[i]);
-            if (c < 0) {
-                c = add_node(cur, s[i]);
-                ++tokens;
-            }
-            cur = c;
+    void insert(const Seqs& S, int32_t row, const Walk& w) {
+        const int64_t n = S.len(row);
+        const int32_t* s = S.at(row);
+        int32_t at = w.node;
+        if (w.mid >= 0) {  // split child `mid` after `midlen` tokens; the old node keeps the suffix
+            const int32_t x = w.mid;
+            const int32_t y = int32_t(nodes.size());
+            Node pre{nodes[size_t(x)].row, nodes[size_t(x)].start, w.midlen, nodes[size_t(x)].parent, 0, {x}};
+            const int32_t par = pre.parent;
+            const int32_t first = S.at(pre.row)[pre.start];
+            nodes.push_back(std::move(pre));
+            Node& X = nodes[size_t(x)];
+            X.start += w.midlen;
+            X.len -= w.midlen;
+            X.parent = y;
+            for (auto& k : nodes[size_t(par)].kids)
+                if (k == x) k = y;
+            map.set(par, first, y);
+            map.set(y, S.at(X.row)[X.start], x);
+            at = y;
         }
-        ++n_end[cur];
-        seqs.push_back(row);
+        int32_t end = at;
+        if (w.matched < n) {  // new leaf with the rest of s
+            end = int32_t(nodes.size());
+            nodes.push_back({row, int32_t(w.matched), int32_t(n - w.matched), at, 0, {}});
+            nodes[size_t(at)].kids.push_back(end);
+            map.set(at, s[w.matched], end);
+            tokens += n - w.matched;
+        }
+        ++nodes[size_t(end)].n_end;
+        seq_rows.push_back(row);
+        seq_end.push_back(end);
     }
 };
 
@@ -143,83 +186,61 @@ struct PackedTrie {
     int64_t n_pairs = 0;
 };
 
-// Compress, lay out in pre-order and pad one token trie.
-void flatten(const TokenTrie& t, const std::vector<std::vector<int32_t>>& seqs, int64_t L,
-             int32_t pad_id, PackedTrie& out) {
+// Lay out one trie in pre-order (children in insertion order) and pad.
+void flatten(const RadixTrie& t, const Seqs& S, int64_t L, int32_t pad_id, PackedTrie& out) {
     const int64_t n = t.tokens;
     out.n = n;
     out.L = L;
     out.token_ids.assign(size_t(L), pad_id);
     out.node_id.assign(size_t(L), -1);
     out.subtree_end.assign(size_t(L), -1);
-    std::vector<int32_t> comp_of(t.token.size(), -1);  // token node -> compressed node
-    std::vector<int64_t> depth_end;                     // ancestors-or-self count at node end
-
-    // Iterative pre-order walk over compressed nodes.  A frame is a token
-    // node starting a compressed node; children are visited in insertion
-    // order by pushing them reversed.
+    const size_t nn = t.nodes.size();
+    std::vector<int32_t> pre_id(nn, -1);    // radix node -> pre-order index
+    std::vector<int64_t> depth_end(nn, 0);  // ancestors-or-self count at a node's last token
     struct Frame {
-        int32_t tok_node;
-        int32_t parent_comp;
+        int32_t node;
         bool exit;
-        int32_t comp;
     };
     std::vector<Frame> stack;
-    std::vector<int32_t> kids;
-    for (int32_t c = t.first_child[0]; c >= 0; c = t.next_sibling[c]) kids.push_back(c);
-    for (auto it = kids.rbegin(); it != kids.rend(); ++it) stack.push_back({*it, -1, false, -1});
+    const auto& rk = t.nodes[0].kids;
+    for (auto it = rk.rbegin(); it != rk.rend(); ++it) stack.push_back({*it, false});
     int64_t off = 0;
     while (!stack.empty()) {
-        Frame f = stack.back();
+        const Frame f = stack.back();
         stack.pop_back();
-        if (f.exit) {  // whole subtree laid out: its last index is off-1
-            const int32_t se = int32_t(off - 1);
-            for (int64_t i = out.node_start[f.comp]; i <= out.node_end[f.comp]; ++i)
-                out.subtree_end[size_t(i)] = se;
+        const auto& x = t.nodes[size_t(f.node)];
+        if (f.exit) {  // subtree laid out: its last index is off - 1
+            const int32_t id = pre_id[size_t(f.node)];
+            std::fill(out.subtree_end.begin() + out.node_start[size_t(id)],
+                      out.subtree_end.begin() + out.node_end[size_t(id)] + 1, int32_t(off - 1));
             continue;
         }
-        const int32_t comp = int32_t(out.node_start.size());
+        const int32_t me = int32_t(out.node_start.size());
+        pre_id[size_t(f.node)] = me;
+        const int32_t par = x.parent > 0 ? pre_id[size_t(x.parent)] : -1;
         out.node_start.push_back(int32_t(off));
-        out.node_parent.push_back(f.parent_comp);
-        int64_t d = f.parent_comp >= 0 ? depth_end[size_t(f.parent_comp)] : 0;
-        int32_t cur = f.tok_node;
-        for (;;) {
-            comp_of[size_t(cur)] = comp;
-            out.token_ids[size_t(off)] = t.token[size_t(cur)];
-            out.node_id[size_t(off)] = comp;
-            ++off;
-            ++d;
-            out.n_pairs += d;
-            // merge into the only child when no sequence ends here
-            if (t.n_children[size_t(cur)] == 1 && t.n_end[size_t(cur)] == 0)
-                cur = t.first_child[size_t(cur)];
-            else
-                break;
-        }
-        out.node_end.push_back(int32_t(off - 1));
-        depth_end.push_back(d);
-        stack.push_back({cur, f.parent_comp, true, comp});
-        kids.clear();
-        for (int32_t c = t.first_child[size_t(cur)]; c >= 0; c = t.next_sibling[size_t(c)])
-            kids.push_back(c);
-        for (auto it = kids.rbegin(); it != kids.rend(); ++it)
-            stack.push_back({*it, comp, false, -1});
+        out.node_end.push_back(int32_t(off + x.len - 1));
+        out.node_parent.push_back(par);
+        std::memcpy(out.token_ids.data() + off, S.at(x.row) + x.start, size_t(x.len) * sizeof(int32_t));
+        std::fill(out.node_id.begin() + off, out.node_id.begin() + off + x.len, me);
+        const int64_t d0 = x.parent > 0 ? depth_end[size_t(x.parent)] : 0;
+        depth_end[size_t(f.node)] = d0 + x.len;
+        out.n_pairs += int64_t(x.len) * d0 + int64_t(x.len) * (x.len + 1) / 2;
+        off += x.len;
+        stack.push_back({f.node, true});
+        for (auto it = x.kids.rbegin(); it != x.kids.rend(); ++it) stack.push_back({*it, false});
     }
 
-    // per-sequence node intervals, in insertion order, root first
-    out.seq_ids = t.seqs;
+    // per-sequence node intervals, insertion order, root first
+    out.seq_ids = t.seq_rows;
     out.seq_iv_ptr.assign(1, 0);
-    for (int32_t row : t.seqs) {
-        const auto& s = seqs[size_t(row)];
-        int32_t cur = 0, last = -1;
-        for (int32_t tok : s) {
-            cur = t.map.find(cur, tok);
-            const int32_t c = comp_of[size_t(cur)];
-            if (c != last) {
-                out.seq_iv.push_back(out.node_start[size_t(c)]);
-                out.seq_iv.push_back(out.node_end[size_t(c)]);
-                last = c;
-            }
+    std::vector<int32_t> path;
+    for (size_t k = 0; k < t.seq_rows.size(); ++k) {
+        path.clear();
+        for (int32_t v = t.seq_end[k]; v > 0; v = t.nodes[size_t(v)].parent) path.push_back(pre_id[size_t(v)]);
+        for (auto it = path.rbegin(); it != path.rend(); ++it) {
+            out.seq_iv.push_back(out.node_start[size_t(*it)]);
+            out.seq_iv.push_back(out.node_end[size_t(*it)]);
         }
         out.seq_iv_ptr.push_back(int32_t(out.seq_iv.size() / 2));
     }
@@ -254,38 +275,44 @@ int tree_pack(const int32_t* ids, const uint8_t* mask, int64_t B, int64_t S,
         return set_error(TREE_E_ARG, "tree_pack: bad batch shape or NULL input");
     try {
         const int64_t M = max_tokens_per_mb;
-        std::vector<std::vector<int32_t>> seqs(static_cast<size_t>(B));
-        int64_t original = 0;
+        Seqs seqs;
+        seqs.off.assign(size_t(B) + 1, 0);
+        seqs.tok.reserve(size_t(B * S));
         for (int64_t r = 0; r < B; ++r) {
-            auto& s = seqs[size_t(r)];
+            const int32_t* ir = ids + r * S;
+            const uint8_t* mr = mask + r * S;
             for (int64_t c = 0; c < S; ++c)
-                if (mask[r * S + c]) s.push_back(ids[r * S + c]);
-            if (s.empty()) return set_error(TREE_E_EMPTY_SEQ, "row %lld has no real token", (long long)r);
-            if (int64_t(s.size()) > M)
-                return set_error(TREE_E_SEQ_TOO_LONG, "row %lld has %zu tokens > max_tokens_per_mb=%lld",
-                                 (long long)r, s.size(), (long long)M);
-            original += int64_t(s.size());
+                if (mr[c]) seqs.tok.push_back(ir[c]);
+            seqs.off[size_t(r) + 1] = int64_t(seqs.tok.size());
+            const int64_t len = seqs.len(int32_t(r));
+            if (len == 0) return set_error(TREE_E_EMPTY_SEQ, "row %lld has no real token", (long long)r);
+            if (len > M)
+                return set_error(TREE_E_SEQ_TOO_LONG, "row %lld has %lld tokens > max_tokens_per_mb=%lld",
+                                 (long long)r, (long long)len, (long long)M);
         }
+        const int64_t original = int64_t(seqs.tok.size());
         std::vector<int32_t> order(static_cast<size_t>(B));
         std::iota(order.begin(), order.end(), 0);
-        std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
-            return seqs[size_t(a)].size() > seqs[size_t(b)].size();
-        });
-        std::vector<std::unique_ptr<TokenTrie>> tries;
+        std::stable_sort(order.begin(), order.end(),
+                         [&](int32_t a, int32_t b) { return seqs.len(a) > seqs.len(b); });
+        std::vector<std::unique_ptr<RadixTrie>> tries;
         for (int32_t r : order) {
-            const auto& s = seqs[size_t(r)];
-            const int64_t n = int64_t(s.size());
-            TokenTrie* dst = nullptr;
-            for (auto& t : tries)
-                if (t->tokens + t->added(s.data(), n) <= M) {
+            const int64_t n = seqs.len(r);
+            RadixTrie* dst = nullptr;
+            RadixTrie::Walk w{};
+            for (auto& t : tries) {
+                w = t->walk(seqs, seqs.at(r), n);
+                if (t->tokens + (n - w.matched) <= M) {
                     dst = t.get();
                     break;
                 }
-            if (!dst) {
-                tries.emplace_back(new TokenTrie());
-                dst = tries.back().get();
             }
-            dst->insert(s.data(), n, r);
+            if (!dst) {
+                tries.emplace_back(new RadixTrie());
+                dst = tries.back().get();
+                w = {0, -1, 0, 0};
+            }
+            dst->insert(seqs, r, w);
         }
         std::unique_ptr<struct tree_pack> p(new struct tree_pack());
         p->tries.resize(tries.size());
@@ -298,7 +325,7 @@ int tree_pack(const int32_t* ids, const uint8_t* mask, int64_t B, int64_t S,
             tree_tokens += n;
             pairs += p->tries[i].n_pairs;
         }
-        for (const auto& s : seqs) unpacked += int64_t(s.size()) * (int64_t(s.size()) + 1) / 2;
+        for (int64_t r = 0; r < B; ++r) unpacked += seqs.len(int32_t(r)) * (seqs.len(int32_t(r)) + 1) / 2;
         p->stats.n_tries = int64_t(p->tries.size());
         p->stats.original_tokens = original;
         p->stats.tree_tokens = tree_tokens;

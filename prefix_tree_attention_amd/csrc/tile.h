@@ -1,0 +1,92 @@
+// Internal: 64-row LDS tiles for the gfx950 attention kernels.
+//
+// A tile holds 64 consecutive tokens x D bf16 of one head, in natural row
+// order, as 16-byte chunks (D/8 per row).  It is filled straight from HBM by
+// global_load_lds_dwordx4 (each lane's 16 bytes land at the instruction's
+// LDS base + 16 * lane), so staging costs no registers and no LDS store
+// instructions.  Chunk c of row r sits at slot position c ^ swz(r) within
+// the row; the swizzle keeps both read patterns the kernels use free of
+// bank conflicts:
+//   - row-major operand reads (ds_read_b128): 16 lanes read one chunk
+//     column of 16 consecutive rows;
+//   - transposed operand reads (ds_read_b64_tr_b16): a 16-lane group reads
+//     4 consecutive rows x 16 consecutive elements, and lane i of the group
+//     receives element i of each of the 4 rows -- i.e. an MFMA operand
+//     fragment whose k index runs over rows.  Two groups (8 rows, two
+//     adjacent chunks) are served together.
+// For D = 128 (16 chunks per 256-byte row) swz(r) = 2 (r % 8) + (r / 8) % 2;
+// for D = 64 (8 chunks per 128-byte row) swz(r) = 2 ((r / 2) % 4) + (r / 8) % 2.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "mfma.h"
+
+namespace treeattn {
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTileRows = 64;
+
+template <int D>
+struct Tile {
+    static constexpr int kChunks = D / 8;              // 16-byte chunks per row
+    static constexpr int kBytes = kTileRows * D * 2;   // 16 KB (D=128) / 8 KB (D=64)
+    static constexpr int kLoadsPerWave = kBytes / 1024 / 4;  // 1 KB per wave instruction, 4 waves
+
+    __device__ static __forceinline__ int swz(int r) {
+        if constexpr (D == 128)
+            return 2 * (r & 7) + ((r >> 3) & 1);
+        else
+            return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+    }
+    // byte offset of (row, chunk) inside the tile
+    __device__ static __forceinline__ int slot(int r, int c) { return (r * kChunks + (c ^ swz(r))) * 16; }
+
+    // Issue this wave's share of the direct loads of one tile.  `g0` points
+    // at element 0 of row 0 (token of row 0, this head); `stride` is the
+    // token stride in elements.  Completion: s_waitcnt vmcnt(0) in each wave,
+    // then a workgroup barrier.
+    __device__ static __forceinline__ void load_async(lds_char* tile, const bf16* __restrict__ g0, int stride,
+                                                      int wave, int lane) {
+#pragma unroll
+        for (int j = 0; j < kLoadsPerWave; ++j) {
+            const int blk = wave * kLoadsPerWave + j;  // 1 KB block = 64 slots
+            const int p = blk * 64 + lane;             // slot this lane fills
+            const int r = p / kChunks, pos = p % kChunks;
+            const int c = pos ^ swz(r);
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(g0 + uint32_t(r * stride + 8 * c)),
+                                             reinterpret_cast<lds_void*>(tile + blk * 1024), 16, 0, 0);
+        }
+    }
+
+    // Row-major operand: 8 bf16 of row r starting at element 8c.
+    __device__ static __forceinline__ bf16x8 row_frag(const lds_char* tile, int r, int c) {
+        return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(tile + slot(r, c));
+    }
+
+    // Transposed operand: for a 16-lane group whose 4 rows start at r0, lane
+    // i (0..15) gets element e0 + i of rows r0..r0+3 (e0 a multiple of 16).
+    __device__ static __forceinline__ i16x4 tr_frag(const lds_char* tile, int r0, int e0, int i) {
+        const int r = r0 + (i >> 2);
+        const int e = e0 + 4 * (i & 3);
+        const int off = slot(r, e >> 3) + ((e >> 2) & 1) * 8;
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<__attribute__((address_space(3))) i16x4*>(const_cast<lds_char*>(tile) + off));
+    }
+};
+
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Eight bf16 from two transposed reads (k 0..3 then k 4..7).
+__device__ __forceinline__ bf16x8 join_tr(const i16x4& lo, const i16x4& hi) {
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+}  // namespace treeattn
