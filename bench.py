@@ -58,7 +58,25 @@ def parse(argv=None):
     ap.add_argument("--sweep", default=None, help="L,b of a sweep point (overrides --config)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=1, help="query heads in the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB elementwise copy kernel 3x (HBM counter calibration)")
     return ap.parse_args(argv)
+
+
+def copy_calibration():
+    """A plain elementwise copy of 1 GiB (read 1 GiB, write 1 GiB), three
+    launches: the reference reading of the FETCH_SIZE / WRITE_SIZE counters
+    for a kernel of known traffic."""
+    import torch
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n}), flush=True)
+    return 0
 
 
 def source_sha(name: str) -> str:
@@ -127,6 +145,8 @@ def main(argv=None):
                           "n_gpus": a.gpus}), flush=True)
         log("bench.py: multi-GPU runs are not part of this build (one trie per GPU; see the sharding design).")
         return 2
+    if a.copy_calibration:
+        return copy_calibration()
     import numpy as np
     import torch
     import workloads

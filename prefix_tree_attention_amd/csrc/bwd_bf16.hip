@@ -89,7 +89,10 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, g = lane >> 4;
-    const int rank = blockIdx.x / Hkv, hkv = blockIdx.x % Hkv;
+    // work item: key/value-head major, then key blocks heaviest first
+    const int nbk = int(gridDim.x) / Hkv;
+    const int work = xcd_logical_block();
+    const int hkv = work / nbk, rank = work % nbk;
     const int kb = k_order[rank];
     const int G = Hq / Hkv;
     const int64_t q_stride = int64_t(Hq) * D, kv_stride = int64_t(Hkv) * D;
@@ -257,9 +260,10 @@ __global__ __launch_bounds__(kThreads, 2) void dq_bf16_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, g = lane >> 4;
-    const int rank = blockIdx.x / Hq, h = blockIdx.x % Hq;
+    const int G = Hq / Hkv, per_kv = (int(gridDim.x) / Hq) * G;
+    const int work = xcd_logical_block();
+    const int hkv = work / per_kv, rank = (work % per_kv) / G, h = hkv * G + work % G;
     const int qb = q_order[rank];
-    const int hkv = h / (Hq / Hkv);
     const int64_t q_stride = int64_t(Hq) * D, kv_stride = int64_t(Hkv) * D;
     const int qrow0 = qb * kBlock + 32 * wave;
 

@@ -51,9 +51,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, g = lane >> 4;
-    const int rank = blockIdx.x / Hq, h = blockIdx.x % Hq;
+    // work item: key/value-head major, then query blocks heaviest first,
+    // then the query heads of the group
+    const int G = Hq / Hkv, per_kv = (int(gridDim.x) / Hq) * G;
+    const int work = xcd_logical_block();
+    const int hkv = work / per_kv, rank = (work % per_kv) / G, h = hkv * G + work % G;
     const int qb = q_order[rank];
-    const int hkv = h / (Hq / Hkv);
     const int64_t q_stride = int64_t(Hq) * D, kv_stride = int64_t(Hkv) * D;
     const int qrow0 = qb * kBlock + 32 * wave;  // first query of this wave
 

@@ -82,6 +82,19 @@ struct Tile {
 
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// XCD-aware work order.  Workgroups are dispatched round-robin over the 8
+// XCDs (block b runs on XCD b % 8), and each XCD has its own L2.  The
+// logical work index returned here gives XCD x the contiguous range
+// [x W/8, (x+1) W/8) of a key/value-head-major order, so the workgroups
+// sharing K/V tiles (or Q/dO tiles) of one key/value head meet in one L2,
+// while each XCD still takes its range heaviest-first.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_logical_block() {
+    const int W = int(gridDim.x), b = int(blockIdx.x);
+    if (W % kXcds != 0) return b;
+    return (b % kXcds) * (W / kXcds) + b / kXcds;
+}
+
 // Eight bf16 from two transposed reads (k 0..3 then k 4..7).
 __device__ __forceinline__ bf16x8 join_tr(const i16x4& lo, const i16x4& hi) {
     typedef short i16x8 __attribute__((ext_vector_type(8)));
