@@ -117,15 +117,18 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
 #pragma unroll
         for (int t = 0; t < NT; ++t) dk[ks][t] = dv[ks][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // the column is walked from its last query block down, so the key blocks
+    // in flight on an XCD read the same Q / dO tiles at about the same time
     const int beg = col_ptr[kb], nsteps = (col_ptr[kb + 1] - beg) * 2 * G;
+    const int last = col_ptr[kb + 1] - 1;
     const int qs32 = int(q_stride);
     auto qtile = [&](int buf) { return smem + buf * kStage; };
     auto gtile = [&](int buf) { return smem + buf * kStage + T::kBytes; };
     auto lsev = [&](int buf) { return smem + buf * kStage + 2 * T::kBytes; };
     auto dlv = [&](int buf) { return smem + buf * kStage + 2 * T::kBytes + 256; };
-    // step st: tile col_ent[beg + st / 2G], query half (st / G) % 2, head hkv G + st % G
+    // step st: tile col_ent[last - st / 2G], query half (st / G) % 2, head hkv G + st % G
     auto issue = [&](int st, int buf) {
-        const int ent = col_ent[beg + st / (2 * G)];
+        const int ent = col_ent[last - st / (2 * G)];
         const int qbase = (ent >> 1) * kBlock + kStep * ((st / G) & 1);
         const int h = hkv * G + st % G;
         const int64_t off = int64_t(qbase) * q_stride + int64_t(h) * D;
@@ -140,7 +143,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
 
     for (int st = 0; st < nsteps; ++st) {
         const int buf = st & 1;
-        const int ent = col_ent[beg + st / (2 * G)];
+        const int ent = col_ent[last - st / (2 * G)];
         const int qbase = (ent >> 1) * kBlock + kStep * ((st / G) & 1);
         const bool partial = ent & 1;
         if (st + 1 < nsteps) issue(st + 1, buf ^ 1);

@@ -40,7 +40,16 @@ __global__ __launch_bounds__(128) void meta_blocks(const int32_t* __restrict__ s
     const int j = b * kBlock + threadIdx.x;
     int s = se[j];
     if (s < -1 || s >= L) s = -1;  // malformed input: treat as a pad, never index out of range
-    if (s >= 0) atomicAdd(&hist[s], 1);
+    // one atomic per run of equal subtree ends (a node's tokens share one),
+    // so a long shared prefix does not serialise on a single counter
+    __shared__ int ss[kBlock];
+    ss[threadIdx.x] = s;
+    __syncthreads();
+    if (s >= 0 && (threadIdx.x == 0 || ss[threadIdx.x - 1] != s)) {
+        int run = 1;
+        while (threadIdx.x + run < kBlock && ss[threadIdx.x + run] == s) ++run;
+        atomicAdd(&hist[s], run);
+    }
     int mn = s, mx = s;
     for (int off = 32; off > 0; off >>= 1) {
         mn = min(mn, __shfl_xor(mn, off));
@@ -181,29 +190,44 @@ __global__ __launch_bounds__(1024) void meta_finish(const int32_t* __restrict__ 
     }
     __syncthreads();
 
-    // 3) entries, ascending
-    for (int qb = t; qb < nb; qb += nt) {
+    // 3) entries, ascending: one wave per row (column), 64 tiles per ballot,
+    //    each nonempty tile written at its rank among the nonempty ones
+    const int lane = t & 63, wv = t >> 6, nw = nt >> 6;
+    const unsigned long long below = (1ull << lane) - 1;
+    for (int qb = wv; qb < nb; qb += nw) {
         int k = row_ptr[qb];
         const uint8_t* row = tc + int64_t(qb) * nb;
-        for (int kb = 0; kb <= qb; ++kb) {
-            const int c = row[kb];
-            if (c) row_ent[k++] = (kb << 1) | (c == 1);
+        for (int k0 = 0; k0 <= qb; k0 += 64) {
+            const int kb = k0 + lane;
+            const int c = kb <= qb ? row[kb] : 0;
+            const unsigned long long m = __ballot(c != 0);
+            if (c) row_ent[k + __popcll(m & below)] = (kb << 1) | (c == 1);
+            k += __popcll(m);
         }
     }
-    for (int kb = t; kb < nb; kb += nt) {
+    for (int kb = wv; kb < nb; kb += nw) {
         int k = col_ptr[kb];
-        for (int qb = kb; qb < nb; ++qb) {
-            const int c = tc[int64_t(qb) * nb + kb];
-            if (c) col_ent[k++] = (qb << 1) | (c == 1);
+        for (int q0 = kb; q0 < nb; q0 += 64) {
+            const int qb = q0 + lane;
+            const int c = qb < nb ? tc[int64_t(qb) * nb + kb] : 0;
+            const unsigned long long m = __ballot(c != 0);
+            if (c) col_ent[k + __popcll(m & below)] = (qb << 1) | (c == 1);
+            k += __popcll(m);
         }
     }
 
-    // 4) heaviest-first orders (stable on index)
+    // 4) heaviest-first orders (stable on index), counts staged in LDS
+    __shared__ int rc_s[kMaxL / kBlock], cc_s[kMaxL / kBlock];
+    for (int i = t; i < nb; i += nt) {
+        rc_s[i] = row_cnt[i];
+        cc_s[i] = col_cnt[i];
+    }
+    __syncthreads();
     for (int x = t; x < nb; x += nt) {
-        const int rc = row_cnt[x], cc = col_cnt[x];
+        const int rc = rc_s[x], cc = cc_s[x];
         int rq = 0, rk = 0;
         for (int y = 0; y < nb; ++y) {
-            const int ry = row_cnt[y], cy = col_cnt[y];
+            const int ry = rc_s[y], cy = cc_s[y];
             rq += (ry > rc) || (ry == rc && y < x);
             rk += (cy > cc) || (cy == cc && y < x);
         }
