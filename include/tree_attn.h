@@ -156,7 +156,8 @@ int tree_meta(const int32_t* d_se, int64_t L, int32_t* d_pos, uint8_t* d_tile_cl
               void* d_ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
- * Attention (device).  Forward: for query head h and token i,
+ * Attention (device).  scale must be finite and > 0.  Forward: for query
+ * head h and token i,
  *   O_i = softmax_j(scale * q_i . k_j) v_j over j in A(i) = {j : j <= i <= se[j]},
  *   LSE_i = ln sum_{j in A(i)} exp(scale * q_i . k_j);
  * rows with no visible key (pads) get O = 0 and LSE = -inf.  Tiles the

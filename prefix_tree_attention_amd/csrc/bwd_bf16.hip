@@ -64,6 +64,13 @@ __global__ __launch_bounds__(256) void delta_bf16_kernel(const bf16* __restrict_
     delta[int64_t(r % Hq) * L + r / Hq] = acc;
 }
 
+// Place a value in accumulation registers (empty asm with an AGPR operand).
+__device__ __forceinline__ void pin_agpr(bf16x8& x) {
+    i32x4 v = __builtin_bit_cast(i32x4, x);
+    asm volatile("" : "+a"(v));
+    x = __builtin_bit_cast(bf16x8, v);
+}
+
 // direct load of 64 consecutive floats (one wave)
 __device__ __forceinline__ void load_row64_async(lds_char* dst, const float* __restrict__ src, int lane) {
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + lane), reinterpret_cast<lds_void*>(dst), 4, 0,
@@ -111,6 +118,16 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
             vf[ks][s] = __builtin_bit_cast(bf16x8, ld16(V + int64_t(key) * kv_stride + hkv * D + 32 * s + 8 * g));
         }
     }
+    // The resident K/V operands live in the accumulation-register file: MFMA
+    // reads its A/B operands from either file, and the vector registers are
+    // needed for the dK/dV accumulators and the per-step scores.
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            pin_agpr(kf[ks][s]);
+            pin_agpr(vf[ks][s]);
+        }
     f32x4 dk[2][NT], dv[2][NT];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
