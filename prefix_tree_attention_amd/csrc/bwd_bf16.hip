@@ -44,13 +44,17 @@ constexpr int kStep = kTileRows;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
-// Delta = rowsum(dO * O)
+// Delta = rowsum(dO * O), and LSE in base 2 (LSE log2 e) for the dK/dV
+// kernel's exponent
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void delta_bf16_kernel(const bf16* __restrict__ O, const bf16* __restrict__ dO,
-                                                         float* __restrict__ delta, int L, int Hq) {
+                                                         const float* __restrict__ LSE, float* __restrict__ delta,
+                                                         float* __restrict__ lse2, int L, int Hq) {
     const int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x;
     if (r >= int64_t(L) * Hq) return;
+    const int64_t hr = int64_t(r % Hq) * L + r / Hq;
+    lse2[hr] = LSE[hr] * kLog2e;
     float acc = 0.f;
 #pragma unroll
     for (int c = 0; c < D / 8; ++c) {
@@ -61,7 +65,7 @@ __global__ __launch_bounds__(256) void delta_bf16_kernel(const bf16* __restrict_
             acc += bf16_to_float(a[w] >> 16) * bf16_to_float(b[w] >> 16);
         }
     }
-    delta[int64_t(r % Hq) * L + r / Hq] = acc;
+    delta[hr] = acc;
 }
 
 // Place a value in accumulation registers (empty asm with an AGPR operand).
@@ -83,13 +87,13 @@ __device__ __forceinline__ void load_row64_async(lds_char* dst, const float* __r
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
+    const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Delta,
     bf16* __restrict__ dK, bf16* __restrict__ dV, const int32_t* __restrict__ se,
     const int32_t* __restrict__ k_order, const int32_t* __restrict__ col_ptr,
     const int32_t* __restrict__ col_ent, int L, int Hq, int Hkv, float scale_log2, float scale) {
     using T = Tile<D>;
     constexpr int NS = D / 32, NT = D / 16;
-    constexpr int kStage = 2 * T::kBytes + 512;  // Q tile, dO tile, LSE[64], Delta[64]
+    constexpr int kStage = 2 * T::kBytes + 512;  // Q tile, dO tile, LSE log2 e [64], Delta[64]
     __shared__ __attribute__((aligned(1024))) char smem_raw[2 * kStage];
     lds_char* const smem = (lds_char*)smem_raw;
 
@@ -143,27 +147,50 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
     auto gtile = [&](int buf) { return smem + buf * kStage + T::kBytes; };
     auto lsev = [&](int buf) { return smem + buf * kStage + 2 * T::kBytes; };
     auto dlv = [&](int buf) { return smem + buf * kStage + 2 * T::kBytes + 256; };
-    // step st: tile col_ent[last - st / 2G], query half (st / G) % 2, head hkv G + st % G
-    auto issue = [&](int st, int buf) {
-        const int ent = col_ent[last - st / (2 * G)];
-        const int qbase = (ent >> 1) * kBlock + kStep * ((st / G) & 1);
-        const int h = hkv * G + st % G;
+    // Steps run over the query heads of the group fastest, then the two
+    // 64-query halves of a tile, then the tiles col_ent[last], col_ent[last-1],
+    // ...; the position is kept as counters (tile, half, head) so the loop
+    // carries no integer division.
+    struct StepPos {
+        int tile, half, head;
+    };
+    auto advance = [&](StepPos& p) {
+        if (++p.head == G) {
+            p.head = 0;
+            if (++p.half == 2) {
+                p.half = 0;
+                ++p.tile;
+            }
+        }
+    };
+    auto issue = [&](const StepPos& p, int buf) {
+        const int ent = col_ent[last - p.tile];
+        const int qbase = (ent >> 1) * kBlock + kStep * p.half;
+        const int h = hkv * G + p.head;
         const int64_t off = int64_t(qbase) * q_stride + int64_t(h) * D;
         T::load_async(qtile(buf), Q + off, qs32, wave, lane);
         T::load_async(gtile(buf), dO + off, qs32, wave, lane);
-        if (wave == 0) load_row64_async(lsev(buf), LSE + int64_t(h) * L + qbase, lane);
+        if (wave == 0) load_row64_async(lsev(buf), LSE2 + int64_t(h) * L + qbase, lane);
         if (wave == 1) load_row64_async(dlv(buf), Delta + int64_t(h) * L + qbase, lane);
     };
-    if (nsteps > 0) issue(0, 0);
+    StepPos cur{0, 0, 0}, nxt{0, 0, 0};
+    if (nsteps > 0) {
+        issue(nxt, 0);
+        advance(nxt);
+    }
     wait_vm_all();
     __syncthreads();
 
     for (int st = 0; st < nsteps; ++st) {
         const int buf = st & 1;
-        const int ent = col_ent[last - st / (2 * G)];
-        const int qbase = (ent >> 1) * kBlock + kStep * ((st / G) & 1);
+        const int ent = col_ent[last - cur.tile];
+        const int qbase = (ent >> 1) * kBlock + kStep * cur.half;
         const bool partial = ent & 1;
-        if (st + 1 < nsteps) issue(st + 1, buf ^ 1);
+        advance(cur);
+        if (st + 1 < nsteps) {
+            issue(nxt, buf ^ 1);
+            advance(nxt);
+        }
         const lds_char* qt = qtile(buf);
         const lds_char* gt = gtile(buf);
         const lds_char* lsp = lsev(buf);
@@ -173,6 +200,12 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
         // gradient products
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
+            // dP accumulates onto -Delta, so it leaves the products as dP - Delta
+            f32x4 ndl[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                ndl[e] = -*reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+                    dlp + 4 * (32 * c + 16 * e + 4 * g));
             f32x4 s[2][2], dp[2][2];  // [ks][e]: lane = key column, queries 32c + 16e + 4g + 0..3
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
@@ -185,7 +218,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
                 }
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    f32x4 cs = {0.f, 0.f, 0.f, 0.f}, cd = {0.f, 0.f, 0.f, 0.f};
+                    f32x4 cs = {0.f, 0.f, 0.f, 0.f}, cd = ndl[e];
 #pragma unroll
                     for (int x = 0; x < NS; ++x) {
                         cs = mfma16x16x32(aq[x], kf[ks][x], cs);
@@ -195,14 +228,11 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
                     dp[ks][e] = cd;
                 }
             }
-            f32x4 l2[2], dl[2];
+            f32x4 l2[2];
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
+            for (int e = 0; e < 2; ++e)
                 l2[e] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-                            lsp + 4 * (32 * c + 16 * e + 4 * g)) * kLog2e;
-                dl[e] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-                    dlp + 4 * (32 * c + 16 * e + 4 * g));
-            }
+                    lsp + 4 * (32 * c + 16 * e + 4 * g));
             bf16x8 pb[2], db[2];
             // P = exp2(scale log2e S - LSE log2e), dS = P (dP - Delta); the
             // subtree-interval predicate only in partial tiles (separate code
@@ -221,7 +251,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
                                 p = (key <= qi && qi <= sek[ks]) ? p : 0.f;
                             }
                             s[ks][e][r] = p;
-                            dp[ks][e][r] = p * (dp[ks][e][r] - dl[e][r]);
+                            dp[ks][e][r] = p * dp[ks][e][r];
                         }
                     pb[ks] = to_bf16x8(s[ks][0], s[ks][1]);
                     db[ks] = to_bf16x8(dp[ks][0], dp[ks][1]);
@@ -414,11 +444,12 @@ hipError_t launch_bwd_d(int phase, const bf16* Q, const bf16* K, const bf16* V, 
     const int L = int(sh.L);
     const int64_t rows = int64_t(L) * sh.Hq;
     const float sl2 = sh.scale * kLog2e;
+    float* lse2 = delta + rows;  // second half of the workspace
     if (phase == kPhaseAll || phase == kPhaseDelta)
-        delta_bf16_kernel<D><<<unsigned((rows + 255) / 256), 256, 0, stream>>>(O, dO, delta, L, sh.Hq);
+        delta_bf16_kernel<D><<<unsigned((rows + 255) / 256), 256, 0, stream>>>(O, dO, lse, delta, lse2, L, sh.Hq);
     if (phase == kPhaseAll || phase == kPhaseDkdv)
         dkdv_bf16_kernel<D><<<unsigned(sh.nb) * unsigned(sh.Hkv), kThreads, 0, stream>>>(
-            Q, K, V, dO, lse, delta, dK, dV, se, mp.k_order, mp.col_ptr, mp.col_ent, L, sh.Hq, sh.Hkv, sl2,
+            Q, K, V, dO, lse2, delta, dK, dV, se, mp.k_order, mp.col_ptr, mp.col_ent, L, sh.Hq, sh.Hkv, sl2,
             sh.scale);
     if (phase == kPhaseAll || phase == kPhaseDq)
         dq_bf16_kernel<D><<<unsigned(sh.nb) * unsigned(sh.Hq), kThreads, 0, stream>>>(

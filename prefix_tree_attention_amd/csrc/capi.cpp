@@ -118,7 +118,7 @@ size_t tree_attn_bwd_workspace_bytes(int64_t L, int32_t Hq, int32_t D, int32_t d
     (void)D;
     (void)dtype;
     if (L <= 0 || Hq <= 0) return 0;
-    return round256(size_t(L) * size_t(Hq) * sizeof(float));  // delta [Hq, L]
+    return round256(2 * size_t(L) * size_t(Hq) * sizeof(float));  // Delta [Hq, L], LSE log2 e [Hq, L]
 }
 
 int tree_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
