@@ -374,7 +374,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_bf16_kernel(
                 }
 #pragma unroll
                 for (int qs = 0; qs < 2; ++qs) {
-                    f32x4 cs = {0.f, 0.f, 0.f, 0.f}, cd = {0.f, 0.f, 0.f, 0.f};
+                    // dP^T accumulates onto -Delta of the lane's query
+                    f32x4 cs = {0.f, 0.f, 0.f, 0.f}, cd = {-dlt[qs], -dlt[qs], -dlt[qs], -dlt[qs]};
 #pragma unroll
                     for (int x = 0; x < NS; ++x) {
                         cs = mfma16x16x32(ak[x], qf[qs][x], cs);
@@ -404,7 +405,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_bf16_kernel(
                                 const int key = kbase + 32 * c + 16 * e + 4 * g + r;
                                 p = (key <= qi && qi <= sek[e][r]) ? p : 0.f;
                             }
-                            dp[qs][e][r] = p * (dp[qs][e][r] - dlt[qs]);
+                            dp[qs][e][r] = p * dp[qs][e][r];
                         }
                     db[qs] = to_bf16x8(dp[qs][0], dp[qs][1]);
                 }

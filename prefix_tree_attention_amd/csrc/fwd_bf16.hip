@@ -35,6 +35,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kStep = kTileRows;  // keys per pipeline step
+constexpr float kRescaleSlack = 8.f;  // log2 units: p <= 256 between rescales
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
@@ -139,14 +140,32 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         bf16x8 pb[2][2];
 #pragma unroll
         for (int qs = 0; qs < 2; ++qs) {
+            // maximum (not maxnum) chains lower to v_maximum3_f32 with no
+            // NaN-quieting of the accumulator inputs
             float mx = -INFINITY;
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
-                mx = fmaxf(fmaxf(mx, fmaxf(sc[qs][b][0], sc[qs][b][1])), fmaxf(sc[qs][b][2], sc[qs][b][3]));
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mnew = fmaxf(m_run[qs], mx * scale_log2);
-            const float muse = mnew == -INFINITY ? 0.f : mnew;
+            for (int b = 0; b < 4; ++b) {
+                mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, sc[qs][b][0]), sc[qs][b][1]);
+                mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, sc[qs][b][2]), sc[qs][b][3]);
+            }
+            mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 16));
+            mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32));
+            // The reference max only moves when some lane's tile max exceeds
+            // it by more than kRescaleSlack (log2 units).  O and l are both
+            // relative to the same reference, so a stale one changes nothing
+            // but the magnitude of p, which stays <= 2^kRescaleSlack; the
+            // O rescale thus runs a few times per row instead of nearly
+            // every step.
+            const float mt = mx * scale_log2;
+            if (__any(mt > m_run[qs] + kRescaleSlack)) {
+                const float mnew = fmaxf(m_run[qs], mt);
+                const float alpha = fast_exp2(m_run[qs] - (mnew == -INFINITY ? 0.f : mnew));
+                l_run[qs] *= alpha;
+#pragma unroll
+                for (int t = 0; t < NT; ++t) oacc[qs][t] *= alpha;
+                m_run[qs] = mnew;
+            }
+            const float muse = m_run[qs] == -INFINITY ? 0.f : m_run[qs];
             float rs = 0.f;
 #pragma unroll
             for (int b = 0; b < 4; ++b)
@@ -156,15 +175,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
                     sc[qs][b][r] = p;
                     rs += p;
                 }
-            // rescale only when some lane's running max moved (exact skip)
-            if (__any(mnew != m_run[qs])) {
-                const float alpha = fast_exp2(m_run[qs] - muse);
-                l_run[qs] *= alpha;
-#pragma unroll
-                for (int t = 0; t < NT; ++t) oacc[qs][t] *= alpha;
-            }
             l_run[qs] += rs;
-            m_run[qs] = mnew;
             pb[qs][0] = to_bf16x8(sc[qs][0], sc[qs][1]);
             pb[qs][1] = to_bf16x8(sc[qs][2], sc[qs][3]);
         }
