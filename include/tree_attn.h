@@ -188,7 +188,8 @@ int tree_attn_bwd(const void* q, const void* k, const void* v, const void* o,
 
 /* One phase of tree_attn_bwd, for callers that time or schedule the
  * backward's kernels separately: TREE_BWD_DELTA computes Delta_i =
- * dO_i . O_i and LSE_i log2 e into d_ws; TREE_BWD_DKDV writes dk and dv;
+ * dO_i . O_i (and, for bf16, LSE_i log2 e) into d_ws, in an internal
+ * layout; TREE_BWD_DKDV writes dk and dv;
  * TREE_BWD_DQ writes dq; TREE_BWD_ALL runs all three in that order (same
  * as tree_attn_bwd).  DKDV and DQ read what a DELTA phase left in the same
  * d_ws, so a DELTA phase must precede them on the stream.  Other arguments and

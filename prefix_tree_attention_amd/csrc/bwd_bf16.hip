@@ -44,7 +44,8 @@ constexpr int kStep = kTileRows;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
-// Delta = rowsum(dO * O), and LSE in base 2 (LSE log2 e) for the dK/dV
+// -Delta = -rowsum(dO * O) (stored negated: it is the initial value of
+// the dP accumulators), and LSE in base 2 (LSE log2 e) for the dK/dV
 // kernel's exponent
 // ---------------------------------------------------------------------------
 template <int D>
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(256) void delta_bf16_kernel(const bf16* __restrict_
             acc += bf16_to_float(a[w] >> 16) * bf16_to_float(b[w] >> 16);
         }
     }
-    delta[hr] = acc;
+    delta[hr] = -acc;
 }
 
 // Place a value in accumulation registers (empty asm with an AGPR operand).
@@ -92,14 +93,19 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
     const int32_t* __restrict__ k_order, const int32_t* __restrict__ col_ptr,
     const int32_t* __restrict__ col_ent, int L, int Hq, int Hkv, float scale_log2, float scale) {
     using T = Tile<D>;
-    constexpr int NS = D / 32, NT = D / 16;
+    constexpr int NX = D / 16;  // k-steps of S = Q K^T and dP = dO V^T
+    constexpr int NT = D / 32;  // 32-row d-blocks of dK^T and dV^T
     constexpr int kStage = 2 * T::kBytes + 512;  // Q tile, dO tile, LSE log2 e [64], Delta[64]
     __shared__ __attribute__((aligned(1024))) char smem_raw[2 * kStage];
     lds_char* const smem = (lds_char*)smem_raw;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n = lane & 15, g = lane >> 4;
+    // 32x32x16 fragments: lane = MFMA column j32 (this lane's key) and k-half h
+    const int j32 = lane & 31, h = lane >> 5;
+    // transposing reads: 16-lane group gi takes 16 d values starting at
+    // 16 (gi % 2) and query rows 4 h + 0..3 of a k-step
+    const int tr_e = 16 * ((lane >> 4) & 1), tr_i = lane & 15;
     // work item: key/value-head major, then key blocks heaviest first
     const int nbk = int(gridDim.x) / Hkv;
     const int work = xcd_logical_block();
@@ -108,35 +114,38 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
     const int G = Hq / Hkv;
     const int64_t q_stride = int64_t(Hq) * D, kv_stride = int64_t(Hkv) * D;
     const int kw0 = kb * kBlock + 32 * wave;
+    const int key = kw0 + j32;
+    const int sek = se[key];
 
-    // K^T, V^T operands of this wave's 32 keys: lane holds key (kw0 + 16 ks + n)
-    bf16x8 kf[2][NS], vf[2][NS];
-    int sek[2];
+    // K^T, V^T operands (B of S and dP): lane holds key kw0 + j32,
+    // d = 16 x + 8 h .. +7 for k-step x.  They live in the accumulation-
+    // register file: MFMA reads A/B operands from either file, and the
+    // vector registers are needed for the accumulators and the scores.
+    bf16x8 kf[NX], vf[NX];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        const int key = kw0 + 16 * ks + n;
-        sek[ks] = se[key];
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            kf[ks][s] = __builtin_bit_cast(bf16x8, ld16(K + int64_t(key) * kv_stride + hkv * D + 32 * s + 8 * g));
-            vf[ks][s] = __builtin_bit_cast(bf16x8, ld16(V + int64_t(key) * kv_stride + hkv * D + 32 * s + 8 * g));
-        }
+    for (int x = 0; x < NX; ++x) {
+        kf[x] = __builtin_bit_cast(bf16x8, ld16(K + int64_t(key) * kv_stride + hkv * D + 16 * x + 8 * h));
+        vf[x] = __builtin_bit_cast(bf16x8, ld16(V + int64_t(key) * kv_stride + hkv * D + 16 * x + 8 * h));
+        pin_agpr(kf[x]);
+        pin_agpr(vf[x]);
     }
-    // The resident K/V operands live in the accumulation-register file: MFMA
-    // reads its A/B operands from either file, and the vector registers are
-    // needed for the dK/dV accumulators and the per-step scores.
+    // Loop-invariant LDS byte offsets of this lane's operand reads (the
+    // swizzle XOR is per lane and per k-step, so it is resolved once here;
+    // the step only adds its buffer, tile and query-half bases).
+    int roff[NX];  // row-major read of k-step x: row j32, chunk 2 x + h
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int x = 0; x < NX; ++x) roff[x] = T::slot(j32, 2 * x + h);
+    int toff[NT][2];  // transposing read of d-block t, rows 4 h + 8 v + 0..3
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            pin_agpr(kf[ks][s]);
-            pin_agpr(vf[ks][s]);
-        }
-    f32x4 dk[2][NT], dv[2][NT];
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+        for (int v = 0; v < 2; ++v) toff[t][v] = T::tr_offset(4 * h + 8 * v, 32 * t + tr_e, tr_i);
+    // dK^T, dV^T accumulators: block t, register r = d 32 t + 8 (r / 4) + 4 h + r % 4
+    f32x16 dk[NT], dv[NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) dk[ks][t] = dv[ks][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dk[t][r] = dv[t][r] = 0.f;
 
     // the column is walked from its last query block down, so the key blocks
     // in flight on an XCD read the same Q / dO tiles at about the same time
@@ -195,101 +204,105 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
         const lds_char* gt = gtile(buf);
         const lds_char* lsp = lsev(buf);
         const lds_char* dlp = dlv(buf);
+        auto lds_f32x4 = [](const lds_char* p) {
+            return *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(p);
+        };
 
-        // two halves of 32 queries: blocks b = 2c, 2c+1 feed k-step c of the
-        // gradient products
+        // Two halves of 32 queries.  In half c, register r of a score
+        // accumulator holds query 32 c + 8 (r / 4) + 4 h + r % 4 against
+        // this lane's key.
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            // dP accumulates onto -Delta, so it leaves the products as dP - Delta
-            f32x4 ndl[2];
+            // S = Q K^T; dP accumulates onto -Delta so it leaves dP - Delta
+            f32x16 sc, dp;
 #pragma unroll
-            for (int e = 0; e < 2; ++e)
-                ndl[e] = -*reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-                    dlp + 4 * (32 * c + 16 * e + 4 * g));
-            f32x4 s[2][2], dp[2][2];  // [ks][e]: lane = key column, queries 32c + 16e + 4g + 0..3
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 ndl = lds_f32x4(dlp + 4 * (32 * c + 8 * j + 4 * h));
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int b = 2 * c + e;
-                bf16x8 aq[NS], ag[NS];
-#pragma unroll
-                for (int x = 0; x < NS; ++x) {
-                    aq[x] = T::row_frag(qt, 16 * b + n, 4 * x + g);
-                    ag[x] = T::row_frag(gt, 16 * b + n, 4 * x + g);
-                }
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    f32x4 cs = {0.f, 0.f, 0.f, 0.f}, cd = ndl[e];
-#pragma unroll
-                    for (int x = 0; x < NS; ++x) {
-                        cs = mfma16x16x32(aq[x], kf[ks][x], cs);
-                        cd = mfma16x16x32(ag[x], vf[ks][x], cd);
-                    }
-                    s[ks][e] = cs;
-                    dp[ks][e] = cd;
+                for (int i = 0; i < 4; ++i) {
+                    sc[4 * j + i] = 0.f;
+                    dp[4 * j + i] = ndl[i];
                 }
             }
-            f32x4 l2[2];
 #pragma unroll
-            for (int e = 0; e < 2; ++e)
-                l2[e] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-                    lsp + 4 * (32 * c + 16 * e + 4 * g));
-            bf16x8 pb[2], db[2];
+            for (int x = 0; x < NX; ++x) {
+                const bf16x8 aq = T::frag_at(qt + 32 * c * T::kRowBytes, roff[x]);
+                const bf16x8 ag = T::frag_at(gt + 32 * c * T::kRowBytes, roff[x]);
+                sc = mfma32x32x16(aq, kf[x], sc);
+                dp = mfma32x32x16(ag, vf[x], dp);
+            }
             // P = exp2(scale log2e S - LSE log2e), dS = P (dP - Delta); the
             // subtree-interval predicate only in partial tiles (separate code
             // path so full tiles carry no mask arithmetic)
+            f32x4 l2[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) l2[j] = lds_f32x4(lsp + 4 * (32 * c + 8 * j + 4 * h));
             auto elementwise = [&](auto masked) {
+                // register r is query q0 + o_r with o_r = 8 (r / 4) + r % 4;
+                // key <= q <= se[key]  <=>  key - q0 <= o_r <= se[key] - q0
+                int lo = 0, hi = 0;
+                if constexpr (decltype(masked)::value) {
+                    const int q0 = qbase + 32 * c + 4 * h;
+                    lo = key - q0;
+                    hi = sek - q0;
+                }
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const int key = kw0 + 16 * ks + n;
-#pragma unroll
-                    for (int e = 0; e < 2; ++e)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            float p = fast_exp2(__builtin_fmaf(s[ks][e][r], scale_log2, -l2[e][r]));
-                            if constexpr (decltype(masked)::value) {
-                                const int qi = qbase + 32 * c + 16 * e + 4 * g + r;
-                                p = (key <= qi && qi <= sek[ks]) ? p : 0.f;
-                            }
-                            s[ks][e][r] = p;
-                            dp[ks][e][r] = p * dp[ks][e][r];
-                        }
-                    pb[ks] = to_bf16x8(s[ks][0], s[ks][1]);
-                    db[ks] = to_bf16x8(dp[ks][0], dp[ks][1]);
+                for (int r = 0; r < 16; ++r) {
+                    float p = fast_exp2(__builtin_fmaf(sc[r], scale_log2, -l2[r / 4][r % 4]));
+                    if constexpr (decltype(masked)::value) {
+                        const int o = 8 * (r / 4) + r % 4;
+                        p = (lo <= o && o <= hi) ? p : 0.f;
+                    }
+                    sc[r] = p;
+                    dp[r] = p * dp[r];
                 }
             };
             if (partial)
                 elementwise(std::true_type{});
             else
                 elementwise(std::false_type{});
+            // B operands of the gradient products, k-step m = queries
+            // 32 c + 16 m + {4 h + 0..3, 8 + 4 h + 0..3}
+            bf16x8 pb[2], db[2];
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const bf16x8 ag = join_tr(T::tr_frag(gt, 32 * c + 4 * g, 16 * t, n),
-                                          T::tr_frag(gt, 32 * c + 16 + 4 * g, 16 * t, n));
-                const bf16x8 aq = join_tr(T::tr_frag(qt, 32 * c + 4 * g, 16 * t, n),
-                                          T::tr_frag(qt, 32 * c + 16 + 4 * g, 16 * t, n));
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    dv[ks][t] = mfma16x16x32(ag, pb[ks], dv[ks][t]);
-                    dk[ks][t] = mfma16x16x32(aq, db[ks], dk[ks][t]);
-                }
+            for (int m = 0; m < 2; ++m) {
+                pb[m] = to_bf16x8(f32x4{sc[8 * m], sc[8 * m + 1], sc[8 * m + 2], sc[8 * m + 3]},
+                                  f32x4{sc[8 * m + 4], sc[8 * m + 5], sc[8 * m + 6], sc[8 * m + 7]});
+                db[m] = to_bf16x8(f32x4{dp[8 * m], dp[8 * m + 1], dp[8 * m + 2], dp[8 * m + 3]},
+                                  f32x4{dp[8 * m + 4], dp[8 * m + 5], dp[8 * m + 6], dp[8 * m + 7]});
             }
+            // dV^T += dO^T P, dK^T += Q^T dS: A = 32 d x 16 queries read
+            // transposed from the row-major tiles, in the same k order
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    // rows 32 c + 16 m + 4 h + {0..3, 8..11}: the 16-row
+                    // shift keeps the swizzle phase, so it is a plain offset
+                    const int rb = (32 * c + 16 * m) * T::kRowBytes;
+                    const bf16x8 ag = join_tr(T::tr_at(gt + rb, toff[t][0]), T::tr_at(gt + rb, toff[t][1]));
+                    const bf16x8 aq = join_tr(T::tr_at(qt + rb, toff[t][0]), T::tr_at(qt + rb, toff[t][1]));
+                    dv[t] = mfma32x32x16(ag, pb[m], dv[t]);
+                    dk[t] = mfma32x32x16(aq, db[m], dk[t]);
+                }
         }
 
         wait_vm_all();
         __syncthreads();
     }
 
-    // lane holds key (kw0 + 16 ks + n), d = 16 t + 4 g .. +3
+    // lane holds key kw0 + j32, d = 32 t + 8 j + 4 h + 0..3 in registers 4 j + 0..3
+    const int64_t off = int64_t(key) * kv_stride + hkv * D + 4 * h;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        const int64_t off = int64_t(kw0 + 16 * ks + n) * kv_stride + hkv * D + 4 * g;
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const f32x4 a = dk[ks][t] * scale, b = dv[ks][t];
-            st8(dK + off + 16 * t, u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])});
-            st8(dV + off + 16 * t, u32x2{pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])});
+        for (int j = 0; j < 4; ++j) {
+            const int d0 = 32 * t + 8 * j;
+            st8(dK + off + d0, u32x2{pack_bf16x2(dk[t][4 * j] * scale, dk[t][4 * j + 1] * scale),
+                                     pack_bf16x2(dk[t][4 * j + 2] * scale, dk[t][4 * j + 3] * scale)});
+            st8(dV + off + d0, u32x2{pack_bf16x2(dv[t][4 * j], dv[t][4 * j + 1]),
+                                     pack_bf16x2(dv[t][4 * j + 2], dv[t][4 * j + 3])});
         }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -323,7 +336,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_bf16_kernel(
     for (int qs = 0; qs < 2; ++qs) {
         const int qi = qrow0 + 16 * qs + n;
         lse2[qs] = LSE[int64_t(h) * L + qi] * kLog2e;
-        dlt[qs] = Delta[int64_t(h) * L + qi];
+        dlt[qs] = -Delta[int64_t(h) * L + qi];  // stored negated
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             qf[qs][s] = __builtin_bit_cast(bf16x8, ld16(Q + int64_t(qi) * q_stride + int64_t(h) * D + 32 * s + 8 * g));

@@ -9,6 +9,17 @@
 // operand whose row/column index is that column and whose k index runs over
 // C's rows -- which lets a score tile feed the next product without a
 // shuffle, provided the k order is permuted consistently on both operands.
+//
+// v_mfma_f32_32x32x16_bf16, D = A * B + C with A 32x16, B 16x32, C/D 32x32:
+//   A operand: lane l holds row (l % 32), k = 8 (l / 32) + 0..7
+//   B operand: lane l holds column (l % 32), k = 8 (l / 32) + 0..7
+//   C/D:       lane l, register r holds column (l % 32),
+//              row 8 (r / 4) + 4 (l / 32) + r % 4
+// (both layouts checked element by element on gfx950 with random integer
+// operands).  For a k-step of 16 C rows starting at 16m, lane l holds rows
+// 16m + 4 (l / 32) + 0..3 in registers 8m + 0..3 and rows
+// 16m + 8 + 4 (l / 32) + 0..3 in registers 8m + 4..7: eight values that
+// serve as a B operand over those rows in that k order.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -27,6 +38,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

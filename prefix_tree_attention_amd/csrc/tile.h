@@ -50,7 +50,9 @@ struct Tile {
         else
             return (r & 7) ^ (2 * ((r >> 3) & 1));
     }
-    // byte offset of (row, chunk) inside the tile
+    static constexpr int kRowBytes = D * 2;
+    // byte offset of (row, chunk) inside the tile; the swizzle depends on
+    // r % 16 only, so moving 16 rows down is a plain add of 16 kRowBytes
     __device__ static __forceinline__ int slot(int r, int c) { return (r * kChunks + (c ^ swz(r))) * 16; }
 
     // Issue this wave's share of the direct loads of one tile.  `g0` points
@@ -77,12 +79,21 @@ struct Tile {
 
     // Transposed operand: for a 16-lane group whose 4 rows start at r0, lane
     // i (0..15) gets element e0 + i of rows r0..r0+3 (e0 a multiple of 16).
-    __device__ static __forceinline__ i16x4 tr_frag(const lds_char* tile, int r0, int e0, int i) {
+    __device__ static __forceinline__ int tr_offset(int r0, int e0, int i) {
         const int r = r0 + (i >> 2);
         const int e = e0 + 4 * (i & 3);
-        const int off = slot(r, e >> 3) + ((e >> 2) & 1) * 8;
+        return slot(r, e >> 3) + ((e >> 2) & 1) * 8;
+    }
+    __device__ static __forceinline__ i16x4 tr_at(const lds_char* base, int off) {
         return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<__attribute__((address_space(3))) i16x4*>(const_cast<lds_char*>(tile) + off));
+            reinterpret_cast<__attribute__((address_space(3))) i16x4*>(const_cast<lds_char*>(base) + off));
+    }
+    __device__ static __forceinline__ i16x4 tr_frag(const lds_char* tile, int r0, int e0, int i) {
+        return tr_at(tile, tr_offset(r0, e0, i));
+    }
+    // Row-major operand at a precomputed byte offset.
+    __device__ static __forceinline__ bf16x8 frag_at(const lds_char* base, int off) {
+        return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(base + off);
     }
 };
 
