@@ -44,38 +44,48 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const int32_t* __restrict__ q_order, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ row_ent, int L, int Hq, int Hkv, float scale_log2) {
     using T = Tile<D>;
-    constexpr int NS = D / 32;  // k-steps of QK^T
-    constexpr int NT = D / 16;  // d-blocks of O^T
+    constexpr int NX = D / 16;  // k-steps of S^T = K Q^T
+    constexpr int NT = D / 32;  // 32-row d-blocks of O^T
     __shared__ __attribute__((aligned(1024))) char smem_raw[4 * T::kBytes];
     lds_char* const smem = (lds_char*)smem_raw;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n = lane & 15, g = lane >> 4;
+    // 32x32x16 fragments: lane = MFMA column j32 (this lane's query) and k-half h
+    const int j32 = lane & 31, h = lane >> 5;
+    const int tr_e = 16 * ((lane >> 4) & 1), tr_i = lane & 15;
     // work item: key/value-head major, then query blocks heaviest first,
     // then the query heads of the group
     const int G = Hq / Hkv, per_kv = (int(gridDim.x) / Hq) * G;
     const int work = xcd_logical_block();
-    const int hkv = work / per_kv, rank = (work % per_kv) / G, h = hkv * G + work % G;
+    const int hkv = work / per_kv, rank = (work % per_kv) / G, h_q = hkv * G + work % G;
     const int qb = q_order[rank];
     const int64_t q_stride = int64_t(Hq) * D, kv_stride = int64_t(Hkv) * D;
-    const int qrow0 = qb * kBlock + 32 * wave;  // first query of this wave
+    const int qi = qb * kBlock + 32 * wave + j32;  // this lane's query
 
-    // Q^T operand: lane holds query (qrow0 + 16 qs + n), d = 32 s + 8 g .. +7
-    bf16x8 qf[2][NS];
+    // Q^T operand (B of S^T): lane holds query qi, d = 16 x + 8 h .. +7
+    bf16x8 qf[NX];
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs)
+    for (int x = 0; x < NX; ++x)
+        qf[x] = __builtin_bit_cast(bf16x8, ld16(Q + int64_t(qi) * q_stride + int64_t(h_q) * D + 16 * x + 8 * h));
+    // loop-invariant swizzled LDS offsets of this lane's operand reads
+    int roff[NX];  // K rows: row j32, chunk 2 x + h
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
-            qf[qs][s] = __builtin_bit_cast(
-                bf16x8, ld16(Q + int64_t(qrow0 + 16 * qs + n) * q_stride + int64_t(h) * D + 32 * s + 8 * g));
+    for (int x = 0; x < NX; ++x) roff[x] = T::slot(j32, 2 * x + h);
+    int toff[NT][2];  // V^T: d-block t, key rows 4 h + 8 v + 0..3
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int v = 0; v < 2; ++v) toff[t][v] = T::tr_offset(4 * h + 8 * v, 32 * t + tr_e, tr_i);
 
-    f32x4 oacc[2][NT];
+    // O^T accumulators: block t, register r = d 32 t + 8 (r / 4) + 4 h + r % 4
+    f32x16 oacc[NT];
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) oacc[qs][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+        for (int r = 0; r < 16; ++r) oacc[t][r] = 0.f;
+    // running max (scaled units) and this lane's partial row sum
+    float m_run = -INFINITY, l_run = 0.f;
 
     const int beg = row_ptr[qb], nsteps = 2 * (row_ptr[qb + 1] - beg);
     const int kvs = int(kv_stride);
@@ -100,96 +110,90 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         const lds_char* kt = ktile(buf);
         const lds_char* vt = vtile(buf);
 
-        // S^T = K Q^T (unscaled): block b = keys 16b..16b+15; lane holds
-        // query column n of group qs, keys 16b + 4g + 0..3
-        f32x4 sc[2][4];
+        // S^T = K Q^T (unscaled) for the step's two 32-key blocks kk:
+        // register r holds key kbase + 32 kk + 8 (r / 4) + 4 h + r % 4
+        // against this lane's query
+        f32x16 sc[2];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            bf16x8 a[NS];
+        for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-            for (int s = 0; s < NS; ++s) a[s] = T::row_frag(kt, 16 * b + n, 4 * s + g);
+            for (int r = 0; r < 16; ++r) sc[kk][r] = 0.f;
 #pragma unroll
-            for (int qs = 0; qs < 2; ++qs) {
-                f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < NS; ++s) c = mfma16x16x32(a[s], qf[qs][s], c);
-                sc[qs][b] = c;
-            }
+            for (int x = 0; x < NX; ++x)
+                sc[kk] = mfma32x32x16(T::frag_at(kt + 32 * kk * T::kRowBytes, roff[x]), qf[x], sc[kk]);
         }
 
         if (partial) {
-            i32x4 sek[4];
+            // key <= qi  <=>  8 (r / 4) + r % 4 <= qi - (kbase + 32 kk + 4 h)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) sek[b] = *reinterpret_cast<const i32x4*>(se + kbase + 16 * b + 4 * g);
+            for (int kk = 0; kk < 2; ++kk) {
+                const int k0 = kbase + 32 * kk + 4 * h, lim = qi - k0;
 #pragma unroll
-            for (int qs = 0; qs < 2; ++qs) {
-                const int qi = qrow0 + 16 * qs + n;
+                for (int j = 0; j < 4; ++j) {
+                    const i32x4 sek = *reinterpret_cast<const i32x4*>(se + k0 + 8 * j);
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int key = kbase + 16 * b + 4 * g + r;
-                        if (!(key <= qi && qi <= sek[b][r])) sc[qs][b][r] = -INFINITY;
-                    }
-            }
-        }
-
-        // online softmax in base 2, one query column per lane; the running
-        // max is kept in scaled units and the scale is folded into the FMA
-        // that forms the exp2 argument.
-        bf16x8 pb[2][2];
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
-            // maximum (not maxnum) chains lower to v_maximum3_f32 with no
-            // NaN-quieting of the accumulator inputs
-            float mx = -INFINITY;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, sc[qs][b][0]), sc[qs][b][1]);
-                mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, sc[qs][b][2]), sc[qs][b][3]);
-            }
-            mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 16));
-            mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32));
-            // The reference max only moves when some lane's tile max exceeds
-            // it by more than kRescaleSlack (log2 units).  O and l are both
-            // relative to the same reference, so a stale one changes nothing
-            // but the magnitude of p, which stays <= 2^kRescaleSlack; the
-            // O rescale thus runs a few times per row instead of nearly
-            // every step.
-            const float mt = mx * scale_log2;
-            if (__any(mt > m_run[qs] + kRescaleSlack)) {
-                const float mnew = fmaxf(m_run[qs], mt);
-                const float alpha = fast_exp2(m_run[qs] - (mnew == -INFINITY ? 0.f : mnew));
-                l_run[qs] *= alpha;
-#pragma unroll
-                for (int t = 0; t < NT; ++t) oacc[qs][t] *= alpha;
-                m_run[qs] = mnew;
-            }
-            const float muse = m_run[qs] == -INFINITY ? 0.f : m_run[qs];
-            float rs = 0.f;
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float p = fast_exp2(__builtin_fmaf(sc[qs][b][r], scale_log2, -muse));
-                    sc[qs][b][r] = p;
-                    rs += p;
+                    for (int i = 0; i < 4; ++i)
+                        if (!(8 * j + i <= lim && qi <= sek[i])) sc[kk][4 * j + i] = -INFINITY;
                 }
-            l_run[qs] += rs;
-            pb[qs][0] = to_bf16x8(sc[qs][0], sc[qs][1]);
-            pb[qs][1] = to_bf16x8(sc[qs][2], sc[qs][3]);
+            }
         }
 
-        // O^T += V^T P^T: k-step c pairs key rows 32c + 4g + 0..3 and
-        // 32c + 16 + 4g + 0..3 (blocks 2c and 2c+1)
+        // online softmax in base 2, one query per lane (its keys split over
+        // the lane pair l, l ^ 32); the running max is kept in scaled units
+        // and the scale is folded into the FMA that forms the exp2 argument.
+        // maximum (not maxnum) chains lower to v_maximum3_f32 with no
+        // NaN-quieting of the accumulator inputs.
+        float mx = -INFINITY;
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const bf16x8 a = join_tr(T::tr_frag(vt, 32 * c + 4 * g, 16 * t, n),
-                                         T::tr_frag(vt, 32 * c + 16 + 4 * g, 16 * t, n));
+            for (int r = 0; r < 16; r += 2)
+                mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, sc[kk][r]), sc[kk][r + 1]);
+        mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32));
+        // The reference max only moves when some lane's tile max exceeds it
+        // by more than kRescaleSlack (log2 units).  O and l are both
+        // relative to the same reference, so a stale one changes nothing but
+        // the magnitude of p, which stays <= 2^kRescaleSlack; the O rescale
+        // thus runs a few times per row instead of nearly every step.
+        const float mt = mx * scale_log2;
+        if (__any(mt > m_run + kRescaleSlack)) {
+            const float mnew = fmaxf(m_run, mt);
+            const float alpha = fast_exp2(m_run - (mnew == -INFINITY ? 0.f : mnew));
+            l_run *= alpha;
 #pragma unroll
-                for (int qs = 0; qs < 2; ++qs) oacc[qs][t] = mfma16x16x32(a, pb[qs][c], oacc[qs][t]);
+            for (int t = 0; t < NT; ++t) oacc[t] *= alpha;
+            m_run = mnew;
+        }
+        const float muse = m_run == -INFINITY ? 0.f : m_run;
+        float rs = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = fast_exp2(__builtin_fmaf(sc[kk][r], scale_log2, -muse));
+                sc[kk][r] = p;
+                rs += p;
+            }
+        l_run += rs;
+        // P^T operands, k-step m = keys 16 m + {4 h + 0..3, 8 + 4 h + 0..3}
+        bf16x8 pb[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const f32x16& a = sc[m / 2];
+            const int b = 8 * (m % 2);
+            pb[m] = to_bf16x8(f32x4{a[b], a[b + 1], a[b + 2], a[b + 3]},
+                              f32x4{a[b + 4], a[b + 5], a[b + 6], a[b + 7]});
+        }
+
+        // O^T += V^T P^T: A = 32 d x 16 keys read transposed from the V tile
+        // in the same key order (rows 16 m + 4 h + {0..3, 8..11})
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int rb = 16 * m * T::kRowBytes;
+                const bf16x8 a = join_tr(T::tr_at(vt + rb, toff[t][0]), T::tr_at(vt + rb, toff[t][1]));
+                oacc[t] = mfma32x32x16(a, pb[m], oacc[t]);
             }
 
         wait_vm_all();
@@ -197,21 +201,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     }
 
     // epilogue: normalise, write O (bf16) and LSE (natural log)
+    float l = l_run + __shfl_xor(l_run, 32);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    bf16* orow = O + int64_t(qi) * q_stride + int64_t(h_q) * D + 4 * h;
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-        float l = l_run[qs];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        const int qi = qrow0 + 16 * qs + n;
-        bf16* orow = O + int64_t(qi) * q_stride + int64_t(h) * D;
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const f32x4 v = oacc[qs][t] * inv;
-            st8(orow + 16 * t + 4 * g, u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
+        for (int j = 0; j < 4; ++j) {
+            const f32x16& a = oacc[t];
+            st8(orow + 32 * t + 8 * j, u32x2{pack_bf16x2(a[4 * j] * inv, a[4 * j + 1] * inv),
+                                             pack_bf16x2(a[4 * j + 2] * inv, a[4 * j + 3] * inv)});
         }
-        if (g == 0) LSE[int64_t(h) * L + qi] = l > 0.f ? (m_run[qs] + __log2f(l)) * 0.69314718055994531f : -INFINITY;
-    }
+    if (h == 0) LSE[int64_t(h_q) * L + qi] = l > 0.f ? (m_run + __log2f(l)) * 0.69314718055994531f : -INFINITY;
 }
 
 }  // namespace
