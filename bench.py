@@ -164,34 +164,44 @@ def main(argv=None):
     stream = torch.cuda.current_stream(dev)
 
     # ---------------- untimed setup ----------------
+    # All tries of the batch are laid end to end (tree_pack_concat) and run
+    # as one launch: no attention crosses tries, so the concatenation is a
+    # packed layout of its own, and one launch avoids per-trie launch and
+    # tail costs on batches of many small tries.
     tries, stats = pta.pack(w.ids, w.mask, w.max_tokens_per_mb)
-    log(f"workload {w.name}: {len(tries)} tries, L={[t.L for t in tries]}, tree tokens {stats['tree_tokens']}, "
-        f"pairs {stats['n_pairs']}, unpacked pairs {stats['unpacked_pairs']}")
+    se_cat, lengths, _ = pta.pack_concat(w.ids, w.mask, w.max_tokens_per_mb)
+    log(f"workload {w.name}: {len(tries)} tries, L={lengths}, one launch of L={len(se_cat)}, tree tokens "
+        f"{stats['tree_tokens']}, pairs {stats['n_pairs']}, unpacked pairs {stats['unpacked_pairs']}")
+    if len(se_cat) > (1 << 20):
+        raise SystemExit(f"batch of {len(se_cat)} packed tokens exceeds one launch (2^20)")
     bufs = []
     pairs_per_trie = []
     for i, tr in enumerate(tries):
-        q, k, v, do = workloads.attention_inputs(tr.L, w.hq, w.hkv, w.d, "bf16", w.qkv_std, 1_000_000 + i)
-        L = tr.L
-        nb = L // 128
         se_i64 = tr.subtree_end.astype(np.int64)
         real = se_i64 >= 0
-        pairs_per_trie.append(int((se_i64[real] - np.arange(L)[real] + 1).sum()))
-        bufs.append({
-            "L": L,
-            "q": q.to(dev), "k": k.to(dev), "v": v.to(dev), "do": do.to(dev),
-            "o": torch.empty((L, w.hq, w.d), dtype=torch.bfloat16, device=dev),
-            "lse": torch.empty((w.hq, L), dtype=torch.float32, device=dev),
-            "dq": torch.empty((L, w.hq, w.d), dtype=torch.bfloat16, device=dev),
-            "dk": torch.empty((L, w.hkv, w.d), dtype=torch.bfloat16, device=dev),
-            "dv": torch.empty((L, w.hkv, w.d), dtype=torch.bfloat16, device=dev),
-            "se": torch.empty(L, dtype=torch.int32, device=dev),
-            "pos": torch.empty(L, dtype=torch.int32, device=dev),
-            "tc": torch.empty((nb, nb), dtype=torch.uint8, device=dev),
-            "mws": torch.empty(pta.meta_workspace_bytes(L), dtype=torch.uint8, device=dev),
-            "bws": torch.empty(pta.bwd_workspace_bytes(L, w.hq, w.d), dtype=torch.uint8, device=dev),
-            "pinned": [torch.empty(L, dtype=torch.int32).pin_memory() for _ in range(2)],
-            "copied": [None, None],
-        })
+        pairs_per_trie.append(int((se_i64[real] - np.arange(tr.L)[real] + 1).sum()))
+    parts = [workloads.attention_inputs(tr.L, w.hq, w.hkv, w.d, "bf16", w.qkv_std, 1_000_000 + i)
+             for i, tr in enumerate(tries)]
+    q, k, v, do = (torch.cat([p_[j] for p_ in parts]) for j in range(4))
+    del parts
+    L = len(se_cat)
+    nb = L // 128
+    bufs.append({
+        "L": L,
+        "q": q.to(dev), "k": k.to(dev), "v": v.to(dev), "do": do.to(dev),
+        "o": torch.empty((L, w.hq, w.d), dtype=torch.bfloat16, device=dev),
+        "lse": torch.empty((w.hq, L), dtype=torch.float32, device=dev),
+        "dq": torch.empty((L, w.hq, w.d), dtype=torch.bfloat16, device=dev),
+        "dk": torch.empty((L, w.hkv, w.d), dtype=torch.bfloat16, device=dev),
+        "dv": torch.empty((L, w.hkv, w.d), dtype=torch.bfloat16, device=dev),
+        "se": torch.empty(L, dtype=torch.int32, device=dev),
+        "pos": torch.empty(L, dtype=torch.int32, device=dev),
+        "tc": torch.empty((nb, nb), dtype=torch.uint8, device=dev),
+        "mws": torch.empty(pta.meta_workspace_bytes(L), dtype=torch.uint8, device=dev),
+        "bws": torch.empty(pta.bwd_workspace_bytes(L, w.hq, w.d), dtype=torch.uint8, device=dev),
+        "pinned": [torch.empty(L, dtype=torch.int32).pin_memory() for _ in range(2)],
+        "copied": [None, None],
+    })
     assert sum(pairs_per_trie) == stats["n_pairs"]
     torch.cuda.synchronize()
     lib = pta.lib()
@@ -201,15 +211,14 @@ def main(argv=None):
     scale = 1.0 / math.sqrt(w.d)
 
     def launch(k_step, cur, events):
-        """Enqueue one step's device work for the pack `cur`."""
-        assert len(cur) == len(bufs)
+        """Enqueue one step's device work for the packed layout `cur`."""
         slot = k_step % 2
-        for i, tr in enumerate(cur):
+        for i, se_host in enumerate([cur]):
             b = bufs[i]
-            assert tr.L == b["L"]
+            assert len(se_host) == b["L"]
             if b["copied"][slot] is not None:
                 b["copied"][slot].synchronize()  # the copy that last read this pinned buffer is done
-            b["pinned"][slot].numpy()[:] = tr.subtree_end
+            b["pinned"][slot].numpy()[:] = se_host
             b["se"].copy_(b["pinned"][slot], non_blocking=True)
             ev = torch.cuda.Event()
             ev.record(stream)
@@ -237,7 +246,7 @@ def main(argv=None):
                 events.append((i, E))
 
     def pack_host():
-        cur, _ = pta.pack(w.ids, w.mask, w.max_tokens_per_mb)
+        cur, _, _ = pta.pack_concat(w.ids, w.mask, w.max_tokens_per_mb)
         return cur
 
     # Steady-state pipeline: the device work of step k is enqueued, then the
@@ -313,7 +322,7 @@ def main(argv=None):
         "gpu_ms_per_step": round(gpu_ms_per_step, 3),
         "host_pack_ms_per_step": round(t_pack / a.steps * 1e3, 3),
         "kernel_ms_per_launch": {p: round(avg[p], 4) for p in PHASES},
-        "config": {"workload": w.name, "tries": len(bufs), "L": [b["L"] for b in bufs], "hq": w.hq,
+        "config": {"workload": w.name, "tries": len(tries), "L": lengths, "launch_L": bufs[0]["L"], "hq": w.hq,
                    "hkv": w.hkv, "head_dim": w.d, "max_tokens_per_mb": w.max_tokens_per_mb,
                    "tree_tokens": tokens, "pairs": n_pairs, "parallelism": "single-gpu"},
         "roofline": roof,

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define TREE_ATTN_ABI_VERSION 1
+#define TREE_ATTN_ABI_VERSION 2
 
 /* status codes */
 #define TREE_OK 0
@@ -128,6 +128,18 @@ int tree_pack_trie(const tree_pack_t* p, int64_t t, tree_trie_view* v);
 
 /* Accounting of the whole pack (guide, section 指标与监控). */
 int tree_pack_stats(const tree_pack_t* p, tree_pack_stats_t* s);
+
+/* All tries of a pack laid end to end, for one launch over the whole batch.
+ * No attention crosses tries (a subtree never leaves its trie), so the
+ * concatenation is itself a valid packed layout: trie t occupies
+ * [off_t, off_t + L_t) with off_t the sum of the earlier L, its subtree
+ * ends are shifted by off_t and pads stay -1; position ids, tile classes
+ * and every attention result restricted to trie t's rows are those of trie
+ * t alone, and tiles across tries classify as empty.  Writes the total
+ * length to *L_total; when out_se is non-NULL it receives the *L_total
+ * concatenated subtree ends and cap (its capacity in int32) must be at
+ * least that.  Errors: TREE_E_ARG (NULL pack or L_total, cap too small). */
+int tree_pack_concat(const tree_pack_t* p, int32_t* out_se, int64_t cap, int64_t* L_total);
 
 /* Release a pack (NULL is a no-op). */
 void tree_pack_free(tree_pack_t* p);

@@ -14,6 +14,7 @@ from .api import (  # noqa: F401
     PackedTrie,
     TreeMeta,
     pack,
+    pack_concat,
     tree_meta,
     meta_workspace_bytes,
     bwd_workspace_bytes,

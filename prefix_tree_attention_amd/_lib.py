@@ -63,6 +63,7 @@ SIGNATURES = {
     "tree_pack_num_tries": (c_i64, [c_vp]),
     "tree_pack_trie": (ctypes.c_int, [c_vp, c_i64, ctypes.POINTER(TrieView)]),
     "tree_pack_stats": (ctypes.c_int, [c_vp, ctypes.POINTER(PackStats)]),
+    "tree_pack_concat": (ctypes.c_int, [c_vp, c_vp, c_i64, ctypes.POINTER(c_i64)]),
     "tree_pack_free": (None, [c_vp]),
     "tree_meta_workspace_bytes": (c_sz, [c_i64]),
     "tree_meta": (ctypes.c_int, [c_vp, c_i64, c_vp, c_vp, c_vp, c_sz, c_vp]),

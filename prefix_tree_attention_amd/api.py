@@ -81,6 +81,38 @@ def pack(ids, mask, max_tokens_per_mb: int, block_size: int = BLOCK, pad_to_maxi
     return tries, stats
 
 
+def pack_concat(ids, mask, max_tokens_per_mb: int, block_size: int = BLOCK, pad_to_maximum: bool = False,
+                pad_id: int = 0):
+    """Pack a batch and lay its tries end to end (``tree_pack`` then
+    ``tree_pack_concat``), for one launch over the whole batch.  Returns
+    ``(subtree_end, lengths, stats)``: the concatenated int32 subtree ends,
+    each trie's padded length in order, and the pack's accounting."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    if ids.ndim != 2 or ids.shape != mask.shape:
+        raise TreeAttnError(-5, "ids and mask must both be [B, S]")
+    L = lib()
+    h = ctypes.c_void_p()
+    check(L.tree_pack(ids.ctypes.data, mask.ctypes.data, ids.shape[0], ids.shape[1], int(max_tokens_per_mb),
+                      int(block_size), int(bool(pad_to_maximum)), int(pad_id), ctypes.byref(h)))
+    try:
+        total = ctypes.c_int64()
+        check(L.tree_pack_concat(h, None, 0, ctypes.byref(total)))
+        se = np.empty(int(total.value), dtype=np.int32)
+        check(L.tree_pack_concat(h, se.ctypes.data, se.size, ctypes.byref(total)))
+        lengths = []
+        for t in range(L.tree_pack_num_tries(h)):
+            v = TrieView()
+            check(L.tree_pack_trie(h, t, ctypes.byref(v)))
+            lengths.append(int(v.L))
+        s = PackStats()
+        check(L.tree_pack_stats(h, ctypes.byref(s)))
+        stats = {k: getattr(s, k) for k, _ in PackStats._fields_}
+    finally:
+        L.tree_pack_free(h)
+    return se, lengths, stats
+
+
 # ---------------------------------------------------------------------------
 # device side
 # ---------------------------------------------------------------------------

@@ -31,7 +31,7 @@ constexpr int64_t kMaxL = 1 << 20;   // largest packed length accepted
 struct MetaLayout {
     int64_t L, nb, T;
     int64_t hdr, blk_min, blk_max, hist, row_cnt, row_ptr, row_ent, col_cnt, col_ptr, col_ent,
-        q_order, k_order, words;
+        q_order, k_order, blk_cnt, blk_hsum, words;
 };
 
 inline int64_t pad64(int64_t w) { return (w + 63) / 64 * 64; }
@@ -54,6 +54,8 @@ inline MetaLayout meta_layout(int64_t L) {
     m.col_ent = o; o += pad64(m.T);
     m.q_order = o; o += pad64(m.nb);
     m.k_order = o; o += pad64(m.nb);
+    m.blk_cnt = o; o += pad64(m.nb);   // real tokens per block, then their exclusive prefix
+    m.blk_hsum = o; o += pad64(m.nb);  // histogram mass per block, then its exclusive prefix
     m.words = o;
     return m;
 }

@@ -1,6 +1,8 @@
 // Metadata kernels of libtreeattn (tree_meta): position ids, 128x128 tile
 // classes and the tile lists of the attention kernels, all derived from the
-// per-token subtree ends se[L] in O(L + nb^2) work.
+// per-token subtree ends se[L] in O(L + nb^2) work spread over one
+// workgroup per 128-token block; a single workgroup only scans and sorts
+// per-block values.
 //
 // AReaL tree-training guide, section 打包数据的生成: a token's position id is
 // the number of tokens it may attend to, minus one.  Key j is visible to
@@ -12,18 +14,20 @@
 // se over the key block (pads count as -1): empty iff hi < 128 qb, full iff
 // lo >= 128 qb + 127, else partial.  A diagonal tile is partial iff its
 // block holds a real token; tiles above the diagonal are empty.  These rules
-// are exact, not conservative.
+// are exact, not conservative.  They also put column kb's nonempty tiles in
+// closed form: the contiguous range qb = kb .. hi / 128 (when the block
+// holds a real token, hi >= 128 kb), full exactly for kb < qb <=
+// (lo - 127) / 128.
 
 #include "device.h"
 
 namespace treeattn {
 namespace {
 
-__global__ void meta_init(int32_t* __restrict__ hist, int64_t n_hist, int32_t* __restrict__ col_cnt,
-                          int nb, int32_t* __restrict__ hdr, int64_t L) {
+__global__ void meta_init(int32_t* __restrict__ hist, int64_t n_hist, int32_t* __restrict__ hdr, int64_t L,
+                          int nb) {
     const int64_t stride = int64_t(gridDim.x) * blockDim.x;
     for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n_hist; i += stride) hist[i] = 0;
-    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < nb; i += stride) col_cnt[i] = 0;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         hdr[0] = int32_t(L);
         hdr[1] = nb;
@@ -31,11 +35,12 @@ __global__ void meta_init(int32_t* __restrict__ hist, int64_t n_hist, int32_t* _
     }
 }
 
-// One workgroup per 128-token block: histogram of subtree ends and the
-// block's min / max subtree end.
+// One workgroup per 128-token block: histogram of subtree ends, the block's
+// min / max subtree end and its real-token count.
 __global__ __launch_bounds__(128) void meta_blocks(const int32_t* __restrict__ se, int32_t* __restrict__ hist,
                                                    int32_t* __restrict__ blk_min, int32_t* __restrict__ blk_max,
-                                                   int32_t* __restrict__ hdr, int L) {
+                                                   int32_t* __restrict__ blk_cnt, int32_t* __restrict__ hdr,
+                                                   int L) {
     const int b = blockIdx.x;
     const int j = b * kBlock + threadIdx.x;
     int s = se[j];
@@ -65,47 +70,62 @@ __global__ __launch_bounds__(128) void meta_blocks(const int32_t* __restrict__ s
     }
     __syncthreads();
     if (threadIdx.x == 0) {
+        const int nreal = sreal[0] + sreal[1];
         blk_min[b] = min(smn[0], smn[1]);
         blk_max[b] = max(smx[0], smx[1]);
-        if (sreal[0] + sreal[1]) atomicAdd(&hdr[2], sreal[0] + sreal[1]);
+        blk_cnt[b] = nreal;
+        if (nreal) atomicAdd(&hdr[2], nreal);
     }
+}
+
+// Class of tile (qb, kb): 0 empty, 1 partial, 2 full; lo / hi are the key
+// block's min / max subtree end.
+__device__ __forceinline__ int tile_class_of(int qb, int kb, int lo, int hi) {
+    if (kb > qb) return 0;
+    if (kb == qb) return hi >= 0 ? 1 : 0;
+    return hi < qb * kBlock ? 0 : (lo >= qb * kBlock + kBlock - 1 ? 2 : 1);
+}
+
+// Sum of one int per thread over the workgroup (blockDim.x a multiple of 64,
+// at most 16 waves); `sh` holds >= 16 ints.
+__device__ inline int block_sum(int x, int* sh) {
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[wave] = x;
+    __syncthreads();
+    int t = 0;
+    for (int w = 0; w < nw; ++w) t += sh[w];
+    return t;
 }
 
 // One workgroup per query block: the class of every tile of its row, the
-// row's nonempty count, and per-column nonempty counts.
+// row's nonempty count, and the block's histogram mass.
 __global__ __launch_bounds__(256) void meta_tiles(const int32_t* __restrict__ blk_min,
                                                   const int32_t* __restrict__ blk_max,
-                                                  uint8_t* __restrict__ tc, int32_t* __restrict__ row_cnt,
-                                                  int32_t* __restrict__ col_cnt, int nb) {
+                                                  const int32_t* __restrict__ hist, uint8_t* __restrict__ tc,
+                                                  int32_t* __restrict__ row_cnt, int32_t* __restrict__ blk_hsum,
+                                                  int nb) {
     const int qb = blockIdx.x;
-    const int qlo = qb * kBlock, qhi = qb * kBlock + kBlock - 1;
     int cnt = 0;
     for (int kb = threadIdx.x; kb < nb; kb += blockDim.x) {
-        int c;
-        if (kb > qb)
-            c = 0;
-        else if (kb == qb)
-            c = blk_max[kb] >= 0 ? 1 : 0;
-        else {
-            const int lo = blk_min[kb], hi = blk_max[kb];
-            c = hi < qlo ? 0 : (lo >= qhi ? 2 : 1);
-        }
+        const int c = tile_class_of(qb, kb, blk_min[kb], blk_max[kb]);
         tc[int64_t(qb) * nb + kb] = uint8_t(c);
-        if (c) {
-            ++cnt;
-            atomicAdd(&col_cnt[kb], 1);
-        }
+        cnt += c != 0;
     }
-    for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
-    __shared__ int part[4];
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = cnt;
-    __syncthreads();
-    if (threadIdx.x == 0) row_cnt[qb] = part[0] + part[1] + part[2] + part[3];
+    const int hs = threadIdx.x < kBlock ? hist[qb * kBlock + threadIdx.x] : 0;
+    __shared__ int sh[16];
+    const int rc = block_sum(cnt, sh);
+    const int hm = block_sum(hs, sh);
+    if (threadIdx.x == 0) {
+        row_cnt[qb] = rc;
+        blk_hsum[qb] = hm;
+    }
 }
 
 // Exclusive scan of one value per thread across a 1024-thread workgroup.
-// Returns the exclusive prefix; *total receives the sum.  Uses `sh` (>= 16
-// ints of shared memory).
+// Returns the exclusive prefix; *total receives the sum.  Uses `sh` (>= 17
+// long longs of shared memory).
 __device__ inline long long block_exclusive_scan(long long x, long long* sh, long long* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     long long inc = x;
@@ -131,53 +151,50 @@ __device__ inline long long block_exclusive_scan(long long x, long long* sh, lon
     return res;
 }
 
-// Single workgroup: position ids, CSR pointers and entries, heaviest-first
-// orders.
-__global__ __launch_bounds__(1024) void meta_finish(const int32_t* __restrict__ se,
-                                                    const int32_t* __restrict__ hist,
-                                                    int32_t* __restrict__ pos, const uint8_t* __restrict__ tc,
-                                                    const int32_t* __restrict__ row_cnt,
-                                                    int32_t* __restrict__ row_ptr, int32_t* __restrict__ row_ent,
-                                                    const int32_t* __restrict__ col_cnt,
-                                                    int32_t* __restrict__ col_ptr, int32_t* __restrict__ col_ent,
-                                                    int32_t* __restrict__ q_order, int32_t* __restrict__ k_order,
-                                                    int L, int nb) {
+// Single workgroup over per-block values: column counts (closed form),
+// exclusive prefixes of (real tokens, histogram mass) per block and of
+// (row, column) counts (the CSR pointers), and the heaviest-first orders.
+__global__ __launch_bounds__(1024) void meta_scan(const int32_t* __restrict__ blk_max,
+                                                  int32_t* __restrict__ blk_cnt, int32_t* __restrict__ blk_hsum,
+                                                  const int32_t* __restrict__ row_cnt, int32_t* __restrict__ col_cnt,
+                                                  int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_ptr,
+                                                  int32_t* __restrict__ q_order, int32_t* __restrict__ k_order,
+                                                  int nb) {
     __shared__ long long sh[32];
     const int t = threadIdx.x, nt = blockDim.x;
+    const int chunk = (nb + nt - 1) / nt;
+    const int a = min(nb, t * chunk), e = min(nb, a + chunk);
+    for (int i = a; i < e; ++i) {
+        const int hi = blk_max[i];
+        col_cnt[i] = hi >= 0 ? min(nb - 1, hi / kBlock) - i + 1 : 0;
+    }
     long long total;
-
-    // 1) position ids
     {
-        const int chunk = (L + nt - 1) / nt;
-        const int a = min(L, t * chunk), b = min(L, a + chunk);
-        long long lt = 0, re = 0;
-        for (int i = a; i < b; ++i) {
-            lt += hist[i];
-            re += se[i] >= 0 && se[i] < L;
+        long long r = 0, h = 0;
+        for (int i = a; i < e; ++i) {
+            r += blk_cnt[i];
+            h += blk_hsum[i];
         }
-        // pack the two counts (each < 2^21) into one scan value
-        const long long base = block_exclusive_scan((lt << 32) | re, sh, &total);
-        long long run_lt = base >> 32, run_re = base & 0xffffffffll;
-        for (int i = a; i < b; ++i) {
-            const bool real = se[i] >= 0 && se[i] < L;
-            run_re += real;
-            pos[i] = real ? int32_t(run_re - run_lt - 1) : 0;
-            run_lt += hist[i];
+        // pack the two counts (each <= 2^20) into one scan value
+        const long long base = block_exclusive_scan((h << 32) | r, sh, &total);
+        long long rr = base & 0xffffffffll, hh = base >> 32;
+        for (int i = a; i < e; ++i) {
+            const int ci = blk_cnt[i], hi = blk_hsum[i];
+            blk_cnt[i] = int32_t(rr);
+            blk_hsum[i] = int32_t(hh);
+            rr += ci;
+            hh += hi;
         }
     }
-
-    // 2) CSR offsets
     {
-        const int chunk = (nb + nt - 1) / nt;
-        const int a = min(nb, t * chunk), b = min(nb, a + chunk);
         long long r = 0, c = 0;
-        for (int i = a; i < b; ++i) {
+        for (int i = a; i < e; ++i) {
             r += row_cnt[i];
             c += col_cnt[i];
         }
         const long long base = block_exclusive_scan((r << 32) | c, sh, &total);
         long long rr = base >> 32, cc = base & 0xffffffffll;
-        for (int i = a; i < b; ++i) {
+        for (int i = a; i < e; ++i) {
             row_ptr[i] = int32_t(rr);
             col_ptr[i] = int32_t(cc);
             rr += row_cnt[i];
@@ -188,51 +205,122 @@ __global__ __launch_bounds__(1024) void meta_finish(const int32_t* __restrict__ 
             col_ptr[nb] = int32_t(total & 0xffffffffll);
         }
     }
+
+    // heaviest-first orders, ties by index: the keys
+    // ((nb - count) << 13) | index are unique, so sorting them ascending
+    // with a bitonic network in LDS gives exactly that order in
+    // O(nb log^2 nb) work (nb <= 8192 = 2^13 blocks)
+    constexpr int kMaxNb = int(kMaxL / kBlock);
+    static_assert(kMaxNb <= (1 << 13), "block index must fit 13 bits");
+    __shared__ unsigned kq[kMaxNb], kk[kMaxNb];
+    int n = 1;
+    while (n < nb) n <<= 1;
+    __syncthreads();  // col_cnt written by other threads above
+    for (int i = t; i < n; i += nt) {
+        kq[i] = i < nb ? (unsigned(nb - row_cnt[i]) << 13) | unsigned(i) : 0xffffffffu;
+        kk[i] = i < nb ? (unsigned(nb - col_cnt[i]) << 13) | unsigned(i) : 0xffffffffu;
+    }
     __syncthreads();
-
-    // 3) entries, ascending: one wave per row (column), 64 tiles per ballot,
-    //    each nonempty tile written at its rank among the nonempty ones
-    const int lane = t & 63, wv = t >> 6, nw = nt >> 6;
-    const unsigned long long below = (1ull << lane) - 1;
-    for (int qb = wv; qb < nb; qb += nw) {
-        int k = row_ptr[qb];
-        const uint8_t* row = tc + int64_t(qb) * nb;
-        for (int k0 = 0; k0 <= qb; k0 += 64) {
-            const int kb = k0 + lane;
-            const int c = kb <= qb ? row[kb] : 0;
-            const unsigned long long m = __ballot(c != 0);
-            if (c) row_ent[k + __popcll(m & below)] = (kb << 1) | (c == 1);
-            k += __popcll(m);
+    for (int k = 2; k <= n; k <<= 1)
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = t; i < n; i += nt) {
+                const int p = i ^ j;
+                if (p > i) {
+                    const bool up = (i & k) == 0;
+                    unsigned x = kq[i], y = kq[p];
+                    if ((x > y) == up) {
+                        kq[i] = y;
+                        kq[p] = x;
+                    }
+                    x = kk[i];
+                    y = kk[p];
+                    if ((x > y) == up) {
+                        kk[i] = y;
+                        kk[p] = x;
+                    }
+                }
+            }
+            __syncthreads();
         }
-    }
-    for (int kb = wv; kb < nb; kb += nw) {
-        int k = col_ptr[kb];
-        for (int q0 = kb; q0 < nb; q0 += 64) {
-            const int qb = q0 + lane;
-            const int c = qb < nb ? tc[int64_t(qb) * nb + kb] : 0;
-            const unsigned long long m = __ballot(c != 0);
-            if (c) col_ent[k + __popcll(m & below)] = (qb << 1) | (c == 1);
-            k += __popcll(m);
-        }
-    }
-
-    // 4) heaviest-first orders (stable on index), counts staged in LDS
-    __shared__ int rc_s[kMaxL / kBlock], cc_s[kMaxL / kBlock];
     for (int i = t; i < nb; i += nt) {
-        rc_s[i] = row_cnt[i];
-        cc_s[i] = col_cnt[i];
+        q_order[i] = int(kq[i] & 0x1fffu);
+        k_order[i] = int(kk[i] & 0x1fffu);
     }
-    __syncthreads();
-    for (int x = t; x < nb; x += nt) {
-        const int rc = rc_s[x], cc = cc_s[x];
-        int rq = 0, rk = 0;
-        for (int y = 0; y < nb; ++y) {
-            const int ry = rc_s[y], cy = cc_s[y];
-            rq += (ry > rc) || (ry == rc && y < x);
-            rk += (cy > cc) || (cy == cc && y < x);
+}
+
+// One workgroup (256 threads) per block b: the position ids of its tokens,
+// row b's tile list (ascending key blocks) and column b's (closed form).
+__global__ __launch_bounds__(256) void meta_lists(const int32_t* __restrict__ se, const int32_t* __restrict__ hist,
+                                                  const int32_t* __restrict__ blk_min,
+                                                  const int32_t* __restrict__ blk_max,
+                                                  const int32_t* __restrict__ blk_roff,
+                                                  const int32_t* __restrict__ blk_hoff,
+                                                  const int32_t* __restrict__ row_ptr,
+                                                  const int32_t* __restrict__ col_ptr, int32_t* __restrict__ pos,
+                                                  int32_t* __restrict__ row_ent, int32_t* __restrict__ col_ent,
+                                                  int L, int nb) {
+    const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const unsigned long long below = (1ull << lane) - 1;
+    __shared__ int sh[8];
+
+    // 1) position ids: pos = (#real up to i, inclusive) - (histogram mass
+    //    below i) - 1, from the block's exclusive prefixes plus a scan
+    //    within the block (waves 0 and 1 hold its 128 tokens)
+    if (t < kBlock) {
+        const int i = b * kBlock + t;
+        const int s = se[i];
+        const int real = s >= 0 && s < L;
+        const int hv = hist[i];
+        int r = real, hx = hv;  // inclusive wave scans
+        for (int off = 1; off < 64; off <<= 1) {
+            const int ry = __shfl_up(r, off), hy = __shfl_up(hx, off);
+            if (lane >= off) {
+                r += ry;
+                hx += hy;
+            }
         }
-        q_order[rq] = x;
-        k_order[rk] = x;
+        if (lane == 63) {
+            sh[2 * wave] = r;
+            sh[2 * wave + 1] = hx;
+        }
+        __syncthreads();
+        const int r_in = r + (wave ? sh[0] : 0);
+        const int h_ex = hx - hv + (wave ? sh[1] : 0);
+        pos[i] = real ? blk_roff[b] + r_in - (blk_hoff[b] + h_ex) - 1 : 0;
+    } else {
+        __syncthreads();
+    }
+
+    // 2) row b: nonempty key blocks kb <= b in ascending order, 256 per pass
+    {
+        int k = row_ptr[b];
+        for (int k0 = 0; k0 <= b; k0 += 256) {
+            const int kb = k0 + t;
+            const int c = kb <= b && kb < nb ? tile_class_of(b, kb, blk_min[kb], blk_max[kb]) : 0;
+            const unsigned long long m = __ballot(c != 0);
+            __syncthreads();  // sh reuse
+            if (lane == 0) sh[wave] = __popcll(m);
+            __syncthreads();
+            int before = 0, tot = 0;
+            for (int w = 0; w < 4; ++w) {
+                before += w < wave ? sh[w] : 0;
+                tot += sh[w];
+            }
+            if (c) row_ent[k + before + __popcll(m & below)] = (kb << 1) | (c == 1);
+            k += tot;
+        }
+    }
+
+    // 3) column b: query blocks b .. hi / 128
+    {
+        const int lo = blk_min[b], hi = blk_max[b];
+        if (hi >= 0) {
+            const int qmax = min(nb - 1, hi / kBlock), base = col_ptr[b];
+            for (int qb = b + t; qb <= qmax; qb += 256) {
+                const int c = tile_class_of(qb, b, lo, hi);
+                col_ent[base + qb - b] = (qb << 1) | (c == 1);
+            }
+        }
     }
 }
 
@@ -243,13 +331,15 @@ hipError_t launch_meta(const int32_t* se, int64_t L, int32_t* pos, uint8_t* tile
     const MetaLayout m = meta_layout(L);
     int32_t* w = static_cast<int32_t*>(ws);
     const int nb = int(m.nb);
-    meta_init<<<64, 256, 0, stream>>>(w + m.hist, L + 1, w + m.col_cnt, nb, w + m.hdr, L);
-    meta_blocks<<<nb, kBlock, 0, stream>>>(se, w + m.hist, w + m.blk_min, w + m.blk_max, w + m.hdr, int(L));
-    meta_tiles<<<nb, 256, 0, stream>>>(w + m.blk_min, w + m.blk_max, tile_class, w + m.row_cnt,
-                                      w + m.col_cnt, nb);
-    meta_finish<<<1, 1024, 0, stream>>>(se, w + m.hist, pos, tile_class, w + m.row_cnt, w + m.row_ptr,
-                                       w + m.row_ent, w + m.col_cnt, w + m.col_ptr, w + m.col_ent,
-                                       w + m.q_order, w + m.k_order, int(L), nb);
+    meta_init<<<64, 256, 0, stream>>>(w + m.hist, L + 1, w + m.hdr, L, nb);
+    meta_blocks<<<nb, kBlock, 0, stream>>>(se, w + m.hist, w + m.blk_min, w + m.blk_max, w + m.blk_cnt, w + m.hdr,
+                                          int(L));
+    meta_tiles<<<nb, 256, 0, stream>>>(w + m.blk_min, w + m.blk_max, w + m.hist, tile_class, w + m.row_cnt,
+                                      w + m.blk_hsum, nb);
+    meta_scan<<<1, 1024, 0, stream>>>(w + m.blk_max, w + m.blk_cnt, w + m.blk_hsum, w + m.row_cnt, w + m.col_cnt,
+                                     w + m.row_ptr, w + m.col_ptr, w + m.q_order, w + m.k_order, nb);
+    meta_lists<<<nb, 256, 0, stream>>>(se, w + m.hist, w + m.blk_min, w + m.blk_max, w + m.blk_cnt, w + m.blk_hsum,
+                                      w + m.row_ptr, w + m.col_ptr, pos, w + m.row_ent, w + m.col_ent, int(L), nb);
     return hipGetLastError();
 }
 

@@ -372,6 +372,28 @@ int tree_pack_stats(const tree_pack_t* p, tree_pack_stats_t* s) {
     return TREE_OK;
 }
 
+int tree_pack_concat(const tree_pack_t* p, int32_t* out_se, int64_t cap, int64_t* L_total) {
+    if (!p || !L_total) return treeattn::set_error(TREE_E_ARG, "tree_pack_concat: NULL argument");
+    int64_t total = 0;
+    for (const PackedTrie& x : p->tries) total += x.L;
+    *L_total = total;
+    if (out_se) {
+        if (cap < total)
+            return treeattn::set_error(TREE_E_ARG, "tree_pack_concat: capacity %lld < %lld", (long long)cap,
+                                       (long long)total);
+        int64_t off = 0;
+        for (const PackedTrie& x : p->tries) {
+            for (int64_t i = 0; i < x.L; ++i) {
+                const int32_t s = x.subtree_end[size_t(i)];
+                out_se[off + i] = s < 0 ? -1 : int32_t(s + off);
+            }
+            off += x.L;
+        }
+    }
+    treeattn::clear_error();
+    return TREE_OK;
+}
+
 void tree_pack_free(tree_pack_t* p) { delete p; }
 
 }  // extern "C"

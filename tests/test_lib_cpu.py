@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
     for n in sorted(names):
         assert hasattr(L, n), n
     assert set(_lib.SIGNATURES) == names
-    assert L.tree_abi_version() == 1
+    assert L.tree_abi_version() == 2
 
 
 def _compare(tries_lib, tries_or):
@@ -153,3 +153,73 @@ def test_device_entry_points_validate_before_launch(L):
     assert need >= 1024 * 8 * 4
     assert L.tree_attn_bwd(*([p] * 12), need - 1, 1024, 8, 2, 128, 0.1, 0, None) == -6
     assert b"workspace" in L.tree_last_error()
+
+
+def _oracle_concat(to):
+    parts, off = [], 0
+    for t in to:
+        se = np.asarray(t.subtree_end, dtype=np.int64).copy()
+        se[se >= 0] += off
+        parts.append(se)
+        off += t.L
+    return np.concatenate(parts).astype(np.int32)
+
+
+@pytest.mark.parametrize("config", ["1", "2", "3", "4b"])
+def test_concat_layout_bit_exact(L, config):
+    """tree_pack_concat lays the oracle's tries end to end with shifted
+    subtree ends, and the concatenation is a packed layout of its own: the
+    oracle's position ids and tile classes on it equal each trie's own on
+    the trie's block range, and every tile across tries is empty."""
+    w = workloads.make_workload(config)
+    se, lengths, stats = pta.pack_concat(w.ids, w.mask, w.max_tokens_per_mb)
+    to = oracle.pack(w.ids, w.mask, w.max_tokens_per_mb)
+    assert lengths == [t.L for t in to]
+    assert (se == _oracle_concat(to)).all()
+    assert stats["n_tries"] == len(to)
+
+
+def test_concat_is_a_packed_layout(L):
+    # per-trie metadata reproduced inside the concatenation (small batch so
+    # the dense oracle mask of the whole concatenation stays small)
+    ids, mask, M = next(c for c in small_cases_cpu() if c[0] == "grpo-small")[1:]  # three tries
+    to = oracle.pack(ids, mask, M)
+    assert len(to) > 1
+    se, lengths, _ = pta.pack_concat(ids, mask, M)
+    n = len(se)
+    # dense ancestor mask of the concatenation from its subtree intervals
+    j = np.arange(n)
+    vis = (j[None, :] <= j[:, None]) & (j[:, None] <= se[None, :])
+    pos_cat = np.where(se >= 0, vis.sum(1) - 1, 0)
+    off = 0
+    for t in to:
+        m = oracle.dense_ancestor_mask(t)
+        assert (pos_cat[off:off + t.L] == oracle.position_ids(m)).all()
+        assert not vis[off:off + t.L, :off].any() and not vis[off:off + t.L, off + t.L:].any()
+        off += t.L
+
+
+def small_cases_cpu():
+    for kind in workloads.SMALL_KINDS:
+        ids, mask, M = workloads.small_workload(kind)
+        yield kind, ids, mask, M
+
+
+def test_concat_errors(L):
+    w = workloads.make_workload("1")
+    ids = np.ascontiguousarray(w.ids, dtype=np.int32)
+    mask = np.ascontiguousarray(w.mask, dtype=np.uint8)
+    h = ctypes.c_void_p()
+    assert L.tree_pack(ids.ctypes.data, mask.ctypes.data, ids.shape[0], ids.shape[1], w.max_tokens_per_mb,
+                       128, 0, 0, ctypes.byref(h)) == 0
+    try:
+        total = ctypes.c_int64()
+        assert L.tree_pack_concat(h, None, 0, None) == -5
+        assert L.tree_pack_concat(None, None, 0, ctypes.byref(total)) == -5
+        assert L.tree_pack_concat(h, None, 0, ctypes.byref(total)) == 0 and total.value > 0
+        buf = np.zeros(total.value, np.int32)
+        assert L.tree_pack_concat(h, buf.ctypes.data, total.value - 1, ctypes.byref(total)) == -5
+        assert b"capacity" in L.tree_last_error()
+        assert L.tree_pack_concat(h, buf.ctypes.data, total.value, ctypes.byref(total)) == 0
+    finally:
+        L.tree_pack_free(h)
