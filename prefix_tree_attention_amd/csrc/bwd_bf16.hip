@@ -48,25 +48,35 @@ constexpr float kLog2e = 1.4426950408889634f;
 // the dP accumulators), and LSE in base 2 (LSE log2 e) for the dK/dV
 // kernel's exponent
 // ---------------------------------------------------------------------------
+// One 16-byte chunk per lane, D / 8 lanes per (token, head) row, so each
+// row is one contiguous 2D-byte read; rows run head-major (grid y = head,
+// tokens along x), so the LSE and output rows [Hq, L] are contiguous too.
 template <int D>
 __global__ __launch_bounds__(256) void delta_bf16_kernel(const bf16* __restrict__ O, const bf16* __restrict__ dO,
                                                          const float* __restrict__ LSE, float* __restrict__ delta,
                                                          float* __restrict__ lse2, int L, int Hq) {
-    const int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (r >= int64_t(L) * Hq) return;
-    const int64_t hr = int64_t(r % Hq) * L + r / Hq;
-    lse2[hr] = LSE[hr] * kLog2e;
+    constexpr int kLanes = D / 8;         // lanes per row
+    constexpr int kRows = 256 / kLanes;   // rows per workgroup
+    const int h = blockIdx.y;
+    const int i = blockIdx.x * kRows + threadIdx.x / kLanes;
+    const int c = threadIdx.x % kLanes;
     float acc = 0.f;
-#pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
-        const u32x4 a = ld16(O + r * D + 8 * c), b = ld16(dO + r * D + 8 * c);
+    if (i < L) {
+        const int64_t off = (int64_t(i) * Hq + h) * D + 8 * c;
+        const u32x4 a = ld16(O + off), b = ld16(dO + off);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             acc += bf16_to_float(a[w] & 0xffffu) * bf16_to_float(b[w] & 0xffffu);
             acc += bf16_to_float(a[w] >> 16) * bf16_to_float(b[w] >> 16);
         }
     }
-    delta[hr] = -acc;
+#pragma unroll
+    for (int o = kLanes / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+    if (c == 0 && i < L) {
+        const int64_t hr = int64_t(h) * L + i;
+        lse2[hr] = LSE[hr] * kLog2e;
+        delta[hr] = -acc;
+    }
 }
 
 // Place a value in accumulation registers (empty asm with an AGPR operand).
@@ -317,7 +327,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_bf16_kernel(
     float scale_log2, float scale) {
     using T = Tile<D>;
     constexpr int NS = D / 32, NT = D / 16;
-    __shared__ __attribute__((aligned(1024))) char smem_raw[4 * T::kBytes];
+    // K and V tiles and the keys' subtree ends, double-buffered
+    __shared__ __attribute__((aligned(1024))) char smem_raw[4 * T::kBytes + 2 * 4 * kStep];
     lds_char* const smem = (lds_char*)smem_raw;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -353,11 +364,18 @@ __global__ __launch_bounds__(kThreads, 2) void dq_bf16_kernel(
     const int kvs = int(kv_stride);
     auto ktile = [&](int buf) { return smem + (2 * buf) * T::kBytes; };
     auto vtile = [&](int buf) { return smem + (2 * buf + 1) * T::kBytes; };
+    auto serow = [&](int buf) { return smem + 4 * T::kBytes + buf * 4 * kStep; };
     auto issue = [&](int st, int buf) {
         const int kbase = (row_ent[beg + (st >> 1)] >> 1) * kBlock + kStep * (st & 1);
         const int64_t off = int64_t(kbase) * kv_stride + int64_t(hkv) * D;
         T::load_async(ktile(buf), K + off, kvs, wave, lane);
         T::load_async(vtile(buf), V + off, kvs, wave, lane);
+        // the keys' subtree ends ride with the tiles (wave w stages 16 of
+        // them), so the partial-tile mask reads LDS instead of issuing
+        // global loads whose wait would also drain the prefetch
+        if (lane < 16)
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(se + kbase + 16 * wave + lane),
+                                             reinterpret_cast<lds_void*>(serow(buf) + 64 * wave), 4, 0, 0);
     };
     if (nsteps > 0) issue(0, 0);
     wait_vm_all();
@@ -404,7 +422,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_bf16_kernel(
                 if constexpr (decltype(masked)::value) {
 #pragma unroll
                     for (int e = 0; e < 2; ++e)
-                        sek[e] = *reinterpret_cast<const i32x4*>(se + kbase + 32 * c + 16 * e + 4 * g);
+                        sek[e] = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(
+                            serow(buf) + 4 * (32 * c + 16 * e + 4 * g));
                 }
 #pragma unroll
                 for (int qs = 0; qs < 2; ++qs) {
@@ -460,7 +479,8 @@ hipError_t launch_bwd_d(int phase, const bf16* Q, const bf16* K, const bf16* V, 
     const float sl2 = sh.scale * kLog2e;
     float* lse2 = delta + rows;  // second half of the workspace
     if (phase == kPhaseAll || phase == kPhaseDelta)
-        delta_bf16_kernel<D><<<unsigned((rows + 255) / 256), 256, 0, stream>>>(O, dO, lse, delta, lse2, L, sh.Hq);
+        delta_bf16_kernel<D><<<dim3(unsigned((L + 256 / (D / 8) - 1) / (256 / (D / 8))), unsigned(sh.Hq)), 256, 0,
+                               stream>>>(O, dO, lse, delta, lse2, L, sh.Hq);
     if (phase == kPhaseAll || phase == kPhaseDkdv)
         dkdv_bf16_kernel<D><<<unsigned(sh.nb) * unsigned(sh.Hkv), kThreads, 0, stream>>>(
             Q, K, V, dO, lse2, delta, dK, dV, se, mp.k_order, mp.col_ptr, mp.col_ent, L, sh.Hq, sh.Hkv, sl2,

@@ -46,7 +46,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     using T = Tile<D>;
     constexpr int NX = D / 16;  // k-steps of S^T = K Q^T
     constexpr int NT = D / 32;  // 32-row d-blocks of O^T
-    __shared__ __attribute__((aligned(1024))) char smem_raw[4 * T::kBytes];
+    // K and V tiles and the keys' subtree ends, double-buffered
+    __shared__ __attribute__((aligned(1024))) char smem_raw[4 * T::kBytes + 2 * 4 * kStep];
     lds_char* const smem = (lds_char*)smem_raw;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -91,11 +92,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const int kvs = int(kv_stride);
     auto ktile = [&](int buf) { return smem + (2 * buf) * T::kBytes; };
     auto vtile = [&](int buf) { return smem + (2 * buf + 1) * T::kBytes; };
+    auto serow = [&](int buf) { return smem + 4 * T::kBytes + buf * 4 * kStep; };
     auto issue = [&](int st, int buf) {
         const int kbase = (row_ent[beg + (st >> 1)] >> 1) * kBlock + kStep * (st & 1);
         const int64_t off = int64_t(kbase) * kv_stride + int64_t(hkv) * D;
         T::load_async(ktile(buf), K + off, kvs, wave, lane);
         T::load_async(vtile(buf), V + off, kvs, wave, lane);
+        // the keys' subtree ends ride with the tiles (wave w stages 16 of
+        // them), so the partial-tile mask reads LDS instead of issuing
+        // global loads whose wait would also drain the prefetch
+        if (lane < 16)
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(se + kbase + 16 * wave + lane),
+                                             reinterpret_cast<lds_void*>(serow(buf) + 64 * wave), 4, 0, 0);
     };
     if (nsteps > 0) issue(0, 0);
     wait_vm_all();
@@ -130,7 +138,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
                 const int k0 = kbase + 32 * kk + 4 * h, lim = qi - k0;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const i32x4 sek = *reinterpret_cast<const i32x4*>(se + k0 + 8 * j);
+                    const i32x4 sek = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(
+                        serow(buf) + 4 * (32 * kk + 8 * j + 4 * h));
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         if (!(8 * j + i <= lim && qi <= sek[i])) sc[kk][4 * j + i] = -INFINITY;
