@@ -181,8 +181,8 @@ int tree_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
                   int32_t Hkv, int32_t D, float scale, int32_t dtype, void* stream);
 
 /* Bytes of device workspace tree_attn_bwd needs: two float rows per query
- * head and token (Delta_i and LSE_i log2 e), 2 * L * Hq * 4 rounded up to
- * 256.  Returns 0 for L <= 0 or Hq <= 0. */
+ * head and token (Delta_i and, for bf16, LSE_i / scale), 2 * L * Hq * 4
+ * rounded up to 256.  Returns 0 for L <= 0 or Hq <= 0. */
 size_t tree_attn_bwd_workspace_bytes(int64_t L, int32_t Hq, int32_t D, int32_t dtype);
 
 /* Backward of tree_attn_fwd (AREAL-DTA notes, §3 问题形式化: a shared
@@ -200,7 +200,7 @@ int tree_attn_bwd(const void* q, const void* k, const void* v, const void* o,
 
 /* One phase of tree_attn_bwd, for callers that time or schedule the
  * backward's kernels separately: TREE_BWD_DELTA computes Delta_i =
- * dO_i . O_i (and, for bf16, LSE_i log2 e) into d_ws, in an internal
+ * dO_i . O_i (and, for bf16, LSE_i / scale) into d_ws, in an internal
  * layout; TREE_BWD_DKDV writes dk and dv;
  * TREE_BWD_DQ writes dq; TREE_BWD_ALL runs all three in that order (same
  * as tree_attn_bwd).  DKDV and DQ read what a DELTA phase left in the same

@@ -11,16 +11,19 @@
 //
 // Three kernels:
 //   delta: Delta for every (token, query head).
-//   dkdv:  one workgroup per (128-key block, key/value head); wave w owns
-//          keys 32w..32w+31 and keeps K^T, V^T operands and the dK^T, dV^T
-//          accumulators in registers.  It walks the nonempty tiles of its
-//          key block (column list) for each query head of the group, 64
-//          queries per step; Q and dO (and LSE, Delta) of a step go HBM ->
-//          LDS by direct loads into double-buffered swizzled tiles.
+//   dkdv:  one workgroup per (pair of 128-key blocks, key/value head);
+//          wave w owns 64 keys and keeps their V^T operands in vector
+//          registers and their dK^T, dV^T accumulators in the 256
+//          accumulation registers; K rows of the 256 keys sit in LDS.  It
+//          walks the query blocks of the pair's columns (a contiguous
+//          range) for each query head of the group, 64 queries per step;
+//          Q and dO (and -LSE / scale, -Delta) of a step go HBM -> LDS by
+//          direct loads into double-buffered swizzled tiles.
 //            S = Q K^T, dP = dO V^T      (A = Q / dO rows of the tiles)
 //            dV^T += dO^T P, dK^T += Q^T dS
 //          (A = dO^T / Q^T by transposing LDS reads of the same tiles,
-//          B = P / dS straight from the score accumulators).
+//          B = P / dS straight from the score accumulators).  Each Q / dO
+//          operand read feeds two 32-key MFMAs.
 //   dq:    one workgroup per (128-query block, query head) like the forward:
 //            S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T,
 //          K^T again by transposing reads of the K tile.
@@ -44,9 +47,9 @@ constexpr int kStep = kTileRows;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
-// -Delta = -rowsum(dO * O) (stored negated: it is the initial value of
-// the dP accumulators), and LSE in base 2 (LSE log2 e) for the dK/dV
-// kernel's exponent
+// -Delta = -rowsum(dO * O) and -LSE / scale: the initial values of the
+// dK/dV kernel's dP and S accumulators, which then leave dP - Delta and
+// S - LSE / scale (so P = exp2(scale log2 e * acc))
 // ---------------------------------------------------------------------------
 // One 16-byte chunk per lane, D / 8 lanes per (token, head) row, so each
 // row is one contiguous 2D-byte read; rows run head-major (grid y = head,
@@ -54,7 +57,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 template <int D>
 __global__ __launch_bounds__(256) void delta_bf16_kernel(const bf16* __restrict__ O, const bf16* __restrict__ dO,
                                                          const float* __restrict__ LSE, float* __restrict__ delta,
-                                                         float* __restrict__ lse2, int L, int Hq) {
+                                                         float* __restrict__ nls, float inv_scale, int L, int Hq) {
     constexpr int kLanes = D / 8;         // lanes per row
     constexpr int kRows = 256 / kLanes;   // rows per workgroup
     const int h = blockIdx.y;
@@ -74,16 +77,9 @@ __global__ __launch_bounds__(256) void delta_bf16_kernel(const bf16* __restrict_
     for (int o = kLanes / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
     if (c == 0 && i < L) {
         const int64_t hr = int64_t(h) * L + i;
-        lse2[hr] = LSE[hr] * kLog2e;
+        nls[hr] = -LSE[hr] * inv_scale;
         delta[hr] = -acc;
     }
-}
-
-// Place a value in accumulation registers (empty asm with an AGPR operand).
-__device__ __forceinline__ void pin_agpr(bf16x8& x) {
-    i32x4 v = __builtin_bit_cast(i32x4, x);
-    asm volatile("" : "+a"(v));
-    x = __builtin_bit_cast(bf16x8, v);
 }
 
 // direct load of 64 consecutive floats (one wave)
@@ -95,104 +91,166 @@ __device__ __forceinline__ void load_row64_async(lds_char* dst, const float* __r
 // ---------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------
+// dK^T / dV^T accumulation, D = A * B + D, with the accumulator held in
+// accumulation registers (AGPRs): the 256 of them hold the 64 keys x D of
+// dK and dV of one wave, which leaves the vector registers to the scores.
+// The compiler's hazard recognizer does not look inside inline asm, so the
+// callers keep the required distances themselves: two wait states between
+// a VALU write of A or B and this read (the bf16 conversions are fenced by
+// an s_nop 1), and nops before the accumulators are first read or written
+// by anything else.  Consecutive updates of one accumulator by MFMAs of
+// this same shape need no wait states.
+__device__ __forceinline__ void mfma32_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                 : "+a"(acc)
+                 : "v"(__builtin_bit_cast(i32x4, a)), "v"(__builtin_bit_cast(i32x4, b)));
+}
+
+// one workgroup per (pair of 128-key blocks, key/value head); wave w owns
+// 64 keys
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Delta,
+    const bf16* __restrict__ dO, const float* __restrict__ NLS, const float* __restrict__ Delta,
     bf16* __restrict__ dK, bf16* __restrict__ dV, const int32_t* __restrict__ se,
-    const int32_t* __restrict__ k_order, const int32_t* __restrict__ col_ptr,
-    const int32_t* __restrict__ col_ent, int L, int Hq, int Hkv, float scale_log2, float scale) {
+    const int32_t* __restrict__ p_order, const int32_t* __restrict__ blk_min,
+    const int32_t* __restrict__ blk_max, int L, int Hq, int Hkv, float scale_log2, float scale) {
     using T = Tile<D>;
     constexpr int NX = D / 16;  // k-steps of S = Q K^T and dP = dO V^T
     constexpr int NT = D / 32;  // 32-row d-blocks of dK^T and dV^T
-    constexpr int kStage = 2 * T::kBytes + 512;  // Q tile, dO tile, LSE log2 e [64], Delta[64]
-    __shared__ __attribute__((aligned(1024))) char smem_raw[2 * kStage];
-    lds_char* const smem = (lds_char*)smem_raw;
+    constexpr int kStage = 2 * T::kBytes + 512;  // Q tile, dO tile, -LSE / scale [64], -Delta [64]
+    constexpr int kKBytes = 4 * T::kBytes;       // K rows of the 256 keys
+    __shared__ __attribute__((aligned(1024))) char smem_raw[kKBytes + 2 * kStage];
+    lds_char* const ktile = (lds_char*)smem_raw;
+    lds_char* const smem = ktile + kKBytes;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // 32x32x16 fragments: lane = MFMA column j32 (this lane's key) and k-half h
+    // 32x32x16 fragments: lane = MFMA column j32 (this lane's key within a
+    // 32-key block) and k-half h
     const int j32 = lane & 31, h = lane >> 5;
     // transposing reads: 16-lane group gi takes 16 d values starting at
     // 16 (gi % 2) and query rows 4 h + 0..3 of a k-step
     const int tr_e = 16 * ((lane >> 4) & 1), tr_i = lane & 15;
-    // work item: key/value-head major, then key blocks heaviest first
-    const int nbk = int(gridDim.x) / Hkv;
+    // work item: key/value-head major, then key-block pairs heaviest first
+    const int npair = int(gridDim.x) / Hkv;
     const int work = xcd_logical_block();
-    const int hkv = work / nbk, rank = work % nbk;
-    const int kb = k_order[rank];
+    const int hkv = work / npair, rank = work % npair;
+    const int kp = p_order[rank];
+    const int nb = L / kBlock;
+    const int kb0 = 2 * kp, kb1 = 2 * kp + 1;
+    const bool has1 = kb1 < nb;
     const int G = Hq / Hkv;
     const int64_t q_stride = int64_t(Hq) * D, kv_stride = int64_t(Hkv) * D;
-    const int kw0 = kb * kBlock + 32 * wave;
-    const int key = kw0 + j32;
-    const int sek = se[key];
 
-    // K^T, V^T operands (B of S and dP): lane holds key kw0 + j32,
-    // d = 16 x + 8 h .. +7 for k-step x.  They live in the accumulation-
-    // register file: MFMA reads A/B operands from either file, and the
-    // vector registers are needed for the accumulators and the scores.
-    bf16x8 kf[NX], vf[NX];
+    // V^T operands (B of dP) in registers: lane holds key
+    // 256 kp + 64 wave + 32 kk + j32, d = 16 x + 8 h .. +7 for k-step x.
+    // K^T operands (B of S) are read from the K rows in LDS with the same
+    // offsets as the Q rows.  Keys past L (the second block of the last
+    // pair at an odd block count) read in-range rows instead; their
+    // gradients are never stored.
+    bf16x8 vf[2][NX];
+    int key[2], sek[2];
 #pragma unroll
-    for (int x = 0; x < NX; ++x) {
-        kf[x] = __builtin_bit_cast(bf16x8, ld16(K + int64_t(key) * kv_stride + hkv * D + 16 * x + 8 * h));
-        vf[x] = __builtin_bit_cast(bf16x8, ld16(V + int64_t(key) * kv_stride + hkv * D + 16 * x + 8 * h));
-        pin_agpr(kf[x]);
-        pin_agpr(vf[x]);
+    for (int kk = 0; kk < 2; ++kk) {
+        key[kk] = kb0 * kBlock + 64 * wave + 32 * kk + j32;
+        const bool ok = key[kk] < L;
+        sek[kk] = ok ? se[key[kk]] : -1;
+        const int64_t base = int64_t(ok ? key[kk] : L - 1) * kv_stride + hkv * D + 8 * h;
+#pragma unroll
+        for (int x = 0; x < NX; ++x) vf[kk][x] = __builtin_bit_cast(bf16x8, ld16(V + base + 16 * x));
     }
-    // Loop-invariant LDS byte offsets of this lane's operand reads (the
-    // swizzle XOR is per lane and per k-step, so it is resolved once here;
-    // the step only adds its buffer, tile and query-half bases).
-    int roff[NX];  // row-major read of k-step x: row j32, chunk 2 x + h
 #pragma unroll
-    for (int x = 0; x < NX; ++x) roff[x] = T::slot(j32, 2 * x + h);
-    int toff[NT][2];  // transposing read of d-block t, rows 4 h + 8 v + 0..3
+    for (int q4 = 0; q4 < 4; ++q4) {
+        const int r0 = kb0 * kBlock + (has1 ? 64 * q4 : 64 * (q4 & 1));
+        T::load_async(ktile + q4 * T::kBytes, K + int64_t(r0) * kv_stride + hkv * D, int(kv_stride), wave, lane);
+    }
+    // Operand read offsets.  Chunk 2 x + h of row j32 sits at position
+    // (2 x + h) ^ s = 2 (x ^ (s / 2)) + ((h ^ s) & 1), s = swz(j32), so the
+    // row-major read of k-step x is at (32 x ^ ru) + rbase; likewise the
+    // transposing read of d-block t (rows 4 h + 8 v + ..) is at
+    // (64 t ^ tx[v]) + tbase[v].  One v_xad_u32 per use instead of a
+    // register per offset.
+    int ru = 32 * (T::swz(j32) >> 1);
+    int rbase = T::slot(j32, h) - ru;
+    int tx[2], tbase[2];
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int v = 0; v < 2; ++v) {
+        tx[v] = 64 * (T::swz(4 * h + 8 * v + (tr_i >> 2)) >> 2);
+        tbase[v] = T::tr_offset(4 * h + 8 * v, tr_e, tr_i) - tx[v];
+    }
+    auto roff = [&](int x) { return ((32 * x) ^ ru) + rbase; };
+    auto toff = [&](int t, int v) { return ((64 * t) ^ tx[v]) + tbase[v]; };
+    // dK^T, dV^T accumulators of key block kk: d-block t, register r =
+    // d 32 t + 8 (r / 4) + 4 h + r % 4
+    f32x16 dk[2][NT], dv[2][NT];
 #pragma unroll
-        for (int v = 0; v < 2; ++v) toff[t][v] = T::tr_offset(4 * h + 8 * v, 32 * t + tr_e, tr_i);
-    // dK^T, dV^T accumulators: block t, register r = d 32 t + 8 (r / 4) + 4 h + r % 4
-    f32x16 dk[NT], dv[NT];
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dk[t][r] = dv[t][r] = 0.f;
+            for (int r = 0; r < 16; ++r) dk[kk][t][r] = dv[kk][t][r] = 0.f;
+    // nops that every accumulator depends on (see mfma32_agpr)
+#define TREEATTN_FENCE_ACC(NOPS)                                                                             \
+    do {                                                                                                     \
+        if constexpr (NT == 4)                                                                               \
+            asm volatile(NOPS                                                                                \
+                         : "+a"(dk[0][0]), "+a"(dk[0][1]), "+a"(dk[0][2]), "+a"(dk[0][3]), "+a"(dk[1][0]),  \
+                           "+a"(dk[1][1]), "+a"(dk[1][2]), "+a"(dk[1][3]), "+a"(dv[0][0]), "+a"(dv[0][1]),   \
+                           "+a"(dv[0][2]), "+a"(dv[0][3]), "+a"(dv[1][0]), "+a"(dv[1][1]), "+a"(dv[1][2]),   \
+                           "+a"(dv[1][3]));                                                                  \
+        else                                                                                                 \
+            asm volatile(NOPS                                                                                \
+                         : "+a"(dk[0][0]), "+a"(dk[0][1]), "+a"(dk[1][0]), "+a"(dk[1][1]), "+a"(dv[0][0]),  \
+                           "+a"(dv[0][1]), "+a"(dv[1][0]), "+a"(dv[1][1]));                                  \
+    } while (0)
+    static_assert(NT == 4 || NT == 2, "D is 128 or 64");
+    TREEATTN_FENCE_ACC("s_nop 1");  // zeroing writes -> first MFMA read
 
-    // the column is walked from its last query block down, so the key blocks
-    // in flight on an XCD read the same Q / dO tiles at about the same time
-    const int beg = col_ptr[kb], nsteps = (col_ptr[kb + 1] - beg) * 2 * G;
-    const int last = col_ptr[kb + 1] - 1;
+    // The pair's nonempty query blocks are the contiguous range from its
+    // first block with a real token to hi / 128 (each column is a range
+    // starting at its own block).  A 64-query step is full (no mask) when
+    // every key precedes every query and every query ends inside every
+    // key's subtree.
+    const int hi0 = blk_max[kb0], hi1 = has1 ? blk_max[kb1] : -1;
+    const int hi = max(hi0, hi1);
+    const int lo = has1 ? min(blk_min[kb0], blk_min[kb1]) : blk_min[kb0];
+    const int qhi = hi >= 0 ? min(nb - 1, hi / kBlock) : -1;
+    const int qlo = hi0 >= 0 ? kb0 : kb1;
+    const int nsteps = (qhi >= qlo ? qhi - qlo + 1 : 0) * 2 * G;
+    const int kmax = kb0 * kBlock + 2 * kBlock - 1;
     const int qs32 = int(q_stride);
     auto qtile = [&](int buf) { return smem + buf * kStage; };
     auto gtile = [&](int buf) { return smem + buf * kStage + T::kBytes; };
     auto lsev = [&](int buf) { return smem + buf * kStage + 2 * T::kBytes; };
     auto dlv = [&](int buf) { return smem + buf * kStage + 2 * T::kBytes + 256; };
     // Steps run over the query heads of the group fastest, then the two
-    // 64-query halves of a tile, then the tiles col_ent[last], col_ent[last-1],
-    // ...; the position is kept as counters (tile, half, head) so the loop
-    // carries no integer division.
+    // 64-query halves of a 128-query block, then the blocks from the last
+    // down, so the pairs in flight on an XCD read the same Q / dO tiles at
+    // about the same time.
     struct StepPos {
-        int tile, half, head;
+        int qbase, head, half;
     };
     auto advance = [&](StepPos& p) {
         if (++p.head == G) {
             p.head = 0;
             if (++p.half == 2) {
                 p.half = 0;
-                ++p.tile;
+                p.qbase -= 3 * kStep;
+            } else {
+                p.qbase += kStep;
             }
         }
     };
     auto issue = [&](const StepPos& p, int buf) {
-        const int ent = col_ent[last - p.tile];
-        const int qbase = (ent >> 1) * kBlock + kStep * p.half;
-        const int h = hkv * G + p.head;
-        const int64_t off = int64_t(qbase) * q_stride + int64_t(h) * D;
+        const int hq = hkv * G + p.head;
+        const int64_t off = int64_t(p.qbase) * q_stride + int64_t(hq) * D;
         T::load_async(qtile(buf), Q + off, qs32, wave, lane);
         T::load_async(gtile(buf), dO + off, qs32, wave, lane);
-        if (wave == 0) load_row64_async(lsev(buf), LSE2 + int64_t(h) * L + qbase, lane);
-        if (wave == 1) load_row64_async(dlv(buf), Delta + int64_t(h) * L + qbase, lane);
+        if (wave == 0) load_row64_async(lsev(buf), NLS + int64_t(hq) * L + p.qbase, lane);
+        if (wave == 1) load_row64_async(dlv(buf), Delta + int64_t(hq) * L + p.qbase, lane);
     };
-    StepPos cur{0, 0, 0}, nxt{0, 0, 0};
+    StepPos cur{qhi * kBlock, 0, 0}, nxt{qhi * kBlock, 0, 0};
     if (nsteps > 0) {
         issue(nxt, 0);
         advance(nxt);
@@ -202,9 +260,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
 
     for (int st = 0; st < nsteps; ++st) {
         const int buf = st & 1;
-        const int ent = col_ent[last - cur.tile];
-        const int qbase = (ent >> 1) * kBlock + kStep * cur.half;
-        const bool partial = ent & 1;
+        const int qbase = cur.qbase;
+        const bool partial = !(qbase >= kmax && qbase + kStep - 1 <= lo);
         advance(cur);
         if (st + 1 < nsteps) {
             issue(nxt, buf ^ 1);
@@ -217,54 +274,65 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
         auto lds_f32x4 = [](const lds_char* p) {
             return *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(p);
         };
+        // opaque per step, so the offsets are formed at each use rather than
+        // hoisted out of the loop into one register each
+        asm volatile("" : "+v"(ru), "+v"(rbase), "+v"(tx[0]), "+v"(tx[1]), "+v"(tbase[0]), "+v"(tbase[1]));
 
         // Two halves of 32 queries.  In half c, register r of a score
         // accumulator holds query 32 c + 8 (r / 4) + 4 h + r % 4 against
-        // this lane's key.
+        // key 32 kk + j32 of this wave.
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            // S = Q K^T; dP accumulates onto -Delta so it leaves dP - Delta
-            f32x16 sc, dp;
+            // S starts at -LSE / scale and dP at -Delta, so they leave
+            // S - LSE / scale and dP - Delta
+            f32x16 sc[2], dp[2];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
+                const f32x4 nls = lds_f32x4(lsp + 4 * (32 * c + 8 * j + 4 * h));
                 const f32x4 ndl = lds_f32x4(dlp + 4 * (32 * c + 8 * j + 4 * h));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    sc[4 * j + i] = 0.f;
-                    dp[4 * j + i] = ndl[i];
-                }
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        sc[kk][4 * j + i] = nls[i];
+                        dp[kk][4 * j + i] = ndl[i];
+                    }
             }
 #pragma unroll
             for (int x = 0; x < NX; ++x) {
-                const bf16x8 aq = T::frag_at(qt + 32 * c * T::kRowBytes, roff[x]);
-                const bf16x8 ag = T::frag_at(gt + 32 * c * T::kRowBytes, roff[x]);
-                sc = mfma32x32x16(aq, kf[x], sc);
-                dp = mfma32x32x16(ag, vf[x], dp);
-            }
-            // P = exp2(scale log2e S - LSE log2e), dS = P (dP - Delta); the
-            // subtree-interval predicate only in partial tiles (separate code
-            // path so full tiles carry no mask arithmetic)
-            f32x4 l2[4];
+                const int ro = roff(x);
+                const bf16x8 aq = T::frag_at(qt + 32 * c * T::kRowBytes, ro);
+                const bf16x8 ag = T::frag_at(gt + 32 * c * T::kRowBytes, ro);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) l2[j] = lds_f32x4(lsp + 4 * (32 * c + 8 * j + 4 * h));
-            auto elementwise = [&](auto masked) {
-                // register r is query q0 + o_r with o_r = 8 (r / 4) + r % 4;
-                // key <= q <= se[key]  <=>  key - q0 <= o_r <= se[key] - q0
-                int lo = 0, hi = 0;
-                if constexpr (decltype(masked)::value) {
-                    const int q0 = qbase + 32 * c + 4 * h;
-                    lo = key - q0;
-                    hi = sek - q0;
+                for (int kk = 0; kk < 2; ++kk) {
+                    const bf16x8 kf = T::frag_at(ktile + (64 * wave + 32 * kk) * T::kRowBytes, ro);
+                    sc[kk] = mfma32x32x16(aq, kf, sc[kk]);
+                    dp[kk] = mfma32x32x16(ag, vf[kk][x], dp[kk]);
                 }
+            }
+            // P = exp2(scale log2e (S - LSE / scale)), dS = P (dP - Delta);
+            // the subtree-interval predicate only in partial steps
+            auto elementwise = [&](auto masked) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float p = fast_exp2(__builtin_fmaf(sc[r], scale_log2, -l2[r / 4][r % 4]));
+                for (int kk = 0; kk < 2; ++kk) {
+                    // register r is query q0 + o_r with o_r = 8 (r / 4) + r % 4;
+                    // key <= q <= se[key]  <=>  key - q0 <= o_r <= se[key] - q0
+                    int lo_k = 0, hi_k = 0;
                     if constexpr (decltype(masked)::value) {
-                        const int o = 8 * (r / 4) + r % 4;
-                        p = (lo <= o && o <= hi) ? p : 0.f;
+                        const int q0 = qbase + 32 * c + 4 * h;
+                        lo_k = key[kk] - q0;
+                        hi_k = sek[kk] - q0;
                     }
-                    sc[r] = p;
-                    dp[r] = p * dp[r];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float p = fast_exp2(sc[kk][r] * scale_log2);
+                        if constexpr (decltype(masked)::value) {
+                            const int o = 8 * (r / 4) + r % 4;
+                            p = (lo_k <= o && o <= hi_k) ? p : 0.f;
+                        }
+                        sc[kk][r] = p;
+                        dp[kk][r] = p * dp[kk][r];
+                    }
                 }
             };
             if (partial)
@@ -273,14 +341,22 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
                 elementwise(std::false_type{});
             // B operands of the gradient products, k-step m = queries
             // 32 c + 16 m + {4 h + 0..3, 8 + 4 h + 0..3}
-            bf16x8 pb[2], db[2];
+            bf16x8 pb[2][2], db[2][2];
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                pb[m] = to_bf16x8(f32x4{sc[8 * m], sc[8 * m + 1], sc[8 * m + 2], sc[8 * m + 3]},
-                                  f32x4{sc[8 * m + 4], sc[8 * m + 5], sc[8 * m + 6], sc[8 * m + 7]});
-                db[m] = to_bf16x8(f32x4{dp[8 * m], dp[8 * m + 1], dp[8 * m + 2], dp[8 * m + 3]},
-                                  f32x4{dp[8 * m + 4], dp[8 * m + 5], dp[8 * m + 6], dp[8 * m + 7]});
-            }
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const f32x16& s = sc[kk];
+                    const f32x16& d = dp[kk];
+                    pb[kk][m] = to_bf16x8(f32x4{s[8 * m], s[8 * m + 1], s[8 * m + 2], s[8 * m + 3]},
+                                          f32x4{s[8 * m + 4], s[8 * m + 5], s[8 * m + 6], s[8 * m + 7]});
+                    db[kk][m] = to_bf16x8(f32x4{d[8 * m], d[8 * m + 1], d[8 * m + 2], d[8 * m + 3]},
+                                          f32x4{d[8 * m + 4], d[8 * m + 5], d[8 * m + 6], d[8 * m + 7]});
+                }
+            // the conversions above are VALU writes that the asm MFMAs read
+            asm volatile("s_nop 1"
+                         : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]), "+v"(db[0][0]),
+                           "+v"(db[0][1]), "+v"(db[1][0]), "+v"(db[1][1]));
             // dV^T += dO^T P, dK^T += Q^T dS: A = 32 d x 16 queries read
             // transposed from the row-major tiles, in the same k order
 #pragma unroll
@@ -290,29 +366,40 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
                     // rows 32 c + 16 m + 4 h + {0..3, 8..11}: the 16-row
                     // shift keeps the swizzle phase, so it is a plain offset
                     const int rb = (32 * c + 16 * m) * T::kRowBytes;
-                    const bf16x8 ag = join_tr(T::tr_at(gt + rb, toff[t][0]), T::tr_at(gt + rb, toff[t][1]));
-                    const bf16x8 aq = join_tr(T::tr_at(qt + rb, toff[t][0]), T::tr_at(qt + rb, toff[t][1]));
-                    dv[t] = mfma32x32x16(ag, pb[m], dv[t]);
-                    dk[t] = mfma32x32x16(aq, db[m], dk[t]);
+                    const int o0 = toff(t, 0), o1 = toff(t, 1);
+                    const bf16x8 ag = join_tr(T::tr_at(gt + rb, o0), T::tr_at(gt + rb, o1));
+                    const bf16x8 aq = join_tr(T::tr_at(qt + rb, o0), T::tr_at(qt + rb, o1));
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        mfma32_agpr(dv[kk][t], ag, pb[kk][m]);
+                        mfma32_agpr(dk[kk][t], aq, db[kk][m]);
+                    }
                 }
         }
 
         wait_vm_all();
         __syncthreads();
     }
+    TREEATTN_FENCE_ACC("s_nop 7\n\ts_nop 7\n\ts_nop 7");  // last MFMA writes -> the reads below
+#undef TREEATTN_FENCE_ACC
 
-    // lane holds key kw0 + j32, d = 32 t + 8 j + 4 h + 0..3 in registers 4 j + 0..3
-    const int64_t off = int64_t(key) * kv_stride + hkv * D + 4 * h;
+    // lane holds key 32 kk + j32 of the wave, d = 32 t + 8 j + 4 h + 0..3 in
+    // registers 4 j + 0..3
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int kk = 0; kk < 2; ++kk) {
+        if (key[kk] >= L) continue;
+        const int64_t off = int64_t(key[kk]) * kv_stride + hkv * D + 4 * h;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int d0 = 32 * t + 8 * j;
-            st8(dK + off + d0, u32x2{pack_bf16x2(dk[t][4 * j] * scale, dk[t][4 * j + 1] * scale),
-                                     pack_bf16x2(dk[t][4 * j + 2] * scale, dk[t][4 * j + 3] * scale)});
-            st8(dV + off + d0, u32x2{pack_bf16x2(dv[t][4 * j], dv[t][4 * j + 1]),
-                                     pack_bf16x2(dv[t][4 * j + 2], dv[t][4 * j + 3])});
-        }
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d0 = 32 * t + 8 * j;
+                st8(dK + off + d0, u32x2{pack_bf16x2(dk[kk][t][4 * j] * scale, dk[kk][t][4 * j + 1] * scale),
+                                         pack_bf16x2(dk[kk][t][4 * j + 2] * scale, dk[kk][t][4 * j + 3] * scale)});
+                st8(dV + off + d0, u32x2{pack_bf16x2(dv[kk][t][4 * j], dv[kk][t][4 * j + 1]),
+                                         pack_bf16x2(dv[kk][t][4 * j + 2], dv[kk][t][4 * j + 3])});
+            }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -477,13 +564,13 @@ hipError_t launch_bwd_d(int phase, const bf16* Q, const bf16* K, const bf16* V, 
     const int L = int(sh.L);
     const int64_t rows = int64_t(L) * sh.Hq;
     const float sl2 = sh.scale * kLog2e;
-    float* lse2 = delta + rows;  // second half of the workspace
+    float* nls = delta + rows;  // second half of the workspace
     if (phase == kPhaseAll || phase == kPhaseDelta)
         delta_bf16_kernel<D><<<dim3(unsigned((L + 256 / (D / 8) - 1) / (256 / (D / 8))), unsigned(sh.Hq)), 256, 0,
-                               stream>>>(O, dO, lse, delta, lse2, L, sh.Hq);
+                               stream>>>(O, dO, lse, delta, nls, 1.0f / sh.scale, L, sh.Hq);
     if (phase == kPhaseAll || phase == kPhaseDkdv)
-        dkdv_bf16_kernel<D><<<unsigned(sh.nb) * unsigned(sh.Hkv), kThreads, 0, stream>>>(
-            Q, K, V, dO, lse2, delta, dK, dV, se, mp.k_order, mp.col_ptr, mp.col_ent, L, sh.Hq, sh.Hkv, sl2,
+        dkdv_bf16_kernel<D><<<unsigned((sh.nb + 1) / 2) * unsigned(sh.Hkv), kThreads, 0, stream>>>(
+            Q, K, V, dO, nls, delta, dK, dV, se, mp.p_order, mp.blk_min, mp.blk_max, L, sh.Hq, sh.Hkv, sl2,
             sh.scale);
     if (phase == kPhaseAll || phase == kPhaseDq)
         dq_bf16_kernel<D><<<unsigned(sh.nb) * unsigned(sh.Hq), kThreads, 0, stream>>>(

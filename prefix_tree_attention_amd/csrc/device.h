@@ -28,10 +28,14 @@ constexpr int64_t kMaxL = 1 << 20;   // largest packed length accepted
 //   col_ent  [T]      (query block << 1) | partial, ascending query block
 //   q_order  [nb]     query blocks, most nonempty tiles first (ties: index)
 //   k_order  [nb]     key blocks, most nonempty tiles first (ties: index)
+//   blk_cnt  [nb]     real tokens per block, then their exclusive prefix
+//   blk_hsum [nb]     histogram mass per block, then its exclusive prefix
+//   p_order  [np]     key-block pairs (2p, 2p + 1), np = (nb + 1) / 2, most
+//                     nonempty query blocks first (ties: index)
 struct MetaLayout {
     int64_t L, nb, T;
     int64_t hdr, blk_min, blk_max, hist, row_cnt, row_ptr, row_ent, col_cnt, col_ptr, col_ent,
-        q_order, k_order, blk_cnt, blk_hsum, words;
+        q_order, k_order, blk_cnt, blk_hsum, p_order, words;
 };
 
 inline int64_t pad64(int64_t w) { return (w + 63) / 64 * 64; }
@@ -54,8 +58,9 @@ inline MetaLayout meta_layout(int64_t L) {
     m.col_ent = o; o += pad64(m.T);
     m.q_order = o; o += pad64(m.nb);
     m.k_order = o; o += pad64(m.nb);
-    m.blk_cnt = o; o += pad64(m.nb);   // real tokens per block, then their exclusive prefix
-    m.blk_hsum = o; o += pad64(m.nb);  // histogram mass per block, then its exclusive prefix
+    m.blk_cnt = o; o += pad64(m.nb);
+    m.blk_hsum = o; o += pad64(m.nb);
+    m.p_order = o; o += pad64((m.nb + 1) / 2);
     m.words = o;
     return m;
 }
@@ -68,12 +73,16 @@ struct MetaPtrs {
     const int32_t* col_ent;
     const int32_t* q_order;
     const int32_t* k_order;
+    const int32_t* blk_min;
+    const int32_t* blk_max;
+    const int32_t* p_order;
 };
 
 inline MetaPtrs meta_ptrs(const void* ws, int64_t L) {
     const MetaLayout m = meta_layout(L);
     const int32_t* w = static_cast<const int32_t*>(ws);
-    return {w + m.row_ptr, w + m.row_ent, w + m.col_ptr, w + m.col_ent, w + m.q_order, w + m.k_order};
+    return {w + m.row_ptr, w + m.row_ent, w + m.col_ptr, w + m.col_ent, w + m.q_order,
+            w + m.k_order, w + m.blk_min, w + m.blk_max, w + m.p_order};
 }
 
 // Backward phases (TREE_BWD_* of the public header).

@@ -159,7 +159,7 @@ __global__ __launch_bounds__(1024) void meta_scan(const int32_t* __restrict__ bl
                                                   const int32_t* __restrict__ row_cnt, int32_t* __restrict__ col_cnt,
                                                   int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_ptr,
                                                   int32_t* __restrict__ q_order, int32_t* __restrict__ k_order,
-                                                  int nb) {
+                                                  int32_t* __restrict__ p_order, int nb) {
     __shared__ long long sh[32];
     const int t = threadIdx.x, nt = blockDim.x;
     const int chunk = (nb + nt - 1) / nt;
@@ -209,16 +209,32 @@ __global__ __launch_bounds__(1024) void meta_scan(const int32_t* __restrict__ bl
     // heaviest-first orders, ties by index: the keys
     // ((nb - count) << 13) | index are unique, so sorting them ascending
     // with a bitonic network in LDS gives exactly that order in
-    // O(nb log^2 nb) work (nb <= 8192 = 2^13 blocks)
+    // O(nb log^2 nb) work (nb <= 8192 = 2^13 blocks).  A key-block pair's
+    // count is the number of query blocks in the union of its two columns:
+    // each column is a contiguous range starting at its own block, so the
+    // union is the range from the first block with a real token to the
+    // larger of the two ends.
     constexpr int kMaxNb = int(kMaxL / kBlock);
     static_assert(kMaxNb <= (1 << 13), "block index must fit 13 bits");
-    __shared__ unsigned kq[kMaxNb], kk[kMaxNb];
+    __shared__ unsigned kq[kMaxNb], kk[kMaxNb], kpr[kMaxNb / 2];
     int n = 1;
     while (n < nb) n <<= 1;
+    const int np = (nb + 1) / 2, npp = (n + 1) / 2;
     __syncthreads();  // col_cnt written by other threads above
     for (int i = t; i < n; i += nt) {
         kq[i] = i < nb ? (unsigned(nb - row_cnt[i]) << 13) | unsigned(i) : 0xffffffffu;
         kk[i] = i < nb ? (unsigned(nb - col_cnt[i]) << 13) | unsigned(i) : 0xffffffffu;
+    }
+    for (int i = t; i < npp; i += nt) {
+        unsigned key = 0xffffffffu;
+        if (i < np) {
+            const int b0 = 2 * i, b1 = 2 * i + 1;
+            const int c0 = col_cnt[b0], c1 = b1 < nb ? col_cnt[b1] : 0;
+            const int end = max(c0 ? b0 + c0 : 0, c1 ? b1 + c1 : 0);  // one past the last query block
+            const int cnt = c0 ? end - b0 : (c1 ? end - b1 : 0);
+            key = (unsigned(nb - cnt) << 13) | unsigned(i);
+        }
+        kpr[i] = key;
     }
     __syncthreads();
     for (int k = 2; k <= n; k <<= 1)
@@ -238,6 +254,14 @@ __global__ __launch_bounds__(1024) void meta_scan(const int32_t* __restrict__ bl
                         kk[i] = y;
                         kk[p] = x;
                     }
+                    if (p < npp && k <= npp) {
+                        x = kpr[i];
+                        y = kpr[p];
+                        if ((x > y) == up) {
+                            kpr[i] = y;
+                            kpr[p] = x;
+                        }
+                    }
                 }
             }
             __syncthreads();
@@ -246,6 +270,7 @@ __global__ __launch_bounds__(1024) void meta_scan(const int32_t* __restrict__ bl
         q_order[i] = int(kq[i] & 0x1fffu);
         k_order[i] = int(kk[i] & 0x1fffu);
     }
+    for (int i = t; i < np; i += nt) p_order[i] = int(kpr[i] & 0x1fffu);
 }
 
 // One workgroup (256 threads) per block b: the position ids of its tokens,
@@ -337,7 +362,8 @@ hipError_t launch_meta(const int32_t* se, int64_t L, int32_t* pos, uint8_t* tile
     meta_tiles<<<nb, 256, 0, stream>>>(w + m.blk_min, w + m.blk_max, w + m.hist, tile_class, w + m.row_cnt,
                                       w + m.blk_hsum, nb);
     meta_scan<<<1, 1024, 0, stream>>>(w + m.blk_max, w + m.blk_cnt, w + m.blk_hsum, w + m.row_cnt, w + m.col_cnt,
-                                     w + m.row_ptr, w + m.col_ptr, w + m.q_order, w + m.k_order, nb);
+                                     w + m.row_ptr, w + m.col_ptr, w + m.q_order, w + m.k_order, w + m.p_order,
+                                     nb);
     meta_lists<<<nb, 256, 0, stream>>>(se, w + m.hist, w + m.blk_min, w + m.blk_max, w + m.blk_cnt, w + m.blk_hsum,
                                       w + m.row_ptr, w + m.col_ptr, pos, w + m.row_ent, w + m.col_ent, int(L), nb);
     return hipGetLastError();

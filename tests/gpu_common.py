@@ -59,7 +59,8 @@ def meta_layout(L: int) -> dict:
     for name, size in (("hdr", 64), ("blk_min", pad(nb)), ("blk_max", pad(nb)), ("hist", pad(L + 1)),
                        ("row_cnt", pad(nb)), ("row_ptr", pad(nb + 1)), ("row_ent", pad(T)),
                        ("col_cnt", pad(nb)), ("col_ptr", pad(nb + 1)), ("col_ent", pad(T)),
-                       ("q_order", pad(nb)), ("k_order", pad(nb))):
+                       ("q_order", pad(nb)), ("k_order", pad(nb)), ("blk_cnt", pad(nb)), ("blk_hsum", pad(nb)),
+                       ("p_order", pad((nb + 1) // 2))):
         out[name] = o
         o += size
     out["nb"] = nb

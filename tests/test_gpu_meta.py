@@ -46,6 +46,16 @@ def _check_trie(torch, p_lib, p_or, tag):
     ko = ws[lay["k_order"]:lay["k_order"] + nb]
     assert qo.tolist() == sorted(range(nb), key=lambda x: (-rc[x], x))
     assert ko.tolist() == sorted(range(nb), key=lambda x: (-cc[x], x))
+    # key-block pairs (2p, 2p + 1): the union of their columns is one
+    # contiguous run of query blocks, and the pairs come heaviest first
+    npair = (nb + 1) // 2
+    pc = []
+    for p in range(npair):
+        qbs = np.nonzero((tc_ref[:, 2 * p:2 * p + 2] != 0).any(1))[0]
+        assert len(qbs) == 0 or qbs[-1] - qbs[0] + 1 == len(qbs), f"pair {p} columns not contiguous"
+        pc.append(len(qbs))
+    po = ws[lay["p_order"]:lay["p_order"] + npair]
+    assert po.tolist() == sorted(range(npair), key=lambda x: (-pc[x], x))
     assert ws[lay["hdr"] + 2] == p_or.n_tokens
 
 
