@@ -84,8 +84,7 @@ __global__ __launch_bounds__(256) void delta_bf16_kernel(const bf16* __restrict_
 
 // direct load of 64 consecutive floats (one wave)
 __device__ __forceinline__ void load_row64_async(lds_char* dst, const float* __restrict__ src, int lane) {
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + lane), reinterpret_cast<lds_void*>(dst), 4, 0,
-                                     0);
+    dma4(src, 4u * lane, lds_addr(dst));
 }
 
 // ---------------------------------------------------------------------------
@@ -101,7 +100,7 @@ __device__ __forceinline__ void load_row64_async(lds_char* dst, const float* __r
 // by anything else.  Consecutive updates of one accumulator by MFMAs of
 // this same shape need no wait states.
 __device__ __forceinline__ void mfma32_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
                  : "+a"(acc)
                  : "v"(__builtin_bit_cast(i32x4, a)), "v"(__builtin_bit_cast(i32x4, b)));
 }
@@ -255,6 +254,12 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
         issue(nxt, 0);
         advance(nxt);
     }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        consume(sek[kk]);
+#pragma unroll
+        for (int x = 0; x < NX; ++x) consume(vf[kk][x]);
+    }
     wait_vm_all();
     __syncthreads();
 
@@ -354,7 +359,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
                                           f32x4{d[8 * m + 4], d[8 * m + 5], d[8 * m + 6], d[8 * m + 7]});
                 }
             // the conversions above are VALU writes that the asm MFMAs read
-            asm volatile("s_nop 1"
+            asm("s_nop 1"
                          : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]), "+v"(db[0][0]),
                            "+v"(db[0][1]), "+v"(db[1][0]), "+v"(db[1][1]));
             // dV^T += dO^T P, dK^T += Q^T dS: A = 32 d x 16 queries read
@@ -460,11 +465,19 @@ __global__ __launch_bounds__(kThreads, 2) void dq_bf16_kernel(
         // the keys' subtree ends ride with the tiles (wave w stages 16 of
         // them), so the partial-tile mask reads LDS instead of issuing
         // global loads whose wait would also drain the prefetch
-        if (lane < 16)
-            __builtin_amdgcn_global_load_lds(static_cast<const void*>(se + kbase + 16 * wave + lane),
-                                             reinterpret_cast<lds_void*>(serow(buf) + 64 * wave), 4, 0, 0);
+        if (lane < 16) dma4(se + kbase + 16 * wave, 4u * lane, lds_addr(serow(buf) + 64 * wave));
     };
     if (nsteps > 0) issue(0, 0);
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+        consume(lse2[qs]);
+        consume(dlt[qs]);
+#pragma unroll
+        for (int x = 0; x < NS; ++x) {
+            consume(qf[qs][x]);
+            consume(gf[qs][x]);
+        }
+    }
     wait_vm_all();
     __syncthreads();
 

@@ -101,11 +101,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         // the keys' subtree ends ride with the tiles (wave w stages 16 of
         // them), so the partial-tile mask reads LDS instead of issuing
         // global loads whose wait would also drain the prefetch
-        if (lane < 16)
-            __builtin_amdgcn_global_load_lds(static_cast<const void*>(se + kbase + 16 * wave + lane),
-                                             reinterpret_cast<lds_void*>(serow(buf) + 64 * wave), 4, 0, 0);
+        if (lane < 16) dma4(se + kbase + 16 * wave, 4u * lane, lds_addr(serow(buf) + 64 * wave));
     };
     if (nsteps > 0) issue(0, 0);
+#pragma unroll
+    for (int x = 0; x < NX; ++x) consume(qf[x]);
     wait_vm_all();
     __syncthreads();
 

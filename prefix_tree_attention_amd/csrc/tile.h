@@ -38,11 +38,28 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTileRows = 64;
 
+__device__ __forceinline__ uint32_t lds_addr(const lds_char* p) { return uint32_t(size_t(p)); }
+
+// Direct HBM -> LDS loads: each lane's 16 (dma16) or 4 (dma4) bytes at
+// base + voff land at LDS address lds + 16 * lane (4 * lane); `base` and
+// `lds` are wave-uniform.  They are issued as inline asm so that the
+// compiler does not count them as pending LDS writes: it cannot tell the
+// buffer being filled from the one being read, and would otherwise wait for
+// the prefetch to land before the first transposing LDS read of a step.
+// Completion is the caller's s_waitcnt vmcnt followed by a workgroup
+// barrier.  M0 carries the LDS address (one wait state before its use); no
+// compiler-generated code in these kernels uses M0.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds));
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds));
+}
+
 template <int D>
 struct Tile {
     static constexpr int kChunks = D / 8;              // 16-byte chunks per row
     static constexpr int kBytes = kTileRows * D * 2;   // 16 KB (D=128) / 8 KB (D=64)
-    static constexpr int kLoadsPerWave = kBytes / 1024 / 4;  // 1 KB per wave instruction, 4 waves
 
     __device__ static __forceinline__ int swz(int r) {
         if constexpr (D == 128)
@@ -55,20 +72,23 @@ struct Tile {
     // r % 16 only, so moving 16 rows down is a plain add of 16 kRowBytes
     __device__ static __forceinline__ int slot(int r, int c) { return (r * kChunks + (c ^ swz(r))) * 16; }
 
-    // Issue this wave's share of the direct loads of one tile.  `g0` points
-    // at element 0 of row 0 (token of row 0, this head); `stride` is the
-    // token stride in elements.  Completion: s_waitcnt vmcnt(0) in each wave,
-    // then a workgroup barrier.
+    // Issue this wave's share of the direct loads of one tile, shared by NW
+    // waves (1 KB per wave instruction, kLoads<NW> instructions each).
+    // `g0` points at element 0 of row 0 (token of row 0, this head);
+    // `stride` is the token stride in elements.  Completion: s_waitcnt vmcnt
+    // in each wave, then a workgroup barrier.
+    template <int NW>
+    static constexpr int kLoads = kBytes / 1024 / NW;
+    template <int NW = 4>
     __device__ static __forceinline__ void load_async(lds_char* tile, const bf16* __restrict__ g0, int stride,
                                                       int wave, int lane) {
 #pragma unroll
-        for (int j = 0; j < kLoadsPerWave; ++j) {
-            const int blk = wave * kLoadsPerWave + j;  // 1 KB block = 64 slots
+        for (int j = 0; j < kLoads<NW>; ++j) {
+            const int blk = wave * kLoads<NW> + j;  // 1 KB block = 64 slots
             const int p = blk * 64 + lane;             // slot this lane fills
             const int r = p / kChunks, pos = p % kChunks;
             const int c = pos ^ swz(r);
-            __builtin_amdgcn_global_load_lds(static_cast<const void*>(g0 + uint32_t(r * stride + 8 * c)),
-                                             reinterpret_cast<lds_void*>(tile + blk * 1024), 16, 0, 0);
+            dma16(g0, uint32_t(r * stride + 8 * c) * 2u, lds_addr(tile + blk * 1024));
         }
     }
 
@@ -97,7 +117,22 @@ struct Tile {
     }
 };
 
+// A compiler-visible use of a loaded value.  The direct loads above are
+// invisible to the compiler's wait-count bookkeeping, so a kernel's
+// prologue loads are consumed here, before its main loop: otherwise the
+// compiler places their waits at the first use inside the loop, where the
+// hardware counter also holds the freshly issued prefetch.
+__device__ __forceinline__ void consume(const bf16x8& v) { asm volatile("" ::"v"(__builtin_bit_cast(i32x4, v))); }
+__device__ __forceinline__ void consume(float v) { asm volatile("" ::"v"(v)); }
+__device__ __forceinline__ void consume(int v) { asm volatile("" ::"v"(v)); }
+
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// wait until at most N of this wave's vector memory operations are pending
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // XCD-aware work order.  Workgroups are dispatched round-robin over the 8
 // XCDs (block b runs on XCD b % 8), and each XCD has its own L2.  The
