@@ -241,11 +241,14 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
             }
         }
     };
+    const uint32_t q_row_bytes = uint32_t(q_stride) * 2u;
     auto issue = [&](const StepPos& p, int buf) {
         const int hq = hkv * G + p.head;
-        const int64_t off = int64_t(p.qbase) * q_stride + int64_t(hq) * D;
-        T::load_async(qtile(buf), Q + off, qs32, wave, lane);
-        T::load_async(gtile(buf), dO + off, qs32, wave, lane);
+        const uint64_t off = uint64_t(uint32_t(p.qbase)) * q_row_bytes + uint32_t(hq * D * 2);
+        T::load_async(qtile(buf), reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(Q) + off), qs32, wave,
+                      lane);
+        T::load_async(gtile(buf), reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(dO) + off), qs32,
+                      wave, lane);
         if (wave == 0) load_row64_async(lsev(buf), NLS + int64_t(hq) * L + p.qbase, lane);
         if (wave == 1) load_row64_async(dlv(buf), Delta + int64_t(hq) * L + p.qbase, lane);
     };
@@ -457,11 +460,14 @@ __global__ __launch_bounds__(kThreads, 2) void dq_bf16_kernel(
     auto ktile = [&](int buf) { return smem + (2 * buf) * T::kBytes; };
     auto vtile = [&](int buf) { return smem + (2 * buf + 1) * T::kBytes; };
     auto serow = [&](int buf) { return smem + 4 * T::kBytes + buf * 4 * kStep; };
+    const char* const Kh = reinterpret_cast<const char*>(K + int64_t(hkv) * D);
+    const char* const Vh = reinterpret_cast<const char*>(V + int64_t(hkv) * D);
+    const uint32_t kv_row_bytes = uint32_t(kv_stride) * 2u;
     auto issue = [&](int st, int buf) {
         const int kbase = (row_ent[beg + (st >> 1)] >> 1) * kBlock + kStep * (st & 1);
-        const int64_t off = int64_t(kbase) * kv_stride + int64_t(hkv) * D;
-        T::load_async(ktile(buf), K + off, kvs, wave, lane);
-        T::load_async(vtile(buf), V + off, kvs, wave, lane);
+        const uint64_t off = uint64_t(uint32_t(kbase)) * kv_row_bytes;
+        T::load_async(ktile(buf), reinterpret_cast<const bf16*>(Kh + off), kvs, wave, lane);
+        T::load_async(vtile(buf), reinterpret_cast<const bf16*>(Vh + off), kvs, wave, lane);
         // the keys' subtree ends ride with the tiles (wave w stages 16 of
         // them), so the partial-tile mask reads LDS instead of issuing
         // global loads whose wait would also drain the prefetch

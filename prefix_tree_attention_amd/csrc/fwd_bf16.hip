@@ -93,11 +93,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     auto ktile = [&](int buf) { return smem + (2 * buf) * T::kBytes; };
     auto vtile = [&](int buf) { return smem + (2 * buf + 1) * T::kBytes; };
     auto serow = [&](int buf) { return smem + 4 * T::kBytes + buf * 4 * kStep; };
+    // byte addresses: a step's tiles start at (head base) + kbase * row bytes
+    const char* const Kh = reinterpret_cast<const char*>(K + int64_t(hkv) * D);
+    const char* const Vh = reinterpret_cast<const char*>(V + int64_t(hkv) * D);
+    const uint32_t kv_row_bytes = uint32_t(kv_stride) * 2u;
     auto issue = [&](int st, int buf) {
         const int kbase = (row_ent[beg + (st >> 1)] >> 1) * kBlock + kStep * (st & 1);
-        const int64_t off = int64_t(kbase) * kv_stride + int64_t(hkv) * D;
-        T::load_async(ktile(buf), K + off, kvs, wave, lane);
-        T::load_async(vtile(buf), V + off, kvs, wave, lane);
+        const uint64_t off = uint64_t(uint32_t(kbase)) * kv_row_bytes;
+        T::load_async(ktile(buf), reinterpret_cast<const bf16*>(Kh + off), kvs, wave, lane);
+        T::load_async(vtile(buf), reinterpret_cast<const bf16*>(Vh + off), kvs, wave, lane);
         // the keys' subtree ends ride with the tiles (wave w stages 16 of
         // them), so the partial-tile mask reads LDS instead of issuing
         // global loads whose wait would also drain the prefetch

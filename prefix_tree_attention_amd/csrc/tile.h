@@ -27,6 +27,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <utility>
 
 #include "mfma.h"
 
@@ -51,6 +52,12 @@ __device__ __forceinline__ uint32_t lds_addr(const lds_char* p) { return uint32_
 // compiler-generated code in these kernels uses M0.
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds));
+}
+// same, LDS address lds + IMM (one scalar add into M0)
+template <int IMM>
+__device__ __forceinline__ void dma16_at(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base),
+                 "s"(lds), "n"(IMM));
 }
 __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds));
@@ -82,14 +89,22 @@ struct Tile {
     template <int NW = 4>
     __device__ static __forceinline__ void load_async(lds_char* tile, const bf16* __restrict__ g0, int stride,
                                                       int wave, int lane) {
-#pragma unroll
-        for (int j = 0; j < kLoads<NW>; ++j) {
-            const int blk = wave * kLoads<NW> + j;  // 1 KB block = 64 slots
-            const int p = blk * 64 + lane;             // slot this lane fills
-            const int r = p / kChunks, pos = p % kChunks;
-            const int c = pos ^ swz(r);
-            dma16(g0, uint32_t(r * stride + 8 * c) * 2u, lds_addr(tile + blk * 1024));
-        }
+        const uint32_t lds0 = lds_addr(tile) + uint32_t(wave * kLoads<NW> * 1024);
+        load_async_j<NW>(lds0, g0, stride, wave, lane, std::make_integer_sequence<int, kLoads<NW>>{});
+    }
+    template <int NW, int... J>
+    __device__ static __forceinline__ void load_async_j(uint32_t lds0, const bf16* __restrict__ g0, int stride,
+                                                        int wave, int lane, std::integer_sequence<int, J...>) {
+        (dma16_at<1024 * J>(g0, lane_offset<NW>(J, stride, wave, lane), lds0), ...);
+    }
+    // byte offset (from g0) of the 16 bytes lane `lane` fills in load J
+    template <int NW>
+    __device__ static __forceinline__ uint32_t lane_offset(int j, int stride, int wave, int lane) {
+        const int blk = wave * kLoads<NW> + j;  // 1 KB block = 64 slots
+        const int p = blk * 64 + lane;          // slot this lane fills
+        const int r = p / kChunks, pos = p % kChunks;
+        const int c = pos ^ swz(r);
+        return uint32_t(r * stride + 8 * c) * 2u;
     }
 
     // Row-major operand: 8 bf16 of row r starting at element 8c.
