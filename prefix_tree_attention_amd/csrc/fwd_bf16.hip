@@ -90,42 +90,37 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
     const int beg = row_ptr[qb], nsteps = 2 * (row_ptr[qb + 1] - beg);
     const int kvs = int(kv_stride);
-    auto ktile = [&](int buf) { return smem + (2 * buf) * T::kBytes; };
-    auto vtile = [&](int buf) { return smem + (2 * buf + 1) * T::kBytes; };
-    auto serow = [&](int buf) { return smem + 4 * T::kBytes + buf * 4 * kStep; };
+    // Software pipeline: while step st runs its softmax and P V, the S^T of
+    // step st + 1 is computed, so the MFMA unit has independent work while
+    // the wave does its exp / row-sum VALU work.  K and V therefore sit in
+    // separate two-deep rings: at step st, V(st) (with the keys' subtree
+    // ends) and K(st + 1) are resident while K(st + 2) and V(st + 1) load.
+    auto ktile = [&](int st) { return smem + (st & 1) * T::kBytes; };
+    auto vtile = [&](int st) { return smem + (2 + (st & 1)) * T::kBytes; };
+    auto serow = [&](int st) { return smem + 4 * T::kBytes + (st & 1) * 4 * kStep; };
     // byte addresses: a step's tiles start at (head base) + kbase * row bytes
     const char* const Kh = reinterpret_cast<const char*>(K + int64_t(hkv) * D);
     const char* const Vh = reinterpret_cast<const char*>(V + int64_t(hkv) * D);
     const uint32_t kv_row_bytes = uint32_t(kv_stride) * 2u;
-    auto issue = [&](int st, int buf) {
-        const int kbase = (row_ent[beg + (st >> 1)] >> 1) * kBlock + kStep * (st & 1);
+    auto kbase_of = [&](int st) { return (row_ent[beg + (st >> 1)] >> 1) * kBlock + kStep * (st & 1); };
+    auto issue_k = [&](int st) {
+        const uint64_t off = uint64_t(uint32_t(kbase_of(st))) * kv_row_bytes;
+        T::load_async(ktile(st), reinterpret_cast<const bf16*>(Kh + off), kvs, wave, lane);
+    };
+    auto issue_v = [&](int st) {
+        const int kbase = kbase_of(st);
         const uint64_t off = uint64_t(uint32_t(kbase)) * kv_row_bytes;
-        T::load_async(ktile(buf), reinterpret_cast<const bf16*>(Kh + off), kvs, wave, lane);
-        T::load_async(vtile(buf), reinterpret_cast<const bf16*>(Vh + off), kvs, wave, lane);
-        // the keys' subtree ends ride with the tiles (wave w stages 16 of
+        T::load_async(vtile(st), reinterpret_cast<const bf16*>(Vh + off), kvs, wave, lane);
+        // the keys' subtree ends ride with the V tile (wave w stages 16 of
         // them), so the partial-tile mask reads LDS instead of issuing
         // global loads whose wait would also drain the prefetch
-        if (lane < 16) dma4(se + kbase + 16 * wave, 4u * lane, lds_addr(serow(buf) + 64 * wave));
+        if (lane < 16) dma4(se + kbase + 16 * wave, 4u * lane, lds_addr(serow(st) + 64 * wave));
     };
-    if (nsteps > 0) issue(0, 0);
-#pragma unroll
-    for (int x = 0; x < NX; ++x) consume(qf[x]);
-    wait_vm_all();
-    __syncthreads();
-
-    for (int st = 0; st < nsteps; ++st) {
-        const int buf = st & 1;
-        const int ent = row_ent[beg + (st >> 1)];
-        const int kbase = (ent >> 1) * kBlock + kStep * (st & 1);
-        const bool partial = ent & 1;
-        if (st + 1 < nsteps) issue(st + 1, buf ^ 1);
-        const lds_char* kt = ktile(buf);
-        const lds_char* vt = vtile(buf);
-
-        // S^T = K Q^T (unscaled) for the step's two 32-key blocks kk:
-        // register r holds key kbase + 32 kk + 8 (r / 4) + 4 h + r % 4
-        // against this lane's query
-        f32x16 sc[2];
+    // S^T = K Q^T (unscaled) of step st for its two 32-key blocks kk:
+    // register r holds key kbase + 32 kk + 8 (r / 4) + 4 h + r % 4 against
+    // this lane's query
+    auto scores = [&](int st, f32x16 (&sc)[2]) {
+        const lds_char* kt = ktile(st);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
@@ -134,6 +129,30 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
             for (int x = 0; x < NX; ++x)
                 sc[kk] = mfma32x32x16(T::frag_at(kt + 32 * kk * T::kRowBytes, roff[x]), qf[x], sc[kk]);
         }
+    };
+
+    f32x16 sa[2], sb[2];
+    if (nsteps > 0) {
+        issue_k(0);
+        issue_v(0);
+        if (nsteps > 1) issue_k(1);
+    }
+#pragma unroll
+    for (int x = 0; x < NX; ++x) consume(qf[x]);
+    wait_vm_all();
+    __syncthreads();
+    scores(0, sa);  // with no steps this reads stale LDS and is never used
+    __syncthreads();  // every wave is done with K(0) before K(2) replaces it
+
+    // one step: softmax and P V of step st on `sc`, scores of step st + 1
+    // into `sn`
+    auto step = [&](int st, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+        const int ent = row_ent[beg + (st >> 1)];
+        const int kbase = (ent >> 1) * kBlock + kStep * (st & 1);
+        const bool partial = ent & 1;
+        if (st + 2 < nsteps) issue_k(st + 2);
+        if (st + 1 < nsteps) issue_v(st + 1);
+        const lds_char* vt = vtile(st);
 
         if (partial) {
             // key <= qi  <=>  8 (r / 4) + r % 4 <= qi - (kbase + 32 kk + 4 h)
@@ -143,7 +162,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const i32x4 sek = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(
-                        serow(buf) + 4 * (32 * kk + 8 * j + 4 * h));
+                        serow(st) + 4 * (32 * kk + 8 * j + 4 * h));
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         if (!(8 * j + i <= lim && qi <= sek[i])) sc[kk][4 * j + i] = -INFINITY;
@@ -178,6 +197,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
             m_run = mnew;
         }
         const float muse = m_run == -INFINITY ? 0.f : m_run;
+
+        // the next step's scores, independent of the exp work below (after
+        // the last step they read a stale K buffer and are discarded)
+        scores(st + 1, sn);
+
         float rs = 0.f;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
@@ -211,6 +235,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
         wait_vm_all();
         __syncthreads();
+    };
+    // a query block's step count is even (two per 128-key tile), so the
+    // score buffers alternate without copies
+    for (int st = 0; st < nsteps; st += 2) {
+        step(st, sa, sb);
+        step(st + 1, sb, sa);
     }
 
     // epilogue: normalise, write O (bf16) and LSE (natural log)
