@@ -19,6 +19,8 @@ convention) and is compared with MI355X's dense bf16 MFMA peak.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--config 4a]
                     [--sweep L,b] [--no-cpu-baseline]
+    python bench.py --logprobs [--vocab 151936] [--config 4a]   (the
+                    tree log-probability gather, its own JSON line)
 """
 
 from __future__ import annotations
@@ -58,6 +60,9 @@ def parse(argv=None):
     ap.add_argument("--sweep", default=None, help="L,b of a sweep point (overrides --config)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=1, help="query heads in the oracle sample")
+    ap.add_argument("--logprobs", action="store_true",
+                    help="time the tree log-probability / entropy gather (logits_stats + gather) instead")
+    ap.add_argument("--vocab", type=int, default=151936, help="vocabulary size of the --logprobs logits")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB elementwise copy kernel 3x (HBM counter calibration)")
     return ap.parse_args(argv)
@@ -147,6 +152,8 @@ def main(argv=None):
         return 2
     if a.copy_calibration:
         return copy_calibration()
+    if a.logprobs:
+        return bench_logprobs(a)
     import numpy as np
     import torch
     import workloads
@@ -335,6 +342,97 @@ def main(argv=None):
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
     return 0
+
+
+def bench_logprobs(a):
+    """Tree log-probabilities and entropies of one batch's packed logits
+    (bf16 [L, V], resident in HBM): tree_logits_stats over every packed row,
+    then tree_gather_logprobs into [B, S].  One JSON line; its roofline is the
+    HBM-bound row-statistics pass, whose algorithmic traffic is the logits
+    read once (2 L V bytes) plus 8 L bytes of output."""
+    import numpy as np
+    import torch
+    import workloads
+    import prefix_tree_attention_amd as pta
+
+    w = workloads.sweep_workload(*(int(x) for x in a.sweep.split(","))) if a.sweep else workloads.make_workload(a.config)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    se, tok, rp, lengths, stats = pta.pack_batch(w.ids, w.mask, w.max_tokens_per_mb)
+    L, V = len(se), int(a.vocab)
+    n_pred = int((w.mask.astype(bool).sum(1) - 1).sum())
+    log(f"logprobs {w.name}: L={L}, V={V}, {n_pred} predictions, logits {2 * L * V / 1e9:.1f} GB bf16")
+    g = torch.Generator(device=dev).manual_seed(2024)
+    x = torch.empty((L, V), dtype=torch.bfloat16, device=dev)
+    for r0 in range(0, L, 2048):
+        x[r0:r0 + 2048] = (torch.randn((min(2048, L - r0), V), generator=g, device=dev) * 2.0).to(torch.bfloat16)
+    tok_d = torch.from_numpy(tok).to(dev)
+    rp_d = torch.from_numpy(rp).to(dev)
+    torch.cuda.synchronize()
+    for _ in range(a.warmup):
+        pta.tree_logprobs(x, tok_d, rp_d)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        ev[i][0].record(stream)
+        lse, ent = pta.logits_stats(x)
+        ev[i][1].record(stream)
+        pta.gather_logprobs(x, lse, ent, tok_d, rp_d)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / a.steps
+    t_stats = sum(e[0].elapsed_time(e[1]) for e in ev) / a.steps
+    t_gather = sum(e[1].elapsed_time(e[2]) for e in ev) / a.steps
+    alg = 2.0 * L * V + 8.0 * L
+    achieved = alg / (t_stats * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "kernel": "logits_stats_kernel",
+            "traffic": _load_traffic_file(f"traffic_logits_stats_kernel_{w.name}-V{V}.json", "logprob.hip")}
+    result = {
+        "metric": "tree log-probability + entropy gather: predictions/s and HBM GB/s of the row-statistics pass",
+        "value": round(n_pred / sec, 1), "unit": "predictions/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(sec * 1e3, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "kernel_ms_per_launch": {"logits_stats": round(t_stats, 4), "gather": round(t_gather, 4)},
+        "config": {"workload": w.name, "L": L, "vocab": V, "batch": list(w.ids.shape), "predictions": n_pred},
+        "roofline": roof,
+    }
+    if not a.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas"]
+                        or [1])
+        except Exception:  # pragma: no cover
+            cores = 1
+        rng = np.random.default_rng(1)
+        picks = [(int(r), int(rng.integers(int(w.mask[r].sum()) - 1)))
+                 for r in rng.integers(w.ids.shape[0], size=4096)]
+        idx = torch.tensor([int(rp[r, j]) for r, j in picks], device=dev)
+        rows = x[idx].float().cpu().numpy()  # one copy of the sampled rows
+        t1 = time.perf_counter()
+        for (r, j), row in zip(picks, rows):
+            oracle.prediction_logprob_entropy(row, int(tok[rp[r, j + 1]]))
+        dt = time.perf_counter() - t1
+        result["cpu_baseline"] = {"value": len(picks) / dt, "unit": "predictions/s", "cores": cores, "kind": "oracle",
+                                  "sample": f"{len(picks)} predictions of the batch at V={V}, one float64 "
+                                            f"log-softmax and entropy each ({dt:.2f} s); the oracle's node cache "
+                                            f"would reuse shared rows, so this rate is per packed row"}
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def _load_traffic_file(name: str, source: str):
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    return float(t["bytes_per_launch"]) if t.get("source_sha") == source_sha(source) else None
 
 
 def _first_trie_rows(w, tr0):

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define TREE_ATTN_ABI_VERSION 2
+#define TREE_ATTN_ABI_VERSION 3
 
 /* status codes */
 #define TREE_OK 0
@@ -141,6 +141,20 @@ int tree_pack_stats(const tree_pack_t* p, tree_pack_stats_t* s);
  * least that.  Errors: TREE_E_ARG (NULL pack or L_total, cap too small). */
 int tree_pack_concat(const tree_pack_t* p, int32_t* out_se, int64_t cap, int64_t* L_total);
 
+/* Token ids of all tries in the concatenated layout of tree_pack_concat
+ * (pads carry the pack's pad id), into out_ids[cap].  Errors: TREE_E_ARG
+ * (NULL argument, cap smaller than the total length). */
+int tree_pack_concat_ids(const tree_pack_t* p, int32_t* out_ids, int64_t cap);
+
+/* Where each sequence sits in the concatenated layout (guide, section
+ * "Log Probability 计算": a sequence's own token order is recovered from
+ * the trie, root to leaf, as the pages' get_sequence_tree_indices does).
+ * out[r * S + k] = packed position of the k-th real token of batch row r
+ * (B, S: the batch shape the pack was built from), -1 for k >= the row's
+ * length.  cap is out's capacity in int32 and must be >= B * S.  Errors:
+ * TREE_E_ARG (NULL argument, cap too small). */
+int tree_pack_row_positions(const tree_pack_t* p, int32_t* out, int64_t cap);
+
 /* Release a pack (NULL is a no-op). */
 void tree_pack_free(tree_pack_t* p);
 
@@ -215,6 +229,44 @@ int tree_attn_bwd_phase(int32_t phase, const void* q, const void* k, const void*
                         const int32_t* d_se, const void* d_meta_ws, void* d_ws, size_t ws_bytes,
                         int64_t L, int32_t Hq, int32_t Hkv, int32_t D, float scale,
                         int32_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Log-probabilities and entropies of packed logits (device).  Guide,
+ * section "Log Probability 计算：树结构的特殊处理": labels cannot come from
+ * rolling the packed ids; each sequence's token k + 1 is predicted by the
+ * logits at the packed position of its token k (inside a node the next
+ * position, at a node's end the row every child's first token reads), and
+ * shared prefixes are computed once.  Here the row statistics are computed
+ * once per packed row and the per-sequence values are gathered, then laid
+ * out per batch row (the pages' merge_packed_tree_results).
+ * ---------------------------------------------------------------------- */
+
+/* Per packed row p of logits [L, V] (row-major, dtype TREE_DTYPE_BF16 or
+ * TREE_DTYPE_FP32, aligned to its element size; V any size >= 1):
+ *   d_lse[p] = ln sum_v exp(logits[p, v]),
+ *   d_ent[p] = -sum_v P_v ln P_v with P = softmax(logits[p, :]), 0 ln 0 = 0,
+ * both float32 [L], accumulated in float32 in one pass over the row.  A row
+ * of -inf gives lse -inf and entropy 0.  L = 0 is a no-op.  Errors:
+ * TREE_E_ARG (NULL pointer, bad shape or dtype, misaligned logits),
+ * TREE_E_HIP (launch). */
+int tree_logits_stats(const void* logits, int64_t L, int64_t V, int32_t dtype, float* d_lse, float* d_ent,
+                      void* stream);
+
+/* The gather, for a batch of B rows of width S: with pos = d_row_pos (from
+ * tree_pack_row_positions, on the device) and ids = the packed token ids
+ * [L] (tree_pack_concat_ids),
+ *   d_logp[r, j] = logits[pos[r, j], ids[pos[r, j + 1]]] - d_lse[pos[r, j]],
+ *   d_out_ent[r, j] = d_ent[pos[r, j]]
+ * for j < (row r's length) - 1, i.e. row r's j-th prediction is that of its
+ * token j + 1; every other entry is pad_value.  d_lse / d_ent come from
+ * tree_logits_stats on the same logits.  Outputs are float32 [B, S],
+ * fully overwritten.  A position outside [0, L) or a token id outside
+ * [0, V) yields NaN for that entry (never an access out of range).  B * S
+ * = 0 is a no-op.  Errors: TREE_E_ARG (NULL pointer, bad shape or dtype),
+ * TREE_E_HIP (launch). */
+int tree_gather_logprobs(const void* logits, int64_t L, int64_t V, int32_t dtype, const float* d_lse,
+                         const float* d_ent, const int32_t* d_ids, const int32_t* d_row_pos, int64_t B,
+                         int64_t S, float pad_value, float* d_logp, float* d_out_ent, void* stream);
 
 #ifdef __cplusplus
 }

@@ -50,4 +50,4 @@ from .attention import (  # noqa: F401
     attention_dq_rows,
     attention_dkdv_cols,
 )
-from .logprobs import gather_tree_logprobs_entropy  # noqa: F401
+from .logprobs import gather_tree_logprobs_entropy, prediction_logprob_entropy  # noqa: F401

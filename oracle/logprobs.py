@@ -21,7 +21,7 @@ Readings (the pages leave these open):
     output holds them in columns 0 .. l - 2 and the padding value after;
     the merged width is the input's S;
   - entropy is that of the full next-token distribution at the predicting
-    position, -sum_v p_v log p_v, p = softmax(logits row);
+    position, -sum_v p_v log p_v, p = softmax(logits row), with 0 log 0 = 0;
   - everything is computed in float64 from the logits as given.
 """
 
@@ -40,8 +40,18 @@ def _log_softmax(row: np.ndarray) -> np.ndarray:
 
 
 def _entropy(row: np.ndarray) -> float:
+    """-sum_v p_v log p_v, with 0 log 0 = 0 (a -inf logit contributes 0)."""
     ls = _log_softmax(row)
-    return float(-(np.exp(ls) * ls).sum())
+    p = np.exp(ls)
+    with np.errstate(invalid="ignore"):  # 0 * -inf is computed, then discarded
+        return float(-np.where(p > 0, p * ls, 0.0).sum())
+
+
+def prediction_logprob_entropy(row: np.ndarray, label: int) -> tuple[float, float]:
+    """One prediction: the log-probability of `label` under softmax(row) and
+    the entropy of that distribution (the quantities every cached piece of
+    the gather below holds)."""
+    return float(_log_softmax(row)[label]), _entropy(row)
 
 
 def gather_tree_logprobs_entropy(tries: list[PackedTrie], logits: list[np.ndarray], batch_size: int,
@@ -66,15 +76,14 @@ def gather_tree_logprobs_entropy(tries: list[PackedTrie], logits: list[np.ndarra
                     # parent's last position predicts this node's first token
                     key = (prev_end, start)
                     if key not in transition:
-                        transition[key] = (float(_log_softmax(lg[prev_end])[trie.token_ids[start]]),
-                                           _entropy(lg[prev_end]))
+                        transition[key] = prediction_logprob_entropy(lg[prev_end], trie.token_ids[start])
                     lp, en = transition[key]
                     lp_parts.append(lp)
                     en_parts.append(en)
                 key = (start, end)
                 if key not in internal:
-                    internal[key] = ([float(_log_softmax(lg[p])[trie.token_ids[p + 1]]) for p in range(start, end)],
-                                     [_entropy(lg[p]) for p in range(start, end)])
+                    preds = [prediction_logprob_entropy(lg[p], trie.token_ids[p + 1]) for p in range(start, end)]
+                    internal[key] = ([a for a, _ in preds], [b for _, b in preds])
                 lps, ens = internal[key]
                 lp_parts.extend(lps)
                 en_parts.extend(ens)

@@ -15,6 +15,7 @@ from .api import (  # noqa: F401
     TreeMeta,
     pack,
     pack_concat,
+    pack_batch,
     tree_meta,
     meta_workspace_bytes,
     bwd_workspace_bytes,
@@ -22,4 +23,7 @@ from .api import (  # noqa: F401
     attn_bwd,
     attn_bwd_phase,
     tree_attention,
+    logits_stats,
+    gather_logprobs,
+    tree_logprobs,
 )

@@ -64,6 +64,8 @@ SIGNATURES = {
     "tree_pack_trie": (ctypes.c_int, [c_vp, c_i64, ctypes.POINTER(TrieView)]),
     "tree_pack_stats": (ctypes.c_int, [c_vp, ctypes.POINTER(PackStats)]),
     "tree_pack_concat": (ctypes.c_int, [c_vp, c_vp, c_i64, ctypes.POINTER(c_i64)]),
+    "tree_pack_concat_ids": (ctypes.c_int, [c_vp, c_vp, c_i64]),
+    "tree_pack_row_positions": (ctypes.c_int, [c_vp, c_vp, c_i64]),
     "tree_pack_free": (None, [c_vp]),
     "tree_meta_workspace_bytes": (c_sz, [c_i64]),
     "tree_meta": (ctypes.c_int, [c_vp, c_i64, c_vp, c_vp, c_vp, c_sz, c_vp]),
@@ -74,6 +76,9 @@ SIGNATURES = {
                                      c_sz, c_i64, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp]),
     "tree_attn_bwd_phase": (ctypes.c_int, [c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                            c_vp, c_sz, c_i64, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp]),
+    "tree_logits_stats": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp]),
+    "tree_gather_logprobs": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_f32,
+                                            c_vp, c_vp, c_vp]),
 }
 BWD_ALL, BWD_DELTA, BWD_DKDV, BWD_DQ = 0, 1, 2, 3
 

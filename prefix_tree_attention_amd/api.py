@@ -113,6 +113,44 @@ def pack_concat(ids, mask, max_tokens_per_mb: int, block_size: int = BLOCK, pad_
     return se, lengths, stats
 
 
+def pack_batch(ids, mask, max_tokens_per_mb: int, block_size: int = BLOCK, pad_to_maximum: bool = False,
+               pad_id: int = 0):
+    """Pack a batch into the concatenated layout and return everything the
+    attention and log-probability calls need: ``(subtree_end, token_ids,
+    row_positions, lengths, stats)``.  ``token_ids`` is the packed ids
+    (``tree_pack_concat_ids``), ``row_positions`` the int32 [B, S] packed
+    position of each row's k-th real token, -1 after it
+    (``tree_pack_row_positions``)."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    if ids.ndim != 2 or ids.shape != mask.shape:
+        raise TreeAttnError(-5, "ids and mask must both be [B, S]")
+    L = lib()
+    h = ctypes.c_void_p()
+    check(L.tree_pack(ids.ctypes.data, mask.ctypes.data, ids.shape[0], ids.shape[1], int(max_tokens_per_mb),
+                      int(block_size), int(bool(pad_to_maximum)), int(pad_id), ctypes.byref(h)))
+    try:
+        total = ctypes.c_int64()
+        check(L.tree_pack_concat(h, None, 0, ctypes.byref(total)))
+        se = np.empty(int(total.value), dtype=np.int32)
+        check(L.tree_pack_concat(h, se.ctypes.data, se.size, ctypes.byref(total)))
+        tok = np.empty(int(total.value), dtype=np.int32)
+        check(L.tree_pack_concat_ids(h, tok.ctypes.data, tok.size))
+        rp = np.empty(ids.shape, dtype=np.int32)
+        check(L.tree_pack_row_positions(h, rp.ctypes.data, rp.size))
+        lengths = []
+        for t in range(L.tree_pack_num_tries(h)):
+            v = TrieView()
+            check(L.tree_pack_trie(h, t, ctypes.byref(v)))
+            lengths.append(int(v.L))
+        st = PackStats()
+        check(L.tree_pack_stats(h, ctypes.byref(st)))
+        stats = {k: getattr(st, k) for k, _ in PackStats._fields_}
+    finally:
+        L.tree_pack_free(h)
+    return se, tok, rp, lengths, stats
+
+
 # ---------------------------------------------------------------------------
 # device side
 # ---------------------------------------------------------------------------
@@ -266,3 +304,53 @@ def tree_attention(q, k, v, meta: TreeMeta, scale: float | None = None):
     if _FN is None:
         _FN = _autograd_fn()
     return _FN.apply(q, k, v, meta, scale)
+
+
+# ---------------------------------------------------------------------------
+# log-probabilities of packed logits
+# ---------------------------------------------------------------------------
+def _check_logits(logits):
+    if not logits.is_cuda or not logits.is_contiguous() or logits.dim() != 2:
+        raise TreeAttnError(-5, "logits must be a contiguous device tensor [L, V]")
+
+
+def logits_stats(logits):
+    """``tree_logits_stats``: per packed row, (lse [L], entropy [L]) fp32."""
+    torch = _torch()
+    _check_logits(logits)
+    L, V = logits.shape
+    lse = torch.empty(L, dtype=torch.float32, device=logits.device)
+    ent = torch.empty(L, dtype=torch.float32, device=logits.device)
+    check(lib().tree_logits_stats(_ptr(logits), L, V, _dtype_code(logits), _ptr(lse), _ptr(ent),
+                                  _stream(logits.device)))
+    return lse, ent
+
+
+def gather_logprobs(logits, lse, ent, token_ids, row_positions, pad_value: float = 0.0):
+    """``tree_gather_logprobs``: (logp [B, S], entropy [B, S]) fp32; row r's
+    j-th entry is the prediction of its token j + 1, pad_value after the
+    row's last prediction.  ``token_ids`` [L] and ``row_positions`` [B, S]
+    are int32 device tensors (see ``pack_batch``)."""
+    torch = _torch()
+    _check_logits(logits)
+    L, V = logits.shape
+    for name, t, dt in (("lse", lse, torch.float32), ("entropy", ent, torch.float32),
+                        ("token_ids", token_ids, torch.int32), ("row_positions", row_positions, torch.int32)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != dt:
+            raise TreeAttnError(-5, f"{name} must be a contiguous {dt} device tensor")
+    if lse.numel() != L or ent.numel() != L or token_ids.numel() != L or row_positions.dim() != 2:
+        raise TreeAttnError(-5, "lse / entropy / token_ids must have L entries, row_positions [B, S]")
+    B, S = row_positions.shape
+    logp = torch.empty((B, S), dtype=torch.float32, device=logits.device)
+    oent = torch.empty((B, S), dtype=torch.float32, device=logits.device)
+    check(lib().tree_gather_logprobs(_ptr(logits), L, V, _dtype_code(logits), _ptr(lse), _ptr(ent),
+                                     _ptr(token_ids), _ptr(row_positions), B, S, float(pad_value), _ptr(logp),
+                                     _ptr(oent), _stream(logits.device)))
+    return logp, oent
+
+
+def tree_logprobs(logits, token_ids, row_positions, pad_value: float = 0.0):
+    """Per-sequence log-probabilities and entropies of a packed batch:
+    ``logits_stats`` then ``gather_logprobs``."""
+    lse, ent = logits_stats(logits)
+    return gather_logprobs(logits, lse, ent, token_ids, row_positions, pad_value)

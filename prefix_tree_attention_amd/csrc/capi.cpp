@@ -160,4 +160,41 @@ int tree_attn_bwd_phase(int32_t phase, const void* q, const void* k, const void*
     return hip_status(e, "tree_attn_bwd");
 }
 
+int tree_logits_stats(const void* logits, int64_t L, int64_t V, int32_t dtype, float* d_lse, float* d_ent,
+                      void* stream) {
+    if (L < 0 || L > (int64_t(1) << 31) - 1 || V <= 0 || V > (int64_t(1) << 31) - 1)
+        return set_error(TREE_E_ARG, "tree_logits_stats: bad shape L=%lld V=%lld", (long long)L, (long long)V);
+    if (dtype != TREE_DTYPE_BF16 && dtype != TREE_DTYPE_FP32)
+        return set_error(TREE_E_ARG, "tree_logits_stats: unknown dtype %d", dtype);
+    if (L == 0) {
+        clear_error();
+        return TREE_OK;
+    }
+    if (!logits || !d_lse || !d_ent) return set_error(TREE_E_ARG, "tree_logits_stats: NULL device pointer");
+    if ((reinterpret_cast<uintptr_t>(logits) & (dtype == TREE_DTYPE_BF16 ? 1u : 3u)) != 0)
+        return set_error(TREE_E_ARG, "tree_logits_stats: logits not aligned to their element size");
+    return hip_status(launch_logits_stats(logits, L, V, dtype, d_lse, d_ent, static_cast<hipStream_t>(stream)),
+                      "tree_logits_stats");
+}
+
+int tree_gather_logprobs(const void* logits, int64_t L, int64_t V, int32_t dtype, const float* d_lse,
+                         const float* d_ent, const int32_t* d_ids, const int32_t* d_row_pos, int64_t B, int64_t S,
+                         float pad_value, float* d_logp, float* d_out_ent, void* stream) {
+    if (L < 0 || L > (int64_t(1) << 31) - 1 || V <= 0 || V > (int64_t(1) << 31) - 1 || B < 0 || S < 0 ||
+        (S > 0 && B > ((int64_t(1) << 40) / S)))
+        return set_error(TREE_E_ARG, "tree_gather_logprobs: bad shape L=%lld V=%lld B=%lld S=%lld", (long long)L,
+                         (long long)V, (long long)B, (long long)S);
+    if (dtype != TREE_DTYPE_BF16 && dtype != TREE_DTYPE_FP32)
+        return set_error(TREE_E_ARG, "tree_gather_logprobs: unknown dtype %d", dtype);
+    if (B * S == 0) {
+        clear_error();
+        return TREE_OK;
+    }
+    if (!d_row_pos || !d_logp || !d_out_ent || (L > 0 && (!logits || !d_lse || !d_ent || !d_ids)))
+        return set_error(TREE_E_ARG, "tree_gather_logprobs: NULL device pointer");
+    return hip_status(launch_gather_logprobs(logits, L, V, dtype, d_lse, d_ent, d_ids, d_row_pos, B, S, pad_value,
+                                             d_logp, d_out_ent, static_cast<hipStream_t>(stream)),
+                      "tree_gather_logprobs");
+}
+
 }  // extern "C"

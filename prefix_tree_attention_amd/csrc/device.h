@@ -113,4 +113,10 @@ hipError_t launch_bwd_f32(int phase, const float* q, const float* k, const float
                           const int32_t* se, const MetaPtrs& mp, float* delta,
                           const AttnShape& sh, hipStream_t stream);
 
+hipError_t launch_logits_stats(const void* logits, int64_t L, int64_t V, int dtype, float* lse, float* ent,
+                               hipStream_t stream);
+hipError_t launch_gather_logprobs(const void* logits, int64_t L, int64_t V, int dtype, const float* lse,
+                                  const float* ent, const int32_t* ids, const int32_t* row_pos, int64_t B, int64_t S,
+                                  float pad_value, float* out_logp, float* out_ent, hipStream_t stream);
+
 }  // namespace treeattn

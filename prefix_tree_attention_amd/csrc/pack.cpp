@@ -251,6 +251,7 @@ void flatten(const RadixTrie& t, const Seqs& S, int64_t L, int32_t pad_id, Packe
 struct tree_pack {
     std::vector<PackedTrie> tries;
     tree_pack_stats_t stats{};
+    int64_t B = 0, S = 0;  // batch shape the pack was built from
 };
 
 extern "C" {
@@ -332,6 +333,8 @@ int tree_pack(const int32_t* ids, const uint8_t* mask, int64_t B, int64_t S,
         p->stats.tree_token_ratio = original ? double(tree_tokens) / double(original) : 0.0;
         p->stats.n_pairs = pairs;
         p->stats.unpacked_pairs = unpacked;
+        p->B = B;
+        p->S = S;
         *out = p.release();
         treeattn::clear_error();
         return TREE_OK;
@@ -389,6 +392,46 @@ int tree_pack_concat(const tree_pack_t* p, int32_t* out_se, int64_t cap, int64_t
             }
             off += x.L;
         }
+    }
+    treeattn::clear_error();
+    return TREE_OK;
+}
+
+int tree_pack_concat_ids(const tree_pack_t* p, int32_t* out_ids, int64_t cap) {
+    if (!p || !out_ids) return treeattn::set_error(TREE_E_ARG, "tree_pack_concat_ids: NULL argument");
+    int64_t total = 0;
+    for (const PackedTrie& x : p->tries) total += x.L;
+    if (cap < total)
+        return treeattn::set_error(TREE_E_ARG, "tree_pack_concat_ids: capacity %lld < %lld", (long long)cap,
+                                   (long long)total);
+    int64_t off = 0;
+    for (const PackedTrie& x : p->tries) {
+        std::copy(x.token_ids.begin(), x.token_ids.end(), out_ids + off);
+        off += x.L;
+    }
+    treeattn::clear_error();
+    return TREE_OK;
+}
+
+int tree_pack_row_positions(const tree_pack_t* p, int32_t* out, int64_t cap) {
+    if (!p || (!out && p->B * p->S > 0))
+        return treeattn::set_error(TREE_E_ARG, "tree_pack_row_positions: NULL argument");
+    if (cap < p->B * p->S)
+        return treeattn::set_error(TREE_E_ARG, "tree_pack_row_positions: capacity %lld < B*S = %lld",
+                                   (long long)cap, (long long)(p->B * p->S));
+    std::fill(out, out + p->B * p->S, -1);
+    int64_t off = 0;
+    for (const PackedTrie& x : p->tries) {
+        // sequence k of the trie is batch row seq_ids[k]; its tokens are the
+        // concatenation of its node intervals, root to leaf
+        for (size_t k = 0; k + 1 < x.seq_iv_ptr.size(); ++k) {
+            int32_t* row = out + int64_t(x.seq_ids[k]) * p->S;
+            int64_t n = 0;
+            for (int32_t iv = x.seq_iv_ptr[k]; iv < x.seq_iv_ptr[k + 1]; ++iv)
+                for (int32_t i = x.seq_iv[size_t(2 * iv)]; i <= x.seq_iv[size_t(2 * iv + 1)]; ++i)
+                    row[n++] = int32_t(off + i);
+        }
+        off += x.L;
     }
     treeattn::clear_error();
     return TREE_OK;

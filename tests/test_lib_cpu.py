@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
     for n in sorted(names):
         assert hasattr(L, n), n
     assert set(_lib.SIGNATURES) == names
-    assert L.tree_abi_version() == 2
+    assert L.tree_abi_version() == 3
 
 
 def _compare(tries_lib, tries_or):
@@ -221,5 +221,57 @@ def test_concat_errors(L):
         assert L.tree_pack_concat(h, buf.ctypes.data, total.value - 1, ctypes.byref(total)) == -5
         assert b"capacity" in L.tree_last_error()
         assert L.tree_pack_concat(h, buf.ctypes.data, total.value, ctypes.byref(total)) == 0
+    finally:
+        L.tree_pack_free(h)
+
+
+def _oracle_rows(to, B, S):
+    """Packed (concatenated) position of each row's k-th token, from the
+    oracle's tries and sequence intervals; -1 after the row's length."""
+    rp = np.full((B, S), -1, np.int64)
+    tok = []
+    off = 0
+    for t in to:
+        for k, row in enumerate(t.seq_ids):
+            pos = t.sequence_indices(k) + off
+            rp[int(row), :len(pos)] = pos
+        tok.append(t.token_ids)
+        off += t.L
+    return rp, np.concatenate(tok)
+
+
+@pytest.mark.parametrize("config", ["1", "2", "3", "4b"])
+def test_row_positions_and_ids_bit_exact(L, config):
+    w = workloads.make_workload(config)
+    se, tok, rp, lengths, _ = pta.pack_batch(w.ids, w.mask, w.max_tokens_per_mb)
+    to = oracle.pack(w.ids, w.mask, w.max_tokens_per_mb)
+    rp_o, tok_o = _oracle_rows(to, *w.ids.shape)
+    assert (rp == rp_o).all() and (tok == tok_o).all() and (se == _oracle_concat(to)).all()
+    # each row's positions hold its own tokens, in order
+    for r in range(w.ids.shape[0]):
+        n = int(w.mask[r].astype(bool).sum())
+        assert (tok[rp[r, :n]] == w.ids[r][w.mask[r].astype(bool)]).all()
+
+
+def test_logprob_entry_points_validate_before_launch(L):
+    p = ctypes.c_void_p(256)
+    assert L.tree_logits_stats(p, 100, 0, 0, p, p, None) == -5          # V
+    assert L.tree_logits_stats(p, 100, 50, 7, p, p, None) == -5         # dtype
+    assert L.tree_logits_stats(None, 100, 50, 0, p, p, None) == -5      # NULL
+    assert L.tree_logits_stats(ctypes.c_void_p(257), 10, 50, 0, p, p, None) == -5  # misaligned bf16
+    assert L.tree_logits_stats(None, 0, 50, 0, None, None, None) == 0   # empty
+    assert L.tree_gather_logprobs(p, 100, 50, 0, p, p, p, p, -1, 4, 0.0, p, p, None) == -5
+    assert L.tree_gather_logprobs(p, 100, 50, 0, p, p, p, None, 2, 4, 0.0, p, p, None) == -5
+    assert L.tree_gather_logprobs(None, 0, 50, 0, None, None, None, None, 0, 4, 0.0, None, None, None) == 0
+    h = ctypes.c_void_p()
+    ids, mask = workloads.worked_example()
+    ids = np.ascontiguousarray(ids, np.int32)
+    mask = np.ascontiguousarray(mask, np.uint8)
+    assert L.tree_pack(ids.ctypes.data, mask.ctypes.data, ids.shape[0], ids.shape[1], 128, 128, 0, 0,
+                       ctypes.byref(h)) == 0
+    try:
+        buf = np.zeros(ids.size, np.int32)
+        assert L.tree_pack_row_positions(h, buf.ctypes.data, ids.size - 1) == -5
+        assert L.tree_pack_concat_ids(h, buf.ctypes.data, 127) == -5
     finally:
         L.tree_pack_free(h)

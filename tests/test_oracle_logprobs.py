@@ -119,3 +119,22 @@ def test_shared_and_duplicate_sequences_agree():
     assert (logp[0, :2] == logp[2, :2]).all() and (ent[0, :3] == ent[2, :3]).all()
     assert logp[0, 2] != logp[2, 2]  # same position, different label
     assert (logp[3] == 0).all()  # one token: nothing to predict
+
+
+def test_minus_inf_logits_are_excluded():
+    # a -inf logit is probability 0: entropy and log-probabilities equal those
+    # of the distribution over the remaining entries (scipy.stats.entropy of
+    # the renormalised table)
+    ids, mask = workloads.worked_example()
+    (trie,) = oracle.pack(ids, mask, 128)
+    V = 12
+    rng = np.random.default_rng(4)
+    lg = rng.normal(size=(trie.L, V))
+    lg[:, 9:] = -np.inf  # ids are 1..8, so every label stays finite
+    logp, ent = oracle.gather_tree_logprobs_entropy([trie], [lg], 3, ids.shape[1])
+    for r, pairs in {0: [(0, 2), (1, 3), (2, 4)], 2: [(0, 7), (6, 8)]}.items():
+        for j, (p, label) in enumerate(pairs):
+            q = np.exp(lg[p, :9] - lg[p, :9].max())
+            q /= q.sum()
+            assert logp[r, j] == pytest.approx(np.log(q[label]), abs=1e-12)
+            assert ent[r, j] == pytest.approx(scipy.stats.entropy(q), abs=1e-12)
