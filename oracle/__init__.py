@@ -51,3 +51,4 @@ from .attention import (  # noqa: F401
     attention_dkdv_cols,
 )
 from .logprobs import gather_tree_logprobs_entropy, prediction_logprob_entropy  # noqa: F401
+from .partition import dfs_order, tree_cost, partition, partition_batch, dummy_tries  # noqa: F401
