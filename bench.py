@@ -21,6 +21,8 @@ convention) and is compared with MI355X's dense bf16 MFMA peak.
                     [--sweep L,b] [--no-cpu-baseline]
     python bench.py --logprobs [--vocab 151936] [--config 4a]   (the
                     tree log-probability gather, its own JSON line)
+    python bench.py --partition K [--config 2]   (the host-side DFS-order
+                    split over K workers, its own JSON line)
 """
 
 from __future__ import annotations
@@ -63,6 +65,8 @@ def parse(argv=None):
     ap.add_argument("--logprobs", action="store_true",
                     help="time the tree log-probability / entropy gather (logits_stats + gather) instead")
     ap.add_argument("--vocab", type=int, default=151936, help="vocabulary size of the --logprobs logits")
+    ap.add_argument("--partition", type=int, default=0,
+                    help="time the DFS-order load-balanced split of the batch over this many workers instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB elementwise copy kernel 3x (HBM counter calibration)")
     return ap.parse_args(argv)
@@ -154,6 +158,8 @@ def main(argv=None):
         return copy_calibration()
     if a.logprobs:
         return bench_logprobs(a)
+    if a.partition:
+        return bench_partition(a)
     import numpy as np
     import torch
     import workloads
@@ -422,6 +428,57 @@ def bench_logprobs(a):
                                             f"would reuse shared rows, so this rate is per packed row"}
     else:
         result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def bench_partition(a):
+    """Host-side DFS-order load-balanced split of one batch over K workers
+    (tree_partition): time per call, the largest per-worker tree (the
+    objective), the tokens the split duplicates relative to one tree, and,
+    for contrast, a structure-blind split: the rows in a seeded random order
+    cut into K runs of balanced token count."""
+    import numpy as np
+    import workloads
+    import prefix_tree_attention_amd as pta
+
+    w = workloads.sweep_workload(*(int(x) for x in a.sweep.split(","))) if a.sweep else workloads.make_workload(a.config)
+    K = int(a.partition)
+    _, one, _ = pta.partition(w.ids, w.mask, 1)
+    for _ in range(max(1, a.warmup)):
+        pta.partition(w.ids, w.mask, K)
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        g, tau, costs = pta.partition(w.ids, w.mask, K)
+    sec = (time.perf_counter() - t0) / a.steps
+    lens = w.mask.astype(bool).sum(1)
+    # structure-blind contrast: rows in a seeded random order (the batch
+    # generators emit prompt groups contiguously, which is not blind), cut
+    # at balanced token counts
+    perm = np.random.default_rng(12345).permutation(len(lens))
+    cum = np.cumsum(lens[perm])
+    blind = np.empty(len(lens), dtype=np.int64)
+    blind[perm] = np.minimum((cum - 1) * K // cum[-1], K - 1)
+    blind_costs = []
+    for j in range(K):
+        rows = np.nonzero(blind == j)[0]
+        if len(rows) == 0:
+            blind_costs.append(0)
+            continue
+        _, c, _ = pta.partition(w.ids[rows], w.mask[rows], 1)
+        blind_costs.append(c)
+    result = {
+        "metric": "DFS-order load-balanced partition: host ms per batch, largest per-worker tree tokens",
+        "value": round(sec * 1e3, 4), "unit": "ms", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "higher_is_better": False, "data": "synthetic",
+        "config": {"workload": w.name, "rows": int(w.ids.shape[0]), "workers": K, "tokens": int(lens.sum())},
+        "single_tree_tokens": one, "max_worker_tree_tokens": tau, "worker_tree_tokens": [int(c) for c in costs],
+        "duplicated_tokens": int(costs.sum() - one), "duplication_bound": int((K - 1) * lens.max()),
+        "balance": round(tau / (one / K), 4),
+        "structure_blind": {"max_worker_tree_tokens": int(max(blind_costs)),
+                            "duplicated_tokens": int(sum(blind_costs) - one),
+                            "balance": round(max(blind_costs) / (one / K), 4)},
+    }
     print(json.dumps(result), flush=True)
     return 0
 

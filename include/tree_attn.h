@@ -155,6 +155,25 @@ int tree_pack_concat_ids(const tree_pack_t* p, int32_t* out_ids, int64_t cap);
  * TREE_E_ARG (NULL argument, cap too small). */
 int tree_pack_row_positions(const tree_pack_t* p, int32_t* out, int64_t cap);
 
+/* Load-balanced split of a batch over K data-parallel workers (AREAL-DTA
+ * notes, §4 负载均衡并行化): the rows' real-token sequences are taken in
+ * lexicographic order (the DFS order of one prefix tree over all of them;
+ * a proper prefix first, equal sequences by row), and cut into at most K
+ * contiguous runs minimising the largest run cost C(T) = tokens of the
+ * run's prefix tree.  The optimum tau is found by binary search between the
+ * longest sequence and the whole tree, each candidate checked by a greedy
+ * scan that starts a new run when the next sequence would exceed it; the
+ * result is that greedy scan at tau, so runs fill from the left and the
+ * last ones may be empty.  Outputs (host memory, caller-owned):
+ * out_group[B] = run of each row; *out_max_cost = tau (if non-NULL);
+ * out_costs[K] = each run's tree tokens (if non-NULL).  Each worker then
+ * packs its rows with tree_pack; workers with fewer tries pad to the
+ * maximum count with empty ones (the guide's DP tree-count sync, 打包数据
+ * 的生成).  Rows may be empty here.  Errors: TREE_E_ARG (K <= 0, bad shape,
+ * NULL input), TREE_E_NOMEM. */
+int tree_partition(const int32_t* ids, const uint8_t* mask, int64_t B, int64_t S, int32_t K, int32_t* out_group,
+                   int64_t* out_max_cost, int64_t* out_costs);
+
 /* Release a pack (NULL is a no-op). */
 void tree_pack_free(tree_pack_t* p);
 

@@ -16,6 +16,7 @@ from .api import (  # noqa: F401
     pack,
     pack_concat,
     pack_batch,
+    partition,
     tree_meta,
     meta_workspace_bytes,
     bwd_workspace_bytes,

@@ -66,6 +66,7 @@ SIGNATURES = {
     "tree_pack_concat": (ctypes.c_int, [c_vp, c_vp, c_i64, ctypes.POINTER(c_i64)]),
     "tree_pack_concat_ids": (ctypes.c_int, [c_vp, c_vp, c_i64]),
     "tree_pack_row_positions": (ctypes.c_int, [c_vp, c_vp, c_i64]),
+    "tree_partition": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_i32, c_vp, ctypes.POINTER(c_i64), c_vp]),
     "tree_pack_free": (None, [c_vp]),
     "tree_meta_workspace_bytes": (c_sz, [c_i64]),
     "tree_meta": (ctypes.c_int, [c_vp, c_i64, c_vp, c_vp, c_vp, c_sz, c_vp]),

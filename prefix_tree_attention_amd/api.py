@@ -151,6 +151,22 @@ def pack_batch(ids, mask, max_tokens_per_mb: int, block_size: int = BLOCK, pad_t
     return se, tok, rp, lengths, stats
 
 
+def partition(ids, mask, K: int):
+    """``tree_partition``: split the batch's rows over K workers in DFS
+    order, minimising the largest per-worker prefix-tree size.  Returns
+    ``(group [B] int32, max_cost, costs [K] int64)``."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    if ids.ndim != 2 or ids.shape != mask.shape:
+        raise TreeAttnError(-5, "ids and mask must both be [B, S]")
+    group = np.empty(ids.shape[0], dtype=np.int32)
+    costs = np.empty(max(int(K), 1), dtype=np.int64)
+    tau = ctypes.c_int64()
+    check(lib().tree_partition(ids.ctypes.data, mask.ctypes.data, ids.shape[0], ids.shape[1], int(K),
+                               group.ctypes.data, ctypes.byref(tau), costs.ctypes.data))
+    return group, int(tau.value), costs
+
+
 # ---------------------------------------------------------------------------
 # device side
 # ---------------------------------------------------------------------------

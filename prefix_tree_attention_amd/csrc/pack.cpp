@@ -437,6 +437,89 @@ int tree_pack_row_positions(const tree_pack_t* p, int32_t* out, int64_t cap) {
     return TREE_OK;
 }
 
+int tree_partition(const int32_t* ids, const uint8_t* mask, int64_t B, int64_t S, int32_t K, int32_t* out_group,
+                   int64_t* out_max_cost, int64_t* out_costs) {
+    using treeattn::set_error;
+    if (K <= 0) return set_error(TREE_E_ARG, "tree_partition: K must be positive (got %d)", K);
+    if (B < 0 || S < 0 || (B > 0 && (!out_group || (S > 0 && (!ids || !mask)))))
+        return set_error(TREE_E_ARG, "tree_partition: bad batch shape or NULL argument");
+    try {
+        // real tokens of each row, in column order
+        std::vector<int64_t> off(size_t(B) + 1, 0);
+        std::vector<int32_t> tok;
+        tok.reserve(size_t(B * S));
+        for (int64_t r = 0; r < B; ++r) {
+            for (int64_t c = 0; c < S; ++c)
+                if (mask[r * S + c]) tok.push_back(ids[r * S + c]);
+            off[size_t(r) + 1] = int64_t(tok.size());
+        }
+        auto len = [&](int64_t r) { return off[size_t(r) + 1] - off[size_t(r)]; };
+        auto at = [&](int64_t r) { return tok.data() + off[size_t(r)]; };
+        // lexicographic (DFS) order, a proper prefix first, ties by row
+        std::vector<int64_t> order(static_cast<size_t>(B));
+        std::iota(order.begin(), order.end(), int64_t(0));
+        std::stable_sort(order.begin(), order.end(), [&](int64_t a, int64_t b) {
+            return std::lexicographical_compare(at(a), at(a) + len(a), at(b), at(b) + len(b));
+        });
+        // tokens each sequence adds to the tree of the sequences before it
+        std::vector<int64_t> add(static_cast<size_t>(B)), full(static_cast<size_t>(B));
+        int64_t lo = 0, hi = 0;
+        for (int64_t i = 0; i < B; ++i) {
+            const int64_t r = order[size_t(i)], n = len(r);
+            int64_t l = 0;
+            if (i > 0) {
+                const int64_t q = order[size_t(i - 1)], m = std::min(n, len(q));
+                const int32_t *x = at(r), *y = at(q);
+                while (l < m && x[l] == y[l]) ++l;
+            }
+            add[size_t(i)] = n - l;
+            full[size_t(i)] = n;
+            lo = std::max(lo, n);
+            hi += n - l;
+        }
+        // greedy check: groups needed under maximum cost tau (a fresh group
+        // costs the sequence's full length)
+        auto groups_for = [&](int64_t tau, int32_t* grp) {
+            int64_t g = -1, cost = 0;
+            for (int64_t i = 0; i < B; ++i) {
+                if (g < 0 || cost + add[size_t(i)] > tau) {
+                    ++g;
+                    cost = full[size_t(i)];
+                } else {
+                    cost += add[size_t(i)];
+                }
+                if (grp) grp[order[size_t(i)]] = int32_t(g);
+            }
+            return g + 1;
+        };
+        if (B > 0) {
+            lo = std::min(lo, hi);
+            while (lo < hi) {
+                const int64_t mid = lo + (hi - lo) / 2;
+                if (groups_for(mid, nullptr) <= K)
+                    hi = mid;
+                else
+                    lo = mid + 1;
+            }
+            groups_for(lo, out_group);
+        }
+        if (out_max_cost) *out_max_cost = B > 0 ? lo : 0;
+        if (out_costs) {
+            std::fill(out_costs, out_costs + K, int64_t(0));
+            int64_t pg = -1;
+            for (int64_t i = 0; i < B; ++i) {
+                const int64_t g = out_group[order[size_t(i)]];
+                out_costs[g] += (g == pg) ? add[size_t(i)] : full[size_t(i)];
+                pg = g;
+            }
+        }
+        treeattn::clear_error();
+        return TREE_OK;
+    } catch (const std::bad_alloc&) {
+        return set_error(TREE_E_NOMEM, "tree_partition: out of host memory");
+    }
+}
+
 void tree_pack_free(tree_pack_t* p) { delete p; }
 
 }  // extern "C"

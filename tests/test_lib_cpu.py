@@ -275,3 +275,45 @@ def test_logprob_entry_points_validate_before_launch(L):
         assert L.tree_pack_concat_ids(h, buf.ctypes.data, 127) == -5
     finally:
         L.tree_pack_free(h)
+
+
+@pytest.mark.parametrize("config", ["1", "2", "3", "4a", "4b"])
+@pytest.mark.parametrize("K", [1, 2, 3, 8])
+def test_partition_bit_exact(L, config, K):
+    w = workloads.make_workload(config)
+    g, tau, costs = pta.partition(w.ids, w.mask, K)
+    go, tauo = oracle.partition_batch(w.ids, w.mask, K)
+    assert (g == go).all() and tau == tauo
+    seqs = oracle.extract_sequences(w.ids, w.mask)
+    for j in range(K):
+        assert costs[j] == oracle.tree_cost([s for s, x in zip(seqs, g) if x == j])
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_partition_random_bit_exact(L, seed):
+    rng = np.random.default_rng(7000 + seed)
+    n_seq = int(rng.integers(1, 40))
+    vocab = int(rng.choice([2, 3, 7]))
+    seqs = []
+    for _ in range(n_seq):
+        if seqs and rng.random() < 0.6:
+            base = seqs[int(rng.integers(len(seqs)))]
+            cut = int(rng.integers(0, len(base) + 1))
+            s = np.concatenate([base[:cut], rng.integers(0, vocab, int(rng.integers(0 if cut else 1, 30)))])
+        else:
+            s = rng.integers(0, vocab, int(rng.integers(1, 40)))
+        seqs.append(s.astype(np.int32))
+    ids, mask = workloads.pad_rows(seqs)
+    K = int(rng.integers(1, 10))
+    g, tau, costs = pta.partition(ids, mask, K)
+    go, tauo = oracle.partition_batch(ids, mask, K)
+    assert (g == go).all() and tau == tauo
+
+
+def test_partition_errors(L):
+    ids, mask = workloads.worked_example()
+    with pytest.raises(pta.TreeAttnError) as e:
+        pta.partition(ids, mask, 0)
+    assert e.value.code == -5
+    g, tau, costs = pta.partition(ids, mask, 5)  # more workers than rows
+    assert tau == 4 and g.tolist() == [0, 1, 2] and costs.tolist() == [4, 4, 3, 0, 0]  # one row per worker
