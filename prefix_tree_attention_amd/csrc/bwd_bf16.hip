@@ -208,16 +208,21 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
 
     // The pair's nonempty query blocks are the contiguous range from its
     // first block with a real token to hi / 128 (each column is a range
-    // starting at its own block).  A 64-query step is full (no mask) when
-    // every key precedes every query and every query ends inside every
-    // key's subtree.
+    // starting at its own block).  A 32-query half is full (no mask) for
+    // this wave when every one of its 64 keys precedes every query of the
+    // half and every query ends inside every key's subtree: a test on the
+    // wave's last key and smallest subtree end (pads count -1, so a wave
+    // holding one always masks).
     const int hi0 = blk_max[kb0], hi1 = has1 ? blk_max[kb1] : -1;
     const int hi = max(hi0, hi1);
-    const int lo = has1 ? min(blk_min[kb0], blk_min[kb1]) : blk_min[kb0];
     const int qhi = hi >= 0 ? min(nb - 1, hi / kBlock) : -1;
     const int qlo = hi0 >= 0 ? kb0 : kb1;
     const int nsteps = (qhi >= qlo ? qhi - qlo + 1 : 0) * 2 * G;
-    const int kmax = kb0 * kBlock + 2 * kBlock - 1;
+    const int kmax_w = kb0 * kBlock + 64 * wave + 63;
+    int lo_w = min(sek[0], sek[1]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) lo_w = min(lo_w, __shfl_xor(lo_w, o));
+    lo_w = __builtin_amdgcn_readfirstlane(lo_w);
     const int qs32 = int(q_stride);
     auto qtile = [&](int buf) { return smem + buf * kStage; };
     auto gtile = [&](int buf) { return smem + buf * kStage + T::kBytes; };
@@ -269,7 +274,6 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
     for (int st = 0; st < nsteps; ++st) {
         const int buf = st & 1;
         const int qbase = cur.qbase;
-        const bool partial = !(qbase >= kmax && qbase + kStep - 1 <= lo);
         advance(cur);
         if (st + 1 < nsteps) {
             issue(nxt, buf ^ 1);
@@ -343,7 +347,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
                     }
                 }
             };
-            if (partial)
+            const int q0c = qbase + 32 * c;
+            if (!(q0c >= kmax_w && q0c + 31 <= lo_w))
                 elementwise(std::true_type{});
             else
                 elementwise(std::false_type{});
