@@ -23,6 +23,8 @@ convention) and is compared with MI355X's dense bf16 MFMA peak.
                     tree log-probability gather, its own JSON line)
     python bench.py --partition K [--config 2]   (the host-side DFS-order
                     split over K workers, its own JSON line)
+    python bench.py --rope [--config 4a]   (rotary embedding of Q and K by
+                    tree position ids, its own JSON line)
 """
 
 from __future__ import annotations
@@ -67,6 +69,8 @@ def parse(argv=None):
     ap.add_argument("--vocab", type=int, default=151936, help="vocabulary size of the --logprobs logits")
     ap.add_argument("--partition", type=int, default=0,
                     help="time the DFS-order load-balanced split of the batch over this many workers instead")
+    ap.add_argument("--rope", action="store_true",
+                    help="time the rotary embedding of Q and K by tree position ids instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB elementwise copy kernel 3x (HBM counter calibration)")
     return ap.parse_args(argv)
@@ -160,6 +164,8 @@ def main(argv=None):
         return bench_logprobs(a)
     if a.partition:
         return bench_partition(a)
+    if a.rope:
+        return bench_rope(a)
     import numpy as np
     import torch
     import workloads
@@ -479,6 +485,68 @@ def bench_partition(a):
                             "duplicated_tokens": int(sum(blind_costs) - one),
                             "balance": round(max(blind_costs) / (one / K), 4)},
     }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def bench_rope(a):
+    """Rotary embedding of the step's Q [L, Hq, D] and K [L, Hkv, D] (bf16,
+    resident) by the tree position ids of tree_meta: one tree_rope per
+    tensor, timed with HIP events; HBM-bound, algorithmic traffic = each
+    tensor read and written once."""
+    import numpy as np
+    import torch
+    import workloads
+    import prefix_tree_attention_amd as pta
+
+    w = workloads.sweep_workload(*(int(x) for x in a.sweep.split(","))) if a.sweep else workloads.make_workload(a.config)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    se, _, _, _, _ = pta.pack_batch(w.ids, w.mask, w.max_tokens_per_mb)
+    L = len(se)
+    meta = pta.tree_meta(se)
+    q, k, _, _ = workloads.attention_inputs(L, w.hq, w.hkv, w.d, "bf16", w.qkv_std, 77)
+    q, k = q.to(dev), k.to(dev)
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+    for _ in range(a.warmup):
+        pta.rope(q, meta.pos, 1e6, out=qo)
+        pta.rope(k, meta.pos, 1e6, out=ko)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        pta.rope(q, meta.pos, 1e6, out=qo)
+        pta.rope(k, meta.pos, 1e6, out=ko)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / a.steps
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / a.steps
+    alg = 2.0 * 2 * L * (w.hq + w.hkv) * w.d
+    achieved = alg / (ms * 1e-3) / 1e9
+    result = {
+        "metric": "rotary embedding of Q and K by tree position ids: tokens/s and HBM GB/s",
+        "value": round(L / sec, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(sec * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic", "kernel_ms_per_step": round(ms, 4),
+        "config": {"workload": w.name, "L": L, "hq": w.hq, "hkv": w.hkv, "head_dim": w.d, "base": 1e6},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "kernel": "rope_kernel", "traffic": None},
+    }
+    if not a.no_cpu_baseline:
+        import oracle
+        n = min(L, 4096)
+        pos = meta.pos[:n].cpu().numpy()
+        qs, ks = q[:n].float().cpu().numpy(), k[:n].float().cpu().numpy()
+        t1 = time.perf_counter()
+        oracle.rope(qs, pos, 1e6)
+        oracle.rope(ks, pos, 1e6)
+        dt = time.perf_counter() - t1
+        result["cpu_baseline"] = {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"the first {n} tokens of Q and K, float64 numpy ({dt:.2f} s)"}
+    else:
+        result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
     return 0
 

@@ -287,6 +287,25 @@ int tree_gather_logprobs(const void* logits, int64_t L, int64_t V, int32_t dtype
                          const float* d_ent, const int32_t* d_ids, const int32_t* d_row_pos, int64_t B,
                          int64_t S, float pad_value, float* d_logp, float* d_out_ent, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Rotary position embedding by tree position ids (device).  Guide, section
+ * 打包数据的生成: position ids are ancestor counts minus one (tree_meta's
+ * d_pos), so a shared prefix carries the same positional encoding in every
+ * sequence through it; they feed the model's rotary embedding.  The pages do
+ * not spell the rotation out; this is the half-split form of the Qwen/Llama
+ * models they train: for head vectors x [L, H, D] (D even), position
+ * p = d_pos[i], f_j = base^(-2j/D), a_j = p f_j,
+ *   y[i,h,j]       = x[i,h,j] cos a_j - x[i,h,j+D/2] sin a_j,
+ *   y[i,h,j+D/2]   = x[i,h,j+D/2] cos a_j + x[i,h,j] sin a_j,
+ * j < D/2; with inverse != 0 the rotation is by -a_j, which is also the
+ * gradient map (dx = inverse rotation of dy).  Angles, sines and cosines are
+ * formed in float64, the rotation in float32; dtype TREE_DTYPE_BF16 or
+ * TREE_DTYPE_FP32 for both x and y.  y may equal x (in place).  L = 0 is a
+ * no-op.  Errors: TREE_E_ARG (NULL pointer, odd or bad D, H, L, base <= 1
+ * or not finite, dtype, misalignment), TREE_E_HIP. */
+int tree_rope(const void* x, void* y, const int32_t* d_pos, int64_t L, int32_t H, int32_t D, double base,
+              int32_t inverse, int32_t dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,4 +27,6 @@ from .api import (  # noqa: F401
     logits_stats,
     gather_logprobs,
     tree_logprobs,
+    rope,
+    tree_rope,
 )

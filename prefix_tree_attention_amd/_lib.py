@@ -80,6 +80,7 @@ SIGNATURES = {
     "tree_logits_stats": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp]),
     "tree_gather_logprobs": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_f32,
                                             c_vp, c_vp, c_vp]),
+    "tree_rope": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i32, c_i32, ctypes.c_double, c_i32, c_i32, c_vp]),
 }
 BWD_ALL, BWD_DELTA, BWD_DKDV, BWD_DQ = 0, 1, 2, 3
 

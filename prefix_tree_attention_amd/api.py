@@ -370,3 +370,48 @@ def tree_logprobs(logits, token_ids, row_positions, pad_value: float = 0.0):
     ``logits_stats`` then ``gather_logprobs``."""
     lse, ent = logits_stats(logits)
     return gather_logprobs(logits, lse, ent, token_ids, row_positions, pad_value)
+
+
+# ---------------------------------------------------------------------------
+# rotary embedding by tree position ids
+# ---------------------------------------------------------------------------
+def rope(x, pos, base: float = 1e6, inverse: bool = False, out=None):
+    """``tree_rope``: rotate head vectors x [L, H, D] by the tree position
+    ids ``pos`` [L] (int32 device, e.g. ``tree_meta(...).pos``); in place
+    when ``out is x``.  ``inverse`` rotates back (the gradient map)."""
+    torch = _torch()
+    if not x.is_cuda or not x.is_contiguous() or x.dim() != 3:
+        raise TreeAttnError(-5, "x must be a contiguous device tensor [L, H, D]")
+    if not pos.is_cuda or pos.dtype != torch.int32 or pos.numel() != x.shape[0] or not pos.is_contiguous():
+        raise TreeAttnError(-5, "pos must be a contiguous int32 device tensor [L]")
+    y = torch.empty_like(x) if out is None else out
+    if y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous():
+        raise TreeAttnError(-5, "out must match x")
+    L, H, D = x.shape
+    check(lib().tree_rope(_ptr(x), _ptr(y), _ptr(pos), L, H, D, float(base), int(bool(inverse)), _dtype_code(x),
+                          _stream(x.device)))
+    return y
+
+
+def _rope_fn():
+    torch = _torch()
+
+    class _Rope(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x, pos, base):
+            ctx.save_for_backward(pos)
+            ctx.base = base
+            return rope(x.contiguous(), pos, base)
+
+        @staticmethod
+        def backward(ctx, gy):
+            (pos,) = ctx.saved_tensors
+            return rope(gy.contiguous(), pos, ctx.base, inverse=True), None, None
+
+    return _Rope
+
+
+def tree_rope(x, pos, base: float = 1e6):
+    """Differentiable rotary embedding by tree position ids (the backward is
+    the inverse rotation of the incoming gradient)."""
+    return _rope_fn().apply(x, pos, base)

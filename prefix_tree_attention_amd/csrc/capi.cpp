@@ -197,4 +197,24 @@ int tree_gather_logprobs(const void* logits, int64_t L, int64_t V, int32_t dtype
                       "tree_gather_logprobs");
 }
 
+int tree_rope(const void* x, void* y, const int32_t* d_pos, int64_t L, int32_t H, int32_t D, double base,
+              int32_t inverse, int32_t dtype, void* stream) {
+    if (L < 0 || L > (int64_t(1) << 31) - 1 || H <= 0 || D <= 0 || D % 2 != 0 || D > 4096 ||
+        int64_t(H) * D > (int64_t(1) << 20))
+        return set_error(TREE_E_ARG, "tree_rope: bad shape L=%lld H=%d D=%d (D even)", (long long)L, H, D);
+    if (!std::isfinite(base) || !(base > 1.0)) return set_error(TREE_E_ARG, "tree_rope: base must be finite and > 1");
+    if (dtype != TREE_DTYPE_BF16 && dtype != TREE_DTYPE_FP32)
+        return set_error(TREE_E_ARG, "tree_rope: unknown dtype %d", dtype);
+    if (L == 0) {
+        clear_error();
+        return TREE_OK;
+    }
+    if (!x || !y || !d_pos) return set_error(TREE_E_ARG, "tree_rope: NULL device pointer");
+    const uintptr_t al = dtype == TREE_DTYPE_BF16 ? 1u : 3u;
+    if ((reinterpret_cast<uintptr_t>(x) & al) || (reinterpret_cast<uintptr_t>(y) & al))
+        return set_error(TREE_E_ARG, "tree_rope: tensors not aligned to their element size");
+    return hip_status(launch_rope(x, y, d_pos, L, H, D, base, inverse ? 1 : 0, dtype, static_cast<hipStream_t>(stream)),
+                      "tree_rope");
+}
+
 }  // extern "C"

@@ -119,4 +119,7 @@ hipError_t launch_gather_logprobs(const void* logits, int64_t L, int64_t V, int 
                                   const float* ent, const int32_t* ids, const int32_t* row_pos, int64_t B, int64_t S,
                                   float pad_value, float* out_logp, float* out_ent, hipStream_t stream);
 
+hipError_t launch_rope(const void* x, void* y, const int32_t* pos, int64_t L, int H, int D, double base, int inverse,
+                       int dtype, hipStream_t stream);
+
 }  // namespace treeattn
