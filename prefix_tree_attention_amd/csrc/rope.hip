@@ -5,11 +5,12 @@
 // f_j = base^(-2j/D) and a_j = pos f_j, the pair (x_j, x_{j+D/2}) is rotated
 // by a_j (by -a_j for the inverse, which is also the gradient map).
 //
-// One lane per (token, pair j): the angle and its sine / cosine are formed
-// in float64 (exact to float32 rounding at any position), then applied to
-// that pair of every head.  Lanes of one token read and write the two
-// contiguous halves of each head vector, so the pass is one coalesced read
-// and write of x: HBM-bound.
+// One lane per (token, pair j) -- or per 16 bytes of pairs when the head
+// size allows: the angle and its sine / cosine are formed in float64 (exact
+// to float32 rounding at any position), then applied to those pairs of
+// every head.  Lanes of one token read and write the two contiguous halves
+// of each head vector, so the pass is one coalesced read and write of x:
+// HBM-bound.
 
 #include "device.h"
 #include "mfma.h"
@@ -45,13 +46,89 @@ __global__ __launch_bounds__(256) void rope_kernel(const T* x, T* y,  // may ali
     }
 }
 
+// Same rotation, 16 bytes per access: a lane takes N = 16 / sizeof(T)
+// consecutive pairs j0 .. j0 + N - 1 (D / 2 a multiple of N), so each head's
+// two halves move as one 16-byte load and store per lane.
+template <typename T>
+__global__ __launch_bounds__(256) void rope_vec_kernel(const T* x, T* y,  // may alias (in place)
+                                                       const int32_t* __restrict__ pos, int64_t L, int H, int D,
+                                                       double log2_base, int inverse) {
+    constexpr int N = 16 / sizeof(T);
+    const int half = D / 2, lanes = half / N;
+    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= L * lanes) return;
+    const int64_t i = idx / lanes;
+    const int j0 = int(idx % lanes) * N;
+    const double p = double(pos[i]);
+    float c[N], sn[N];
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+        double sd, cd;
+        sincos(p * exp2(-2.0 * double(j0 + u) / double(D) * log2_base), &sd, &cd);
+        c[u] = float(cd);
+        sn[u] = inverse ? -float(sd) : float(sd);
+    }
+    typedef T vec __attribute__((ext_vector_type(N)));
+    auto rot = [&](const vec& a, const vec& b, vec& ya, vec& yb) {
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+            const float x1 = to_f(a[u]), x2 = to_f(b[u]);
+            ya[u] = from_f<T>(__builtin_fmaf(x1, c[u], -x2 * sn[u]));
+            yb[u] = from_f<T>(__builtin_fmaf(x2, c[u], x1 * sn[u]));
+        }
+    };
+    // x and y may be one tensor, so the compiler cannot move a head's loads
+    // above the previous head's stores; heads never overlap, so four are
+    // loaded explicitly before any of them is stored
+    constexpr int kH = 4;
+    int h = 0;
+    for (; h + kH <= H; h += kH) {
+        vec a[kH], b[kH];
+#pragma unroll
+        for (int u = 0; u < kH; ++u) {
+            const int64_t o = (i * H + h + u) * D + j0;
+            a[u] = *reinterpret_cast<const vec*>(x + o);
+            b[u] = *reinterpret_cast<const vec*>(x + o + half);
+        }
+#pragma unroll
+        for (int u = 0; u < kH; ++u) {
+            const int64_t o = (i * H + h + u) * D + j0;
+            vec ya, yb;
+            rot(a[u], b[u], ya, yb);
+            *reinterpret_cast<vec*>(y + o) = ya;
+            *reinterpret_cast<vec*>(y + o + half) = yb;
+        }
+    }
+    for (; h < H; ++h) {
+        const int64_t o = (i * H + h) * D + j0;
+        vec ya, yb;
+        rot(*reinterpret_cast<const vec*>(x + o), *reinterpret_cast<const vec*>(x + o + half), ya, yb);
+        *reinterpret_cast<vec*>(y + o) = ya;
+        *reinterpret_cast<vec*>(y + o + half) = yb;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_rope(const void* x, void* y, const int32_t* pos, int64_t L, int H, int D, double base, int inverse,
                        int dtype, hipStream_t stream) {
+    const double l2b = log2(base);
+    const int elem = dtype == 0 ? 2 : 4, N = 16 / elem;
+    const bool vec = (D / 2) % N == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(y) & 15) == 0;
+    if (vec) {
+        const int64_t n = L * ((D / 2) / N);
+        const unsigned grid = unsigned((n + 255) / 256);
+        if (dtype == 0)
+            rope_vec_kernel<bf16><<<grid, 256, 0, stream>>>(static_cast<const bf16*>(x), static_cast<bf16*>(y), pos, L,
+                                                            H, D, l2b, inverse);
+        else
+            rope_vec_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(x), static_cast<float*>(y), pos,
+                                                             L, H, D, l2b, inverse);
+        return hipGetLastError();
+    }
     const int64_t n = L * (D / 2);
     const unsigned grid = unsigned((n + 255) / 256);
-    const double l2b = log2(base);
     if (dtype == 0)
         rope_kernel<bf16><<<grid, 256, 0, stream>>>(static_cast<const bf16*>(x), static_cast<bf16*>(y), pos, L, H, D,
                                                     l2b, inverse);
