@@ -208,11 +208,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
 
     // The pair's nonempty query blocks are the contiguous range from its
     // first block with a real token to hi / 128 (each column is a range
-    // starting at its own block).  A 32-query half is full (no mask) for
-    // this wave when every one of its 64 keys precedes every query of the
-    // half and every query ends inside every key's subtree: a test on the
-    // wave's last key and smallest subtree end (pads count -1, so a wave
-    // holding one always masks).
+    // starting at its own block).
     const int hi0 = blk_max[kb0], hi1 = has1 ? blk_max[kb1] : -1;
     const int hi = max(hi0, hi1);
     const int qhi = hi >= 0 ? min(nb - 1, hi / kBlock) : -1;
@@ -271,6 +267,14 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
     wait_vm_all();
     __syncthreads();
 
+    // One step is 64 queries in two halves of 32.  Per half the MFMA stream
+    // is S (NX), dP (NX), then dV/dK (8 NT); the exponentials run between
+    // the dP MFMAs, and dS of the half's second 16 queries between the first
+    // gradient MFMAs, so the matrix core keeps work queued while the vector
+    // unit runs (one wave per SIMD hides nothing by itself).  Scheduling
+    // barriers pin that order; each group issues the LDS reads of the group
+    // two ahead.
+#define TREEATTN_SCHED() __builtin_amdgcn_sched_barrier(0)
     for (int st = 0; st < nsteps; ++st) {
         const int buf = st & 1;
         const int qbase = cur.qbase;
@@ -283,116 +287,209 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
         const lds_char* gt = gtile(buf);
         const lds_char* lsp = lsev(buf);
         const lds_char* dlp = dlv(buf);
-        auto lds_f32x4 = [](const lds_char* p) {
-            return *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(p);
+        const lds_char* kt = ktile + 64 * wave * T::kRowBytes;
+
+        struct SOps {
+            bf16x8 aq, k0, k1;
         };
+        struct TOps {
+            bf16x8 ag, aq;
+        };
+        // k-step x of S: Q rows of the half and the wave's two 32-key K blocks
+        auto rd_s = [&](int c, int x) {
+            const int ro = roff(x);
+            return SOps{T::frag_at(qt + 32 * c * T::kRowBytes, ro), T::frag_at(kt, ro),
+                        T::frag_at(kt + 32 * T::kRowBytes, ro)};
+        };
+        // k-step x of dP: dO rows of the half
+        auto rd_g = [&](int c, int x) { return T::frag_at(gt + 32 * c * T::kRowBytes, roff(x)); };
+        // d-block t, k-step m of the gradients: dO^T and Q^T, rows
+        // 32 c + 16 m + 4 h + {0..3, 8..11} (a 16-row move keeps the swizzle
+        // phase, so it is a plain offset)
+        auto rd_t = [&](int c, int t, int m) {
+            const int rb = (32 * c + 16 * m) * T::kRowBytes;
+            const int o0 = toff(t, 0), o1 = toff(t, 1);
+            return TOps{join_tr(T::tr_at(gt + rb, o0), T::tr_at(gt + rb, o1)),
+                        join_tr(T::tr_at(qt + rb, o0), T::tr_at(qt + rb, o1))};
+        };
+        // S starts at -LSE / scale and dP at -Delta, so they leave
+        // S - LSE / scale and dP - Delta; register r of a score accumulator
+        // holds query 32 c + 8 (r / 4) + 4 h + r % 4 against key 32 kk + j32
+        auto rd_init = [&](int c, f32x16& nl, f32x16& nd) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 a = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+                    lsp + 4 * (32 * c + 8 * j + 4 * h));
+                const f32x4 b = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+                    dlp + 4 * (32 * c + 8 * j + 4 * h));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    nl[4 * j + i] = a[i];
+                    nd[4 * j + i] = b[i];
+                }
+            }
+        };
+        auto cvt8 = [](const f32x16& s, int m) {
+            return to_bf16x8(f32x4{s[8 * m], s[8 * m + 1], s[8 * m + 2], s[8 * m + 3]},
+                             f32x4{s[8 * m + 4], s[8 * m + 5], s[8 * m + 6], s[8 * m + 7]});
+        };
+
+        constexpr int kExp = 32 / NX;     // exponentials per dP k-step
+        constexpr int kDs = 16 / NT / 2;  // dS products per gradient MFMA pair
         // opaque per step, so the offsets are formed at each use rather than
         // hoisted out of the loop into one register each
         asm volatile("" : "+v"(ru), "+v"(rbase), "+v"(tx[0]), "+v"(tx[1]), "+v"(tbase[0]), "+v"(tbase[1]));
-
-        // Two halves of 32 queries.  In half c, register r of a score
-        // accumulator holds query 32 c + 8 (r / 4) + 4 h + r % 4 against
-        // key 32 kk + j32 of this wave.
+        f32x16 nl, nd;
+        SOps so[NX];
+        rd_init(0, nl, nd);
+        so[0] = rd_s(0, 0);
+        so[1] = rd_s(0, 1);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            // S starts at -LSE / scale and dP at -Delta, so they leave
-            // S - LSE / scale and dP - Delta
             f32x16 sc[2], dp[2];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const f32x4 nls = lds_f32x4(lsp + 4 * (32 * c + 8 * j + 4 * h));
-                const f32x4 ndl = lds_f32x4(dlp + 4 * (32 * c + 8 * j + 4 * h));
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) {
-                        sc[kk][4 * j + i] = nls[i];
-                        dp[kk][4 * j + i] = ndl[i];
-                    }
-            }
+            bf16x8 ag[NX], pb[2][2], db[2][2];
+            TOps tr[2][NT];
+            TREEATTN_SCHED();
+            // S = Q K^T
 #pragma unroll
             for (int x = 0; x < NX; ++x) {
-                const int ro = roff(x);
-                const bf16x8 aq = T::frag_at(qt + 32 * c * T::kRowBytes, ro);
-                const bf16x8 ag = T::frag_at(gt + 32 * c * T::kRowBytes, ro);
+                if (x + 2 < NX)
+                    so[x + 2] = rd_s(c, x + 2);
+                else
+                    ag[x + 2 - NX] = rd_g(c, x + 2 - NX);
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const bf16x8 kf = T::frag_at(ktile + (64 * wave + 32 * kk) * T::kRowBytes, ro);
-                    sc[kk] = mfma32x32x16(aq, kf, sc[kk]);
-                    dp[kk] = mfma32x32x16(ag, vf[kk][x], dp[kk]);
-                }
+                for (int kk = 0; kk < 2; ++kk)
+                    sc[kk] = mfma32x32x16(so[x].aq, kk ? so[x].k1 : so[x].k0, x == 0 ? nl : sc[kk]);
+                TREEATTN_SCHED();
             }
-            // P = exp2(scale log2e (S - LSE / scale)), dS = P (dP - Delta);
-            // the subtree-interval predicate only in partial steps
-            auto elementwise = [&](auto masked) {
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    // register r is query q0 + o_r with o_r = 8 (r / 4) + r % 4;
-                    // key <= q <= se[key]  <=>  key - q0 <= o_r <= se[key] - q0
-                    int lo_k = 0, hi_k = 0;
-                    if constexpr (decltype(masked)::value) {
-                        const int q0 = qbase + 32 * c + 4 * h;
-                        lo_k = key[kk] - q0;
-                        hi_k = sek[kk] - q0;
-                    }
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float p = fast_exp2(sc[kk][r] * scale_log2);
-                        if constexpr (decltype(masked)::value) {
-                            const int o = 8 * (r / 4) + r % 4;
-                            p = (lo_k <= o && o <= hi_k) ? p : 0.f;
-                        }
-                        sc[kk][r] = p;
-                        dp[kk][r] = p * dp[kk][r];
-                    }
-                }
-            };
-            const int q0c = qbase + 32 * c;
-            if (!(q0c >= kmax_w && q0c + 31 <= lo_w))
-                elementwise(std::true_type{});
-            else
-                elementwise(std::false_type{});
-            // B operands of the gradient products, k-step m = queries
-            // 32 c + 16 m + {4 h + 0..3, 8 + 4 h + 0..3}
-            bf16x8 pb[2][2], db[2][2];
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    const f32x16& s = sc[kk];
-                    const f32x16& d = dp[kk];
-                    pb[kk][m] = to_bf16x8(f32x4{s[8 * m], s[8 * m + 1], s[8 * m + 2], s[8 * m + 3]},
-                                          f32x4{s[8 * m + 4], s[8 * m + 5], s[8 * m + 6], s[8 * m + 7]});
-                    db[kk][m] = to_bf16x8(f32x4{d[8 * m], d[8 * m + 1], d[8 * m + 2], d[8 * m + 3]},
-                                          f32x4{d[8 * m + 4], d[8 * m + 5], d[8 * m + 6], d[8 * m + 7]});
-                }
-            // the conversions above are VALU writes that the asm MFMAs read
-            asm("s_nop 1"
-                         : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]), "+v"(db[0][0]),
-                           "+v"(db[0][1]), "+v"(db[1][0]), "+v"(db[1][1]));
-            // dV^T += dO^T P, dK^T += Q^T dS: A = 32 d x 16 queries read
-            // transposed from the row-major tiles, in the same k order
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-#pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    // rows 32 c + 16 m + 4 h + {0..3, 8..11}: the 16-row
-                    // shift keeps the swizzle phase, so it is a plain offset
-                    const int rb = (32 * c + 16 * m) * T::kRowBytes;
-                    const int o0 = toff(t, 0), o1 = toff(t, 1);
-                    const bf16x8 ag = join_tr(T::tr_at(gt + rb, o0), T::tr_at(gt + rb, o1));
-                    const bf16x8 aq = join_tr(T::tr_at(qt + rb, o0), T::tr_at(qt + rb, o1));
+            // dP = dO V^T, with P = exp2(scale log2e (S - LSE / scale)) of
+            // 32 / NX scores after each k-step; the subtree-interval
+            // predicate only where the half is partial for this wave:
+            // register r is query q0 + o_r, o_r = 8 (r / 4) + r % 4, and
+            // key <= q <= se[key]  <=>  key - q0 <= o_r <= se[key] - q0
+            auto dp_exp = [&](auto masked_t) {
+                constexpr bool kMasked = decltype(masked_t)::value;
+                // Opaque and different in the two variants, so the common
+                // work (reads, scaling, conversions) stays inside each rather
+                // than being hoisted above the branch or sunk below it, out
+                // of reach of the dP MFMAs.
+                float sl = scale_log2;
+                if constexpr (kMasked)
+                    asm volatile("; partial half" : "+v"(ru), "+v"(rbase), "+v"(tx[0]), "+v"(tx[1]),
+                                 "+v"(tbase[0]), "+v"(tbase[1]), "+s"(sl));
+                else
+                    asm volatile("; full half" : "+v"(ru), "+v"(rbase), "+v"(tx[0]), "+v"(tx[1]), "+v"(tbase[0]),
+                                 "+v"(tbase[1]), "+s"(sl));
+                TREEATTN_SCHED();
+                int lo_k[2] = {0, 0}, hi_k[2] = {0, 0};
+                if constexpr (kMasked) {
+                    const int q0 = qbase + 32 * c + 4 * h;
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk) {
-                        mfma32_agpr(dv[kk][t], ag, pb[kk][m]);
-                        mfma32_agpr(dk[kk][t], aq, db[kk][m]);
+                        lo_k[kk] = key[kk] - q0;
+                        hi_k[kk] = sek[kk] - q0;
                     }
                 }
+                auto ex = [&](int e) {
+                    const int kk = e >> 4, r = e & 15;
+                    float p = fast_exp2(sc[kk][r] * sl);
+                    if constexpr (kMasked) {
+                        const int o = 8 * (r / 4) + r % 4;
+                        p = (lo_k[kk] <= o && o <= hi_k[kk]) ? p : 0.f;
+                    }
+                    sc[kk][r] = p;
+                    if ((e & 7) == 7) pb[kk][(e >> 3) & 1] = cvt8(sc[kk], (e >> 3) & 1);
+                };
+#pragma unroll
+                for (int x = 0; x < NX; ++x) {
+                    if (x + 2 < NX)
+                        ag[x + 2] = rd_g(c, x + 2);
+                    else
+                        tr[0][x + 2 - NX] = rd_t(c, x + 2 - NX, 0);
+                    dp[0] = mfma32x32x16(ag[x], vf[0][x], x == 0 ? nd : dp[0]);
+#pragma unroll
+                    for (int e = 0; e < kExp / 2; ++e) ex(kExp * x + e);
+                    dp[1] = mfma32x32x16(ag[x], vf[1][x], x == 0 ? nd : dp[1]);
+#pragma unroll
+                    for (int e = kExp / 2; e < kExp; ++e) ex(kExp * x + e);
+                    TREEATTN_SCHED();
+                }
+                if constexpr (kMasked)
+                    asm volatile("; partial half end" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]));
+                else
+                    asm volatile("; full half end" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]));
+            };
+            // A half is full (no mask) for this wave when every one of its 64
+            // keys precedes every query of the half and every query ends
+            // inside every key's subtree: a test on the wave's last key and
+            // smallest subtree end (pads count -1, so a wave holding one
+            // always masks).
+            const int q0c = qbase + 32 * c;
+            if (q0c >= kmax_w && q0c + 31 <= lo_w)
+                dp_exp(std::false_type{});
+            else
+                dp_exp(std::true_type{});
+            // dS = P (dP - Delta) of k-step 0 (queries 32 c + 0..15)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) dp[kk][r] *= sc[kk][r];
+                db[kk][0] = cvt8(dp[kk], 0);
+            }
+            // the conversions are VALU writes that the asm MFMAs read
+            asm("s_nop 1"
+                : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]), "+v"(db[0][0]), "+v"(db[1][0]));
+            TREEATTN_SCHED();
+            // dV^T += dO^T P, dK^T += Q^T dS, k-step 0, with dS of k-step 1
+            // in between
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                if (t + 2 < NT)
+                    tr[0][t + 2] = rd_t(c, t + 2, 0);
+                else
+                    tr[1][t + 2 - NT] = rd_t(c, t + 2 - NT, 1);
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    mfma32_agpr(dv[kk][t], tr[0][t].ag, pb[kk][0]);
+                    mfma32_agpr(dk[kk][t], tr[0][t].aq, db[kk][0]);
+#pragma unroll
+                    for (int i = 0; i < kDs; ++i) {
+                        const int e = (2 * t + kk) * kDs + i;  // 0..15
+                        const int k2 = e >> 3, r = 8 + (e & 7);
+                        dp[k2][r] *= sc[k2][r];
+                        if ((e & 7) == 7) db[k2][1] = cvt8(dp[k2], 1);
+                    }
+                }
+                TREEATTN_SCHED();
+            }
+            asm("s_nop 1" : "+v"(db[0][1]), "+v"(db[1][1]));
+            TREEATTN_SCHED();
+            // k-step 1, then the next half's first reads
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                if (t + 2 < NT) {
+                    tr[1][t + 2] = rd_t(c, t + 2, 1);
+                } else if (c == 0) {
+                    if (t + 2 == NT) {
+                        rd_init(1, nl, nd);
+                    } else {
+                        so[0] = rd_s(1, 0);
+                        so[1] = rd_s(1, 1);
+                    }
+                }
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    mfma32_agpr(dv[kk][t], tr[1][t].ag, pb[kk][1]);
+                    mfma32_agpr(dk[kk][t], tr[1][t].aq, db[kk][1]);
+                }
+                TREEATTN_SCHED();
+            }
         }
 
         wait_vm_all();
         __syncthreads();
     }
+#undef TREEATTN_SCHED
     TREEATTN_FENCE_ACC("s_nop 7\n\ts_nop 7\n\ts_nop 7");  // last MFMA writes -> the reads below
 #undef TREEATTN_FENCE_ACC
 
