@@ -254,10 +254,13 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
         if (wave == 1) load_row64_async(dlv(buf), Delta + int64_t(hq) * L + p.qbase, lane);
     };
     StepPos cur{qhi * kBlock, 0, 0}, nxt{qhi * kBlock, 0, 0};
-    if (nsteps > 0) {
-        issue(nxt, 0);
-        advance(nxt);
-    }
+    // the first two steps' tiles; step st issues step st + 2's
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        if (i < nsteps) {
+            issue(nxt, i);
+            advance(nxt);
+        }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
         consume(sek[kk]);
@@ -267,67 +270,66 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
     wait_vm_all();
     __syncthreads();
 
+    const lds_char* kt = ktile + 64 * wave * T::kRowBytes;
+    struct SOps {
+        bf16x8 aq, k0, k1;
+    };
+    // k-step x of S: Q rows of half c of buffer buf and the wave's two
+    // 32-key K blocks
+    auto rd_s = [&](int buf, int c, int x) {
+        const int ro = roff(x);
+        return SOps{T::frag_at(qtile(buf) + 32 * c * T::kRowBytes, ro), T::frag_at(kt, ro),
+                    T::frag_at(kt + 32 * T::kRowBytes, ro)};
+    };
+    // S starts at -LSE / scale and dP at -Delta, so they leave
+    // S - LSE / scale and dP - Delta; register r of a score accumulator
+    // holds query 32 c + 8 (r / 4) + 4 h + r % 4 against key 32 kk + j32
+    auto rd_init = [&](int buf, int c, f32x16& nl, f32x16& nd) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const f32x4 a = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+                lsev(buf) + 4 * (32 * c + 8 * j + 4 * h));
+            const f32x4 b = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+                dlv(buf) + 4 * (32 * c + 8 * j + 4 * h));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                nl[4 * j + i] = a[i];
+                nd[4 * j + i] = b[i];
+            }
+        }
+    };
+    // the first reads of a step (made at the end of the previous one)
+    f32x16 nl, nd;
+    SOps so[NX];
+    rd_init(0, 0, nl, nd);
+    so[0] = rd_s(0, 0, 0);
+    so[1] = rd_s(0, 0, 1);
+
     // One step is 64 queries in two halves of 32.  Per half the MFMA stream
-    // is S (NX), dP (NX), then dV/dK (8 NT); the exponentials run between
-    // the dP MFMAs, and dS of the half's second 16 queries between the first
+    // is S (NX), dP (NX), then dV (2 NT), dK (2 NT) and both again (4 NT);
+    // the exponentials run between the dP MFMAs and dS between the first
     // gradient MFMAs, so the matrix core keeps work queued while the vector
     // unit runs (one wave per SIMD hides nothing by itself).  Scheduling
     // barriers pin that order; each group issues the LDS reads of the group
-    // two ahead.
+    // two ahead.  The step's barrier sits two gradient groups before its
+    // end, once its last reads have returned, so the next step's tiles are
+    // requested and its first operands read while those groups run.
 #define TREEATTN_SCHED() __builtin_amdgcn_sched_barrier(0)
     for (int st = 0; st < nsteps; ++st) {
         const int buf = st & 1;
         const int qbase = cur.qbase;
         advance(cur);
-        if (st + 1 < nsteps) {
-            issue(nxt, buf ^ 1);
-            advance(nxt);
-        }
         const lds_char* qt = qtile(buf);
         const lds_char* gt = gtile(buf);
-        const lds_char* lsp = lsev(buf);
-        const lds_char* dlp = dlv(buf);
-        const lds_char* kt = ktile + 64 * wave * T::kRowBytes;
 
-        struct SOps {
-            bf16x8 aq, k0, k1;
-        };
-        struct TOps {
-            bf16x8 ag, aq;
-        };
-        // k-step x of S: Q rows of the half and the wave's two 32-key K blocks
-        auto rd_s = [&](int c, int x) {
-            const int ro = roff(x);
-            return SOps{T::frag_at(qt + 32 * c * T::kRowBytes, ro), T::frag_at(kt, ro),
-                        T::frag_at(kt + 32 * T::kRowBytes, ro)};
-        };
         // k-step x of dP: dO rows of the half
         auto rd_g = [&](int c, int x) { return T::frag_at(gt + 32 * c * T::kRowBytes, roff(x)); };
-        // d-block t, k-step m of the gradients: dO^T and Q^T, rows
-        // 32 c + 16 m + 4 h + {0..3, 8..11} (a 16-row move keeps the swizzle
-        // phase, so it is a plain offset)
-        auto rd_t = [&](int c, int t, int m) {
+        // d-block t, k-step m of the gradients from the dO tile (dO^T) or
+        // the Q tile (Q^T): rows 32 c + 16 m + 4 h + {0..3, 8..11} (a 16-row
+        // move keeps the swizzle phase, so it is a plain offset)
+        auto rd_tr = [&](const lds_char* tile, int c, int t, int m) {
             const int rb = (32 * c + 16 * m) * T::kRowBytes;
-            const int o0 = toff(t, 0), o1 = toff(t, 1);
-            return TOps{join_tr(T::tr_at(gt + rb, o0), T::tr_at(gt + rb, o1)),
-                        join_tr(T::tr_at(qt + rb, o0), T::tr_at(qt + rb, o1))};
-        };
-        // S starts at -LSE / scale and dP at -Delta, so they leave
-        // S - LSE / scale and dP - Delta; register r of a score accumulator
-        // holds query 32 c + 8 (r / 4) + 4 h + r % 4 against key 32 kk + j32
-        auto rd_init = [&](int c, f32x16& nl, f32x16& nd) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const f32x4 a = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-                    lsp + 4 * (32 * c + 8 * j + 4 * h));
-                const f32x4 b = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-                    dlp + 4 * (32 * c + 8 * j + 4 * h));
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    nl[4 * j + i] = a[i];
-                    nd[4 * j + i] = b[i];
-                }
-            }
+            return join_tr(T::tr_at(tile + rb, toff(t, 0)), T::tr_at(tile + rb, toff(t, 1)));
         };
         auto cvt8 = [](const f32x16& s, int m) {
             return to_bf16x8(f32x4{s[8 * m], s[8 * m + 1], s[8 * m + 2], s[8 * m + 3]},
@@ -339,22 +341,29 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
         // opaque per step, so the offsets are formed at each use rather than
         // hoisted out of the loop into one register each
         asm volatile("" : "+v"(ru), "+v"(rbase), "+v"(tx[0]), "+v"(tx[1]), "+v"(tbase[0]), "+v"(tbase[1]));
-        f32x16 nl, nd;
-        SOps so[NX];
-        rd_init(0, nl, nd);
-        so[0] = rd_s(0, 0);
-        so[1] = rd_s(0, 1);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             f32x16 sc[2], dp[2];
             bf16x8 ag[NX], pb[2][2], db[2][2];
-            TOps tr[2][NT];
+            bf16x8 tg[2][NT], tq[2][NT];  // dO^T, Q^T of k-step m, d-block t
+            // gradient operand reads in the order they are consumed: dO^T of
+            // k-step 0 (dV), Q^T of k-step 0 (dK), then both of k-step 1
+            auto rd_unit = [&](int u) {
+                if (u < NT) {
+                    tg[0][u] = rd_tr(gt, c, u, 0);
+                } else if (u < 2 * NT) {
+                    tq[0][u - NT] = rd_tr(qt, c, u - NT, 0);
+                } else {
+                    tg[1][u - 2 * NT] = rd_tr(gt, c, u - 2 * NT, 1);
+                    tq[1][u - 2 * NT] = rd_tr(qt, c, u - 2 * NT, 1);
+                }
+            };
             TREEATTN_SCHED();
             // S = Q K^T
 #pragma unroll
             for (int x = 0; x < NX; ++x) {
                 if (x + 2 < NX)
-                    so[x + 2] = rd_s(c, x + 2);
+                    so[x + 2] = rd_s(buf, c, x + 2);
                 else
                     ag[x + 2 - NX] = rd_g(c, x + 2 - NX);
 #pragma unroll
@@ -405,7 +414,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
                     if (x + 2 < NX)
                         ag[x + 2] = rd_g(c, x + 2);
                     else
-                        tr[0][x + 2 - NX] = rd_t(c, x + 2 - NX, 0);
+                        rd_unit(x + 2 - NX);
                     dp[0] = mfma32x32x16(ag[x], vf[0][x], x == 0 ? nd : dp[0]);
 #pragma unroll
                     for (int e = 0; e < kExp / 2; ++e) ex(kExp * x + e);
@@ -414,10 +423,14 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
                     for (int e = kExp / 2; e < kExp; ++e) ex(kExp * x + e);
                     TREEATTN_SCHED();
                 }
+                // also the two wait states between the P conversions (VALU
+                // writes) and the asm MFMAs that read them
                 if constexpr (kMasked)
-                    asm volatile("; partial half end" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]));
+                    asm volatile("s_nop 1 ; partial half end"
+                                 : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]));
                 else
-                    asm volatile("; full half end" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]));
+                    asm volatile("s_nop 1 ; full half end"
+                                 : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]));
             };
             // A half is full (no mask) for this wave when every one of its 64
             // keys precedes every query of the half and every query ends
@@ -429,65 +442,79 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
                 dp_exp(std::false_type{});
             else
                 dp_exp(std::true_type{});
-            // dS = P (dP - Delta) of k-step 0 (queries 32 c + 0..15)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-                for (int r = 0; r < 8; ++r) dp[kk][r] *= sc[kk][r];
-                db[kk][0] = cvt8(dp[kk], 0);
-            }
-            // the conversions are VALU writes that the asm MFMAs read
-            asm("s_nop 1"
-                : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]), "+v"(db[0][0]), "+v"(db[1][0]));
             TREEATTN_SCHED();
-            // dV^T += dO^T P, dK^T += Q^T dS, k-step 0, with dS of k-step 1
-            // in between
+            // dS = P (dP - Delta), 16 products per k-step m (queries
+            // 32 c + 16 m + ..), spread over the gradient MFMAs before the
+            // ones that read them; the conversions are VALU writes that the
+            // asm MFMAs read, hence the s_nop 1 fences
+            auto ds_part = [&](int m, int t, int kk) {
+#pragma unroll
+                for (int i = 0; i < kDs; ++i) {
+                    const int e = (2 * t + kk) * kDs + i;  // 0..15
+                    const int k2 = e >> 3, r = 8 * m + (e & 7);
+                    dp[k2][r] *= sc[k2][r];
+                    if ((e & 7) == 7) db[k2][m] = cvt8(dp[k2], m);
+                }
+            };
+            // dV^T += dO^T P, k-step 0, with dS of k-step 0
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                if (t + 2 < NT)
-                    tr[0][t + 2] = rd_t(c, t + 2, 0);
-                else
-                    tr[1][t + 2 - NT] = rd_t(c, t + 2 - NT, 1);
+                rd_unit(t + 2);
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    mfma32_agpr(dv[kk][t], tr[0][t].ag, pb[kk][0]);
-                    mfma32_agpr(dk[kk][t], tr[0][t].aq, db[kk][0]);
+                    mfma32_agpr(dv[kk][t], tg[0][t], pb[kk][0]);
+                    ds_part(0, t, kk);
+                }
+                TREEATTN_SCHED();
+            }
+            asm("s_nop 1" : "+v"(db[0][0]), "+v"(db[1][0]));
+            TREEATTN_SCHED();
+            // dK^T += Q^T dS, k-step 0, with dS of k-step 1
 #pragma unroll
-                    for (int i = 0; i < kDs; ++i) {
-                        const int e = (2 * t + kk) * kDs + i;  // 0..15
-                        const int k2 = e >> 3, r = 8 + (e & 7);
-                        dp[k2][r] *= sc[k2][r];
-                        if ((e & 7) == 7) db[k2][1] = cvt8(dp[k2], 1);
-                    }
+            for (int t = 0; t < NT; ++t) {
+                rd_unit(NT + t + 2);
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    mfma32_agpr(dk[kk][t], tq[0][t], db[kk][0]);
+                    ds_part(1, t, kk);
                 }
                 TREEATTN_SCHED();
             }
             asm("s_nop 1" : "+v"(db[0][1]), "+v"(db[1][1]));
             TREEATTN_SCHED();
-            // k-step 1, then the next half's first reads
+            // k-step 1 of both, then the next half's first reads; in the
+            // second half, the step's barrier once the last reads of this
+            // buffer have returned, then the tiles of step st + 2 into it
+            // and the first reads of step st + 1 (stale but in-bounds LDS
+            // after the last step, never used)
+            constexpr int kBarT = NT - 2;
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                if (t + 2 < NT) {
-                    tr[1][t + 2] = rd_t(c, t + 2, 1);
-                } else if (c == 0) {
-                    if (t + 2 == NT) {
-                        rd_init(1, nl, nd);
-                    } else {
-                        so[0] = rd_s(1, 0);
-                        so[1] = rd_s(1, 1);
+                const int u = 2 * NT + t + 2;
+                if (c == 1 && t == kBarT) {
+                    wait_vm_all();
+                    __syncthreads();
+                    if (st + 2 < nsteps) {
+                        issue(nxt, buf);
+                        advance(nxt);
                     }
+                }
+                if (u < 3 * NT) {
+                    rd_unit(u);
+                } else if (u == 3 * NT) {
+                    rd_init(c == 0 ? buf : buf ^ 1, c ^ 1, nl, nd);
+                } else {
+                    so[0] = rd_s(c == 0 ? buf : buf ^ 1, c ^ 1, 0);
+                    so[1] = rd_s(c == 0 ? buf : buf ^ 1, c ^ 1, 1);
                 }
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    mfma32_agpr(dv[kk][t], tr[1][t].ag, pb[kk][1]);
-                    mfma32_agpr(dk[kk][t], tr[1][t].aq, db[kk][1]);
+                    mfma32_agpr(dv[kk][t], tg[1][t], pb[kk][1]);
+                    mfma32_agpr(dk[kk][t], tq[1][t], db[kk][1]);
                 }
                 TREEATTN_SCHED();
             }
         }
-
-        wait_vm_all();
-        __syncthreads();
     }
 #undef TREEATTN_SCHED
     TREEATTN_FENCE_ACC("s_nop 7\n\ts_nop 7\n\ts_nop 7");  // last MFMA writes -> the reads below
