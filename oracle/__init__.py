@@ -32,6 +32,7 @@ from .packing import (  # noqa: F401
     PackedTrie,
     extract_sequences,
     ffd_build_tries,
+    prefix_order_build_tries,
     compress_trie,
     flatten_trie,
     pack,

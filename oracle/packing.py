@@ -1,5 +1,5 @@
-"""Oracle packer: extraction, first-fit-decreasing trie building, chain
-compression, pre-order flattening, padding, the dense ancestor mask, position
+"""Oracle packer: extraction, first-fit-decreasing (or prefix-order) trie
+building, chain compression, pre-order flattening, padding, the dense ancestor mask, position
 ids, 128x128 tile classes and the packed-run accounting.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).  Plain Python and NumPy;
@@ -125,6 +125,28 @@ def ffd_build_tries(seqs: list[list[int]], max_tokens: int) -> list[OracleTrie]:
     return tries
 
 
+def prefix_order_build_tries(seqs: list[list[int]], max_tokens: int) -> list[OracleTrie]:
+    """Prefix-order packing, an option beside the pages' first-fit
+    decreasing.  [DTA] section 4 (负载均衡并行化) puts the sequences in
+    lexicographic order, the DFS order of one tree over all of them, so that
+    a contiguous run of them loses the least sharing.  Here the same order
+    fills tries of at most ``max_tokens`` tree tokens: each sequence goes into
+    the most recently opened trie if the tokens it adds keep that trie within
+    the budget, otherwise it opens a new one.  Reading: ties in the order
+    keep the row order, as in the partition."""
+    order = sorted(range(len(seqs)), key=lambda r: (list(seqs[r]), r))
+    tries: list[OracleTrie] = []
+    for r in order:
+        s = seqs[r]
+        if tries and tries[-1].num_tokens + tries[-1].additional_tokens(s) <= max_tokens:
+            tries[-1].insert(s, r)
+        else:
+            t = OracleTrie()
+            t.insert(s, r)
+            tries.append(t)
+    return tries
+
+
 # ---------------------------------------------------------------------------
 # step 3: compression (and pre-order numbering)
 # ---------------------------------------------------------------------------
@@ -237,9 +259,13 @@ def flatten_trie(trie: OracleTrie, nodes: list[CNode], L: int, pad_id: int) -> P
 
 
 def pack(ids, mask, max_tokens_per_mb, block_size: int = BLOCK_SIZE,
-         pad_to_maximum: bool = False, pad_id: int = 0) -> list[PackedTrie]:
+         pad_to_maximum: bool = False, pad_id: int = 0, order: str = "ffd") -> list[PackedTrie]:
     """Whole packing path of [TT] "参数背后的源码校验逻辑" and "树构建流程":
-    validate, extract, FFD-build tries, compress, flatten and pad."""
+    validate, extract, build tries (the pages' first-fit decreasing, or with
+    ``order="prefix"`` the prefix-order packing above), compress, flatten and
+    pad."""
+    if order not in ("ffd", "prefix"):
+        raise PackError("arg", f"unknown packing order {order!r}")
     if max_tokens_per_mb is None or int(max_tokens_per_mb) <= 0:
         raise PackError("max_tokens", "max_tokens_per_mb must be a positive integer")
     M = int(max_tokens_per_mb)
@@ -256,7 +282,8 @@ def pack(ids, mask, max_tokens_per_mb, block_size: int = BLOCK_SIZE,
         if len(s) > M:
             raise PackError("seq_too_long", f"row {r} has {len(s)} tokens > max_tokens_per_mb={M}")
     out = []
-    for trie in ffd_build_tries(seqs, M):
+    build = ffd_build_tries if order == "ffd" else prefix_order_build_tries
+    for trie in build(seqs, M):
         nodes = compress_trie(trie)
         n = trie.num_tokens
         L = M if pad_to_maximum else -(-n // block_size) * block_size
