@@ -62,6 +62,8 @@ def parse(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="4a", help="workload: 2, 3, 4a, 4b")
     ap.add_argument("--sweep", default=None, help="L,b of a sweep point (overrides --config)")
+    ap.add_argument("--pack", default="ffd", choices=["ffd", "prefix"],
+                    help="trie assignment: the pages' first-fit decreasing, or prefix (lexicographic next-fit) order")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=1, help="query heads in the oracle sample")
     ap.add_argument("--logprobs", action="store_true",
@@ -187,8 +189,8 @@ def main(argv=None):
     # as one launch: no attention crosses tries, so the concatenation is a
     # packed layout of its own, and one launch avoids per-trie launch and
     # tail costs on batches of many small tries.
-    tries, stats = pta.pack(w.ids, w.mask, w.max_tokens_per_mb)
-    se_cat, lengths, _ = pta.pack_concat(w.ids, w.mask, w.max_tokens_per_mb)
+    tries, stats = pta.pack(w.ids, w.mask, w.max_tokens_per_mb, order=a.pack)
+    se_cat, lengths, _ = pta.pack_concat(w.ids, w.mask, w.max_tokens_per_mb, order=a.pack)
     log(f"workload {w.name}: {len(tries)} tries, L={lengths}, one launch of L={len(se_cat)}, tree tokens "
         f"{stats['tree_tokens']}, pairs {stats['n_pairs']}, unpacked pairs {stats['unpacked_pairs']}")
     if len(se_cat) > (1 << 20):
@@ -265,7 +267,7 @@ def main(argv=None):
                 events.append((i, E))
 
     def pack_host():
-        cur, _, _ = pta.pack_concat(w.ids, w.mask, w.max_tokens_per_mb)
+        cur, _, _ = pta.pack_concat(w.ids, w.mask, w.max_tokens_per_mb, order=a.pack)
         return cur
 
     # Steady-state pipeline: the device work of step k is enqueued, then the
@@ -343,7 +345,7 @@ def main(argv=None):
         "kernel_ms_per_launch": {p: round(avg[p], 4) for p in PHASES},
         "config": {"workload": w.name, "tries": len(tries), "L": lengths, "launch_L": bufs[0]["L"], "hq": w.hq,
                    "hkv": w.hkv, "head_dim": w.d, "max_tokens_per_mb": w.max_tokens_per_mb,
-                   "tree_tokens": tokens, "pairs": n_pairs, "parallelism": "single-gpu"},
+                   "tree_tokens": tokens, "pairs": n_pairs, "pack": a.pack, "parallelism": "single-gpu"},
         "roofline": roof,
     }
     if not a.no_cpu_baseline:

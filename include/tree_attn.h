@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define TREE_ATTN_ABI_VERSION 3
+#define TREE_ATTN_ABI_VERSION 4
 
 /* status codes */
 #define TREE_OK 0
@@ -119,6 +119,25 @@ typedef struct {
 int tree_pack(const int32_t* ids, const uint8_t* mask, int64_t B, int64_t S,
               int64_t max_tokens_per_mb, int32_t block_size, int32_t pad_to_maximum,
               int32_t pad_id, tree_pack_t** out);
+
+/* How tree_pack_ordered assigns sequences to tries. */
+#define TREE_PACK_FFD 0    /* first-fit decreasing, as tree_pack */
+#define TREE_PACK_PREFIX 1 /* prefix order, see below */
+
+/* tree_pack with a choice of assignment.  TREE_PACK_FFD is tree_pack.
+ * TREE_PACK_PREFIX takes the sequences in lexicographic order (token ids
+ * compared as integers, a proper prefix first, ties by row): the DFS order
+ * of one tree over the whole batch that AREAL-DTA's load-balancing section
+ * (负载均衡并行化) partitions.  Each sequence goes into the most recently
+ * opened trie if its uncompressed token count plus what the sequence adds
+ * stays <= max_tokens_per_mb, otherwise it opens a new trie, so every trie
+ * is a contiguous run of that order and keeps a prompt's responses
+ * together where first-fit by length spreads them.  Sequences are inserted
+ * in that order.  Arguments, layout, ownership and errors are those of
+ * tree_pack, plus TREE_E_ARG for an unknown order. */
+int tree_pack_ordered(const int32_t* ids, const uint8_t* mask, int64_t B, int64_t S,
+                      int64_t max_tokens_per_mb, int32_t block_size, int32_t pad_to_maximum,
+                      int32_t pad_id, int32_t order, tree_pack_t** out);
 
 /* Number of tries, or -1 if p is NULL. */
 int64_t tree_pack_num_tries(const tree_pack_t* p);

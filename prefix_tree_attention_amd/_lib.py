@@ -60,6 +60,8 @@ SIGNATURES = {
     "tree_abi_version": (ctypes.c_int, []),
     "tree_last_error": (ctypes.c_char_p, []),
     "tree_pack": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, ctypes.POINTER(c_vp)]),
+    "tree_pack_ordered": (ctypes.c_int,
+                          [c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_vp)]),
     "tree_pack_num_tries": (c_i64, [c_vp]),
     "tree_pack_trie": (ctypes.c_int, [c_vp, c_i64, ctypes.POINTER(TrieView)]),
     "tree_pack_stats": (ctypes.c_int, [c_vp, ctypes.POINTER(PackStats)]),

@@ -48,18 +48,33 @@ def _arr(ptr, n) -> np.ndarray:
     return np.ctypeslib.as_array(ptr, shape=(int(n),)).copy()
 
 
-def pack(ids, mask, max_tokens_per_mb: int, block_size: int = BLOCK, pad_to_maximum: bool = False,
-         pad_id: int = 0):
-    """Pack a padded [B, S] batch into tries (``tree_pack``).  Returns
-    ``(tries, stats)`` with ``stats`` a dict of the pack's accounting."""
+_ORDERS = {"ffd": 0, "prefix": 1}  # TREE_PACK_FFD, TREE_PACK_PREFIX
+
+
+def _pack_handle(ids, mask, max_tokens_per_mb, block_size, pad_to_maximum, pad_id, order):
+    """Validate the batch and call ``tree_pack_ordered``; returns the
+    library-owned pack handle and the contiguous int32 ids."""
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     mask = np.ascontiguousarray(mask, dtype=np.uint8)
     if ids.ndim != 2 or ids.shape != mask.shape:
         raise TreeAttnError(-5, "ids and mask must both be [B, S]")
-    L = lib()
+    if order not in _ORDERS:
+        raise TreeAttnError(-5, f"order must be one of {sorted(_ORDERS)} (got {order!r})")
     h = ctypes.c_void_p()
-    check(L.tree_pack(ids.ctypes.data, mask.ctypes.data, ids.shape[0], ids.shape[1], int(max_tokens_per_mb),
-                      int(block_size), int(bool(pad_to_maximum)), int(pad_id), ctypes.byref(h)))
+    check(lib().tree_pack_ordered(ids.ctypes.data, mask.ctypes.data, ids.shape[0], ids.shape[1],
+                                  int(max_tokens_per_mb), int(block_size), int(bool(pad_to_maximum)), int(pad_id),
+                                  _ORDERS[order], ctypes.byref(h)))
+    return h, ids
+
+
+def pack(ids, mask, max_tokens_per_mb: int, block_size: int = BLOCK, pad_to_maximum: bool = False,
+         pad_id: int = 0, order: str = "ffd"):
+    """Pack a padded [B, S] batch into tries (``tree_pack_ordered``; order
+    ``"ffd"`` is the pages' first-fit decreasing, ``"prefix"`` the
+    lexicographic next-fit packing).  Returns ``(tries, stats)`` with
+    ``stats`` a dict of the pack's accounting."""
+    L = lib()
+    h, ids = _pack_handle(ids, mask, max_tokens_per_mb, block_size, pad_to_maximum, pad_id, order)
     try:
         tries = []
         for t in range(L.tree_pack_num_tries(h)):
@@ -82,19 +97,13 @@ def pack(ids, mask, max_tokens_per_mb: int, block_size: int = BLOCK, pad_to_maxi
 
 
 def pack_concat(ids, mask, max_tokens_per_mb: int, block_size: int = BLOCK, pad_to_maximum: bool = False,
-                pad_id: int = 0):
-    """Pack a batch and lay its tries end to end (``tree_pack`` then
-    ``tree_pack_concat``), for one launch over the whole batch.  Returns
-    ``(subtree_end, lengths, stats)``: the concatenated int32 subtree ends,
-    each trie's padded length in order, and the pack's accounting."""
-    ids = np.ascontiguousarray(ids, dtype=np.int32)
-    mask = np.ascontiguousarray(mask, dtype=np.uint8)
-    if ids.ndim != 2 or ids.shape != mask.shape:
-        raise TreeAttnError(-5, "ids and mask must both be [B, S]")
+                pad_id: int = 0, order: str = "ffd"):
+    """Pack a batch and lay its tries end to end (``tree_pack_ordered``
+    then ``tree_pack_concat``), for one launch over the whole batch.
+    Returns ``(subtree_end, lengths, stats)``: the concatenated int32 subtree
+    ends, each trie's padded length in order, and the pack's accounting."""
     L = lib()
-    h = ctypes.c_void_p()
-    check(L.tree_pack(ids.ctypes.data, mask.ctypes.data, ids.shape[0], ids.shape[1], int(max_tokens_per_mb),
-                      int(block_size), int(bool(pad_to_maximum)), int(pad_id), ctypes.byref(h)))
+    h, ids = _pack_handle(ids, mask, max_tokens_per_mb, block_size, pad_to_maximum, pad_id, order)
     try:
         total = ctypes.c_int64()
         check(L.tree_pack_concat(h, None, 0, ctypes.byref(total)))
@@ -114,21 +123,15 @@ def pack_concat(ids, mask, max_tokens_per_mb: int, block_size: int = BLOCK, pad_
 
 
 def pack_batch(ids, mask, max_tokens_per_mb: int, block_size: int = BLOCK, pad_to_maximum: bool = False,
-               pad_id: int = 0):
+               pad_id: int = 0, order: str = "ffd"):
     """Pack a batch into the concatenated layout and return everything the
     attention and log-probability calls need: ``(subtree_end, token_ids,
     row_positions, lengths, stats)``.  ``token_ids`` is the packed ids
     (``tree_pack_concat_ids``), ``row_positions`` the int32 [B, S] packed
     position of each row's k-th real token, -1 after it
-    (``tree_pack_row_positions``)."""
-    ids = np.ascontiguousarray(ids, dtype=np.int32)
-    mask = np.ascontiguousarray(mask, dtype=np.uint8)
-    if ids.ndim != 2 or ids.shape != mask.shape:
-        raise TreeAttnError(-5, "ids and mask must both be [B, S]")
+    (``tree_pack_row_positions``).  ``order`` as in ``pack``."""
     L = lib()
-    h = ctypes.c_void_p()
-    check(L.tree_pack(ids.ctypes.data, mask.ctypes.data, ids.shape[0], ids.shape[1], int(max_tokens_per_mb),
-                      int(block_size), int(bool(pad_to_maximum)), int(pad_id), ctypes.byref(h)))
+    h, ids = _pack_handle(ids, mask, max_tokens_per_mb, block_size, pad_to_maximum, pad_id, order)
     try:
         total = ctypes.c_int64()
         check(L.tree_pack_concat(h, None, 0, ctypes.byref(total)))

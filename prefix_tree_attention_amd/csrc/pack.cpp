@@ -10,6 +10,9 @@
 // children keep insertion order, a chain node merges into its only child
 // exactly when no sequence ends at it (which is when both carry the same
 // sequences), empty rows are an error, pads get node -1 / subtree end -1.
+// tree_pack_ordered adds prefix-order packing: the lexicographic (DFS) order
+// of AREAL-DTA's load-balancing section fills tries one after another (next
+// fit), so each trie is a contiguous run of that order.
 //
 // The tries are built directly in compressed (radix) form: a node's tokens
 // are a run of one source sequence, referenced by (sequence, start, length),
@@ -259,9 +262,18 @@ extern "C" {
 int tree_pack(const int32_t* ids, const uint8_t* mask, int64_t B, int64_t S,
               int64_t max_tokens_per_mb, int32_t block_size, int32_t pad_to_maximum,
               int32_t pad_id, tree_pack_t** out) {
+    return tree_pack_ordered(ids, mask, B, S, max_tokens_per_mb, block_size, pad_to_maximum, pad_id, TREE_PACK_FFD,
+                             out);
+}
+
+int tree_pack_ordered(const int32_t* ids, const uint8_t* mask, int64_t B, int64_t S,
+                      int64_t max_tokens_per_mb, int32_t block_size, int32_t pad_to_maximum,
+                      int32_t pad_id, int32_t order_kind, tree_pack_t** out) {
     using treeattn::set_error;
     if (out) *out = nullptr;
     if (!out) return set_error(TREE_E_ARG, "tree_pack: out is NULL");
+    if (order_kind != TREE_PACK_FFD && order_kind != TREE_PACK_PREFIX)
+        return set_error(TREE_E_ARG, "tree_pack_ordered: unknown order %d", order_kind);
     if (max_tokens_per_mb <= 0)
         return set_error(TREE_E_MAX_TOKENS, "max_tokens_per_mb must be a positive integer (got %lld)",
                          (long long)max_tokens_per_mb);
@@ -294,17 +306,26 @@ int tree_pack(const int32_t* ids, const uint8_t* mask, int64_t B, int64_t S,
         const int64_t original = int64_t(seqs.tok.size());
         std::vector<int32_t> order(static_cast<size_t>(B));
         std::iota(order.begin(), order.end(), 0);
-        std::stable_sort(order.begin(), order.end(),
-                         [&](int32_t a, int32_t b) { return seqs.len(a) > seqs.len(b); });
+        const bool prefix = order_kind == TREE_PACK_PREFIX;
+        if (prefix)  // lexicographic (DFS) order, a proper prefix first, ties by row
+            std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+                return std::lexicographical_compare(seqs.at(a), seqs.at(a) + seqs.len(a), seqs.at(b),
+                                                    seqs.at(b) + seqs.len(b));
+            });
+        else  // longest first, ties by row
+            std::stable_sort(order.begin(), order.end(),
+                             [&](int32_t a, int32_t b) { return seqs.len(a) > seqs.len(b); });
         std::vector<std::unique_ptr<RadixTrie>> tries;
         for (int32_t r : order) {
             const int64_t n = seqs.len(r);
             RadixTrie* dst = nullptr;
             RadixTrie::Walk w{};
-            for (auto& t : tries) {
+            // first fit over all tries, or (prefix order) the newest one only
+            for (size_t k = prefix && !tries.empty() ? tries.size() - 1 : 0; k < tries.size(); ++k) {
+                RadixTrie* t = tries[k].get();
                 w = t->walk(seqs, seqs.at(r), n);
                 if (t->tokens + (n - w.matched) <= M) {
-                    dst = t.get();
+                    dst = t;
                     break;
                 }
             }

@@ -2,8 +2,9 @@
 (tree_pack_concat) and run through tree_meta / tree_attn_fwd / tree_attn_bwd
 as a single packed layout, which is how bench.py times multi-trie batches.
 Every trie's slice of the results must equal that trie run alone against
-the oracle: elementwise on a scaled-down batch of three tries, and on
-sampled rows and key columns of the full GRPO batch (24 tries)."""
+the oracle: elementwise on a scaled-down batch of several tries (in the
+pages' first-fit-decreasing and in prefix order), and on sampled rows and
+key columns of the full GRPO batch (24 tries)."""
 
 import math
 
@@ -18,8 +19,8 @@ from gpu_common import BF16_ATOL, BF16_RTOL, announce, assert_close, bf16_ref, s
 pytestmark = pytest.mark.gpu
 
 
-def _concat_run(torch, ids, mask, M, hq, hkv, d, std, seed):
-    se, lengths, _ = pta.pack_concat(ids, mask, M)
+def _concat_run(torch, ids, mask, M, hq, hkv, d, std, seed, order="ffd"):
+    se, lengths, _ = pta.pack_concat(ids, mask, M, order=order)
     parts = [workloads.attention_inputs(Lt, hq, hkv, d, "bf16", std, seed + t) for t, Lt in enumerate(lengths)]
     q, k, v, do = (torch.cat([p[j] for p in parts]) for j in range(4))
     meta = pta.tree_meta(se)
@@ -31,14 +32,15 @@ def _concat_run(torch, ids, mask, M, hq, hkv, d, std, seed):
             q, k, v, do, o.cpu(), lse.cpu(), dq.cpu(), dk.cpu(), dv.cpu())
 
 
-def test_concat_small_elementwise():
+@pytest.mark.parametrize("order", ["ffd", "prefix"])
+def test_concat_small_elementwise(order):
     torch = torch_cuda()
     ids, mask, M = workloads.small_workload("grpo-small")
-    to = oracle.pack(ids, mask, M)
+    to = oracle.pack(ids, mask, M, order=order)
     hq, hkv, d = 8, 2, 128
-    announce(f"concat grpo-small: {len(to)} tries, L={[t.L for t in to]}")
+    announce(f"concat grpo-small ({order} order): {len(to)} tries, L={[t.L for t in to]}")
     se, lengths, tc, pos, q, k, v, do, o, lse, dq, dk, dv = _concat_run(torch, ids, mask, M, hq, hkv, d,
-                                                                         1.0 / math.sqrt(d), 500)
+                                                                         1.0 / math.sqrt(d), 500, order)
     assert lengths == [t.L for t in to] and len(to) > 1
     scale = 1.0 / math.sqrt(d)
     off = 0

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
     for n in sorted(names):
         assert hasattr(L, n), n
     assert set(_lib.SIGNATURES) == names
-    assert L.tree_abi_version() == 3
+    assert L.tree_abi_version() == 4
 
 
 def _compare(tries_lib, tries_or):
@@ -108,6 +108,57 @@ def test_random_batches_bit_exact(L, seed):
     masks = [oracle.dense_ancestor_mask(p) for p in to]
     acc = oracle.accounting(to, masks, mask.sum(1))
     assert st["n_pairs"] == acc["n_pairs"]
+
+
+@pytest.mark.parametrize("config", ["1", "2", "3", "4a", "4b"])
+def test_prefix_order_configs_bit_exact(L, config):
+    w = workloads.make_workload(config)
+    tl, st = pta.pack(w.ids, w.mask, w.max_tokens_per_mb, order="prefix")
+    to = oracle.pack(w.ids, w.mask, w.max_tokens_per_mb, order="prefix")
+    _compare(tl, to)
+    _stats_vs_oracle(st, to, w.mask)
+    # the layout of every trie is the same as if its rows were packed alone
+    for p in to:
+        rows = p.seq_ids
+        alone = oracle.pack(w.ids[rows], w.mask[rows], w.max_tokens_per_mb, order="prefix")
+        assert len(alone) == 1 and alone[0].n_tokens == p.n_tokens
+
+
+@pytest.mark.parametrize("L_,b", [(8192, 1), (8192, 8), (16384, 4)])
+def test_prefix_order_sweep_points_bit_exact(L, L_, b):
+    w = workloads.sweep_workload(L_, b)
+    tl, _ = pta.pack(w.ids, w.mask, w.max_tokens_per_mb, order="prefix")
+    _compare(tl, oracle.pack(w.ids, w.mask, w.max_tokens_per_mb, order="prefix"))
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_prefix_order_random_batches_bit_exact(L, seed):
+    rng = np.random.default_rng(5000 + seed)
+    seqs = []
+    for _ in range(int(rng.integers(1, 30))):
+        if seqs and rng.random() < 0.6:
+            base = seqs[int(rng.integers(len(seqs)))]
+            cut = int(rng.integers(0, len(base) + 1))
+            tail = rng.integers(0, 4, int(rng.integers(0 if cut else 1, 90)))
+            s = np.concatenate([base[:cut], tail]).astype(np.int32)
+        else:
+            s = rng.integers(0, 4, int(rng.integers(1, 120))).astype(np.int32)
+        seqs.append(s if len(s) else np.array([0], np.int32))
+    ids, mask = workloads.pad_rows(seqs)
+    M = max(int(rng.choice([128, 256])), -(-max(len(s) for s in seqs) // 128) * 128)
+    tl, _ = pta.pack(ids, mask, M, pad_to_maximum=bool(seed % 2), pad_id=seed % 5, order="prefix")
+    _compare(tl, oracle.pack(ids, mask, M, pad_to_maximum=bool(seed % 2), pad_id=seed % 5, order="prefix"))
+
+
+def test_prefix_order_unknown_order(L):
+    ids, mask = workloads.worked_example()
+    h = ctypes.c_void_p()
+    rc = L.tree_pack_ordered(np.ascontiguousarray(ids, np.int32).ctypes.data,
+                             np.ascontiguousarray(mask, np.uint8).ctypes.data, ids.shape[0], ids.shape[1], 128, 128,
+                             0, 0, 2, ctypes.byref(h))
+    assert rc == -5 and not h.value and "unknown order" in L.tree_last_error().decode()
+    with pytest.raises(pta.TreeAttnError):
+        pta.pack(ids, mask, 128, order="lpt")
 
 
 def test_error_codes_match_oracle(L):
