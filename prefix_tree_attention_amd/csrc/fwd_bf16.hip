@@ -144,6 +144,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     scores(0, sa);  // with no steps this reads stale LDS and is never used
     __syncthreads();  // every wave is done with K(0) before K(2) replaces it
 
+#define TREEATTN_SCHED() __builtin_amdgcn_sched_barrier(0)
     // one step: softmax and P V of step st on `sc`, scores of step st + 1
     // into `sn`
     auto step = [&](int st, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
@@ -198,40 +199,71 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         }
         const float muse = m_run == -INFINITY ? 0.f : m_run;
 
-        // the next step's scores, independent of the exp work below (after
-        // the last step they read a stale K buffer and are discarded)
-        scores(st + 1, sn);
-
-        float rs = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
+        // The next step's scores (independent of the exp work; after the
+        // last step they read a stale K buffer and are discarded) as two
+        // chains, one per 32-key block, with this step's exponentials
+        // between their MFMAs; then O^T += V^T P^T.  Scheduling barriers pin
+        // that order, and every LDS operand is read two MFMA groups before
+        // its use: left to itself the compiler fed one chain through a
+        // single register quadruple, so each of its MFMAs waited a full LDS
+        // round trip.
+        {
+            const lds_char* ktn = ktile(st + 1);
+            auto rd_k = [&](int x, int kk) { return T::frag_at(ktn + 32 * kk * T::kRowBytes, roff[x]); };
+            // A = 32 d x 16 keys of V^T, read transposed from the V tile in
+            // the P^T key order (rows 16 m + 4 h + {0..3, 8..11}); unit
+            // u = 4 t + m
+            auto rd_v = [&](int u) {
+                const int rb = 16 * (u & 3) * T::kRowBytes;
+                return join_tr(T::tr_at(vt + rb, toff[u >> 2][0]), T::tr_at(vt + rb, toff[u >> 2][1]));
+            };
+            constexpr int kE = 32 / NX;  // exponentials per k-step
+            bf16x8 kf[NX][2], va[4 * NT], pb[4];
+            float rs = 0.f;
+            // P = exp2(scale log2e S - m), and the P^T operand of k-step m
+            // (keys 16 m + {4 h + 0..3, 8 + 4 h + 0..3}) once its 8 are done
+            auto ex = [&](int e) {
+                const int kk = e >> 4, r = e & 15;
                 const float p = fast_exp2(__builtin_fmaf(sc[kk][r], scale_log2, -muse));
                 sc[kk][r] = p;
                 rs += p;
-            }
-        l_run += rs;
-        // P^T operands, k-step m = keys 16 m + {4 h + 0..3, 8 + 4 h + 0..3}
-        bf16x8 pb[4];
+                if ((e & 7) == 7) {
+                    const f32x16& a = sc[kk];
+                    const int b = 8 * ((e >> 3) & 1);
+                    pb[e >> 3] = to_bf16x8(f32x4{a[b], a[b + 1], a[b + 2], a[b + 3]},
+                                           f32x4{a[b + 4], a[b + 5], a[b + 6], a[b + 7]});
+                }
+            };
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const f32x16& a = sc[m / 2];
-            const int b = 8 * (m % 2);
-            pb[m] = to_bf16x8(f32x4{a[b], a[b + 1], a[b + 2], a[b + 3]},
-                              f32x4{a[b + 4], a[b + 5], a[b + 6], a[b + 7]});
+            for (int x = 0; x < 2; ++x) {
+                kf[x][0] = rd_k(x, 0);
+                kf[x][1] = rd_k(x, 1);
+            }
+            TREEATTN_SCHED();
+#pragma unroll
+            for (int x = 0; x < NX; ++x) {
+                if (x + 2 < NX) {
+                    kf[x + 2][0] = rd_k(x + 2, 0);
+                    kf[x + 2][1] = rd_k(x + 2, 1);
+                } else {
+                    va[x + 2 - NX] = rd_v(x + 2 - NX);
+                }
+                sn[0] = mfma32x32x16(kf[x][0], qf[x], x == 0 ? f32x16{} : sn[0]);
+#pragma unroll
+                for (int e = 0; e < kE / 2; ++e) ex(kE * x + e);
+                sn[1] = mfma32x32x16(kf[x][1], qf[x], x == 0 ? f32x16{} : sn[1]);
+#pragma unroll
+                for (int e = kE / 2; e < kE; ++e) ex(kE * x + e);
+                TREEATTN_SCHED();
+            }
+            l_run += rs;
+#pragma unroll
+            for (int u = 0; u < 4 * NT; ++u) {
+                if (u + 2 < 4 * NT) va[u + 2] = rd_v(u + 2);
+                oacc[u >> 2] = mfma32x32x16(va[u], pb[u & 3], oacc[u >> 2]);
+                TREEATTN_SCHED();
+            }
         }
-
-        // O^T += V^T P^T: A = 32 d x 16 keys read transposed from the V tile
-        // in the same key order (rows 16 m + 4 h + {0..3, 8..11})
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int rb = 16 * m * T::kRowBytes;
-                const bf16x8 a = join_tr(T::tr_at(vt + rb, toff[t][0]), T::tr_at(vt + rb, toff[t][1]));
-                oacc[t] = mfma32x32x16(a, pb[m], oacc[t]);
-            }
 
         wait_vm_all();
         __syncthreads();
@@ -242,6 +274,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         step(st, sa, sb);
         step(st + 1, sb, sa);
     }
+
+#undef TREEATTN_SCHED
 
     // epilogue: normalise, write O (bf16) and LSE (natural log)
     float l = l_run + __shfl_xor(l_run, 32);
