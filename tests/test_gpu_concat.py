@@ -4,7 +4,7 @@ as a single packed layout, which is how bench.py times multi-trie batches.
 Every trie's slice of the results must equal that trie run alone against
 the oracle: elementwise on a scaled-down batch of several tries (in the
 pages' first-fit-decreasing and in prefix order), and on sampled rows and
-key columns of the full GRPO batch (24 tries)."""
+key columns of the full GRPO batch (24 tries, or 22 in prefix order)."""
 
 import math
 
@@ -62,13 +62,14 @@ def test_concat_small_elementwise(order):
         off += po.L
 
 
-def test_concat_grpo_full_size_sampled():
+@pytest.mark.parametrize("order", ["ffd", "prefix"])
+def test_concat_grpo_full_size_sampled(order):
     torch = torch_cuda()
     w = workloads.make_workload("2")
-    to = oracle.pack(w.ids, w.mask, w.max_tokens_per_mb)
-    announce(f"concat config2: {len(to)} tries, L={sum(t.L for t in to)}")
+    to = oracle.pack(w.ids, w.mask, w.max_tokens_per_mb, order=order)
+    announce(f"concat config2 ({order} order): {len(to)} tries, L={sum(t.L for t in to)}")
     se, lengths, tc, pos, q, k, v, do, o, lse, dq, dk, dv = _concat_run(torch, w.ids, w.mask, w.max_tokens_per_mb,
-                                                                         w.hq, w.hkv, w.d, w.qkv_std, 9000)
+                                                                         w.hq, w.hkv, w.d, w.qkv_std, 9000, order)
     for nm, x in (("O", o), ("dQ", dq), ("dK", dk), ("dV", dv)):
         assert np.isfinite(x.float().numpy()).all(), nm
     scale = 1.0 / math.sqrt(w.d)
