@@ -7,22 +7,23 @@
 //   LSE_i = ln sum_{j in A(i)} exp(scale q_i.k_j).
 //
 // Work decomposition: one workgroup (4 waves) per (128-query block, query
-// head); wave w owns queries 32w..32w+31 of the block as two 16-column MFMA
-// groups.  The workgroup walks only the nonempty key tiles of its query
-// block (row list of the metadata), 64 keys per pipeline step.  K and V of a
-// step go HBM -> LDS by direct loads into double-buffered swizzled tiles
-// (tile.h) while the previous step computes.  Partial tiles apply the
+// head); wave w owns queries 32w..32w+31 of the block, one query per MFMA
+// column (32x32x16 MFMAs).  The workgroup walks only the nonempty key tiles
+// of its query block (row list of the metadata), 64 keys per pipeline step.
+// K and V of a step go HBM -> LDS by direct loads into swizzled two-deep
+// rings (tile.h) while earlier steps compute.  Partial tiles apply the
 // subtree-interval predicate; full tiles skip it.
 //
 // Products are computed transposed: S^T = K Q^T (A = K rows from LDS, B =
 // Q^T held in registers), O^T = V^T P^T (A = V^T read from the row-major V
 // tile by transposing LDS loads, B = P^T taken straight from the S^T
-// accumulators).  Each lane thus owns one query column, so softmax
-// statistics need only an in-lane reduction plus two cross-lane steps, and
-// the rescaling of O^T is per lane.  S^T block b covers keys 16b..16b+15;
-// k-step c of the PV product pairs blocks 2c and 2c+1, and the transposing
-// reads of V take exactly the key rows those accumulator lanes hold.
-// Softmax runs in base 2 with scale*log2(e) folded into one FMA.
+// accumulators).  Each lane thus owns one query column, keys split over
+// the lane pair l, l ^ 32, so softmax statistics need an in-lane reduction
+// plus one cross-lane step, and the rescaling of O^T is per lane.  k-step m
+// of the PV product covers keys 16m .. 16m + 15 of the step, and the
+// transposing reads of V take exactly the key rows those accumulator
+// registers hold.  Softmax runs in base 2 with scale*log2(e) folded into
+// one FMA.
 
 #include <cmath>
 
