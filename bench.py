@@ -156,9 +156,10 @@ def cpu_baseline(w, p_oracle_input, n_heads: int):
 def main(argv=None):
     a = parse(argv)
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus": a.gpus}), flush=True)
-        log("bench.py: multi-GPU runs are not part of this build (one trie per GPU; see the sharding design).")
+        log("bench.py: multi-GPU runs are not implemented: the path runs one GPU's share of a batch, and the batch "
+            "would be split over data-parallel ranks by tree_partition.")
         return 2
     if a.copy_calibration:
         return copy_calibration()
