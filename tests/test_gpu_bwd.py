@@ -92,10 +92,12 @@ def _pick_keys(po, rng, n_keys, max_desc):
     return keys
 
 
-@pytest.mark.parametrize("config", ["4a", "4b", "2", "3"])
+@pytest.mark.parametrize("config", ["4a", "4b", "2", "3", "L65536-b8"])
 def test_bwd_full_size_sampled(config):
+    # "L65536-b8": the sweep point whose first trie fills the largest budget
+    # (L = 65536)
     torch = torch_cuda()
-    w = workloads.make_workload(config)
+    w = workloads.sweep_workload(65536, 8) if config == "L65536-b8" else workloads.make_workload(config)
     tl, _ = pta.pack(w.ids, w.mask, w.max_tokens_per_mb)
     to = oracle.pack(w.ids, w.mask, w.max_tokens_per_mb)
     pl, po = tl[0], to[0]
