@@ -46,7 +46,7 @@ def _full_check(torch, name, ids, mask, M, hq, hkv, d, dtype, seed):
 
 
 @pytest.mark.parametrize("case", list(range(6)))
-@pytest.mark.parametrize("shape", [(8, 2, 128), (4, 1, 64), (2, 2, 128)])
+@pytest.mark.parametrize("shape", [(8, 2, 128), (4, 1, 64), (2, 2, 128), (8, 1, 128)])
 def test_fwd_bf16_small(case, shape):
     torch = torch_cuda()
     name, ids, mask, M = list(small_cases())[case]
