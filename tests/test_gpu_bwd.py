@@ -148,3 +148,29 @@ def test_autograd_function_matches_entry_points():
     torch.cuda.synchronize()
     assert torch.equal(o, o2)
     assert torch.equal(qd.grad, dq) and torch.equal(kd.grad, dk) and torch.equal(vd.grad, dv)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("fp32", 64)])
+def test_bwd_scale_argument(dtype, d):
+    """A softmax scale other than 1/sqrt(D) reaches every place it enters:
+    the -LSE / scale initial value of S, the exp2 argument and dK."""
+    torch = torch_cuda()
+    ids, mask, M = workloads.small_workload("nested")
+    (pl,), _ = pta.pack(ids, mask, M)
+    (po,) = oracle.pack(ids, mask, M)
+    scale = 0.37
+    announce(f"bwd scale {scale} {dtype} d={d}")
+    q, k, v, do = workloads.attention_inputs(pl.L, 4, 2, d, dtype, 0.09 if dtype == "bf16" else 0.5, 17)
+    meta = pta.tree_meta(pl.subtree_end)
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    o, lse = pta.attn_fwd(qd, kd, vd, meta, scale=scale)
+    dq, dk, dv = pta.attn_bwd(qd, kd, vd, o, lse, dod, meta, scale=scale)
+    torch.cuda.synchronize()
+    m = oracle.dense_ancestor_mask(po)
+    Q, K, V, G = (bf16_ref(x) for x in (q, k, v, do))
+    o_ref, lse_ref = oracle.attention_forward(Q, K, V, m, scale)
+    dq_ref, dk_ref, dv_ref = oracle.attention_backward(Q, K, V, o_ref, lse_ref, G, m, scale)
+    atol, rtol = (F32_ATOL, F32_RTOL) if dtype == "fp32" else (BF16_ATOL, BF16_RTOL)
+    assert_close(bf16_ref(dq.cpu()), dq_ref, atol, rtol, "scaled dQ")
+    assert_close(bf16_ref(dk.cpu()), dk_ref, atol, rtol, "scaled dK")
+    assert_close(bf16_ref(dv.cpu()), dv_ref, atol, rtol, "scaled dV")
