@@ -94,8 +94,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     // Software pipeline: while step st runs its softmax and P V, the S^T of
     // step st + 1 is computed, so the MFMA unit has independent work while
     // the wave does its exp / row-sum VALU work.  K and V therefore sit in
-    // separate two-deep rings: at step st, V(st) (with the keys' subtree
-    // ends) and K(st + 1) are resident while K(st + 2) and V(st + 1) load.
+    // separate two-deep rings: at step st, V(st) and K(st + 1) (with its
+    // keys' subtree ends) are resident while K(st + 2) and V(st + 1) load.
     auto ktile = [&](int st) { return smem + (st & 1) * T::kBytes; };
     auto vtile = [&](int st) { return smem + (2 + (st & 1)) * T::kBytes; };
     auto serow = [&](int st) { return smem + 4 * T::kBytes + (st & 1) * 4 * kStep; };
@@ -105,17 +105,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const uint32_t kv_row_bytes = uint32_t(kv_stride) * 2u;
     auto kbase_of = [&](int st) { return (row_ent[beg + (st >> 1)] >> 1) * kBlock + kStep * (st & 1); };
     auto issue_k = [&](int st) {
-        const uint64_t off = uint64_t(uint32_t(kbase_of(st))) * kv_row_bytes;
-        T::load_async(ktile(st), reinterpret_cast<const bf16*>(Kh + off), kvs, wave, lane);
-    };
-    auto issue_v = [&](int st) {
         const int kbase = kbase_of(st);
         const uint64_t off = uint64_t(uint32_t(kbase)) * kv_row_bytes;
-        T::load_async(vtile(st), reinterpret_cast<const bf16*>(Vh + off), kvs, wave, lane);
-        // the keys' subtree ends ride with the V tile (wave w stages 16 of
-        // them), so the partial-tile mask reads LDS instead of issuing
-        // global loads whose wait would also drain the prefetch
+        T::load_async(ktile(st), reinterpret_cast<const bf16*>(Kh + off), kvs, wave, lane);
+        // the keys' subtree ends ride with the K tile (wave w stages 16 of
+        // them): a step's mask is applied while the step before it runs its
+        // P V product, and reading LDS there issues no global load whose
+        // wait would also drain the prefetch
         if (lane < 16) dma4(se + kbase + 16 * wave, 4u * lane, lds_addr(serow(st) + 64 * wave));
+    };
+    auto issue_v = [&](int st) {
+        const uint64_t off = uint64_t(uint32_t(kbase_of(st))) * kv_row_bytes;
+        T::load_async(vtile(st), reinterpret_cast<const bf16*>(Vh + off), kvs, wave, lane);
     };
     // S^T = K Q^T (unscaled) of step st for its two 32-key blocks kk:
     // register r holds key kbase + 32 kk + 8 (r / 4) + 4 h + r % 4 against
@@ -131,6 +132,46 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
                 sc[kk] = mfma32x32x16(T::frag_at(kt + 32 * kk * T::kRowBytes, roff[x]), qf[x], sc[kk]);
         }
     };
+    // partial tiles: key <= qi and qi <= se[key], i.e.
+    // 8 (r / 4) + r % 4 <= qi - (kbase + 32 kk + 4 h) and qi <= se[key]
+    auto mask = [&](int st, f32x16 (&s)[2]) {
+        const int kbase = kbase_of(st);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int k0 = kbase + 32 * kk + 4 * h, lim = qi - k0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const i32x4 sek = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(
+                    serow(st) + 4 * (32 * kk + 8 * j + 4 * h));
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (!(8 * j + i <= lim && qi <= sek[i])) s[kk][4 * j + i] = -INFINITY;
+            }
+        }
+    };
+    // Online softmax in base 2, one query per lane (its keys split over the
+    // lane pair l, l ^ 32).  The running max m_run is kept in scaled units
+    // and only moves when some lane's tile max exceeds it by more than
+    // kRescaleSlack (log2 units): O and l are both relative to the same
+    // reference, so a stale one changes nothing but the magnitude of p,
+    // which stays <= 2^kRescaleSlack, and the O rescale runs a few times per
+    // row instead of nearly every step.  rebase() takes the row max of a
+    // step's masked scores, moves the reference if needed and returns the
+    // factor alpha that carries sums over the old reference to the new one
+    // (resc false: no move, alpha unused).  maximum (not maxnum) lowers to
+    // v_maximum3_f32 with no NaN-quieting of the accumulator inputs.
+    auto rebase = [&](float mx, bool ok, bool& resc) {
+        mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32));
+        const float mt = mx * scale_log2;
+        resc = __any(ok & (mt > m_run + kRescaleSlack));
+        const float mnew = resc ? fmaxf(m_run, mt) : m_run;
+        const float alpha = fast_exp2(m_run - (mnew == -INFINITY ? 0.f : mnew));
+        m_run = mnew;
+        return alpha;
+    };
+    auto max2 = [](float m, float a, float b) {
+        return __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, a), b);
+    };
 
     f32x16 sa[2], sb[2];
     if (nsteps > 0) {
@@ -142,128 +183,148 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     for (int x = 0; x < NX; ++x) consume(qf[x]);
     wait_vm_all();
     __syncthreads();
-    scores(0, sa);  // with no steps this reads stale LDS and is never used
-    __syncthreads();  // every wave is done with K(0) before K(2) replaces it
-
-#define TREEATTN_SCHED() __builtin_amdgcn_sched_barrier(0)
-    // one step: softmax and P V of step st on `sc`, scores of step st + 1
-    // into `sn`
-    auto step = [&](int st, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-        const int ent = row_ent[beg + (st >> 1)];
-        const int kbase = (ent >> 1) * kBlock + kStep * (st & 1);
-        const bool partial = ent & 1;
-        if (st + 2 < nsteps) issue_k(st + 2);
-        if (st + 1 < nsteps) issue_v(st + 1);
-        const lds_char* vt = vtile(st);
-
-        if (partial) {
-            // key <= qi  <=>  8 (r / 4) + r % 4 <= qi - (kbase + 32 kk + 4 h)
+    if (nsteps > 0) {
+        // step 0's scores, mask, reference and exp2 arguments; the steps
+        // below prepare each following step the same way beside their P V
+        scores(0, sa);
+        if (row_ent[beg] & 1) mask(0, sa);
+        float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int k0 = kbase + 32 * kk + 4 * h, lim = qi - k0;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const i32x4 sek = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(
-                        serow(st) + 4 * (32 * kk + 8 * j + 4 * h));
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (!(8 * j + i <= lim && qi <= sek[i])) sc[kk][4 * j + i] = -INFINITY;
-                }
-            }
+        for (int r = 0; r < 16; r += 2) {
+            m0 = max2(m0, sa[0][r], sa[0][r + 1]);
+            m1 = max2(m1, sa[1][r], sa[1][r + 1]);
         }
-
-        // online softmax in base 2, one query per lane (its keys split over
-        // the lane pair l, l ^ 32); the running max is kept in scaled units
-        // and the scale is folded into the FMA that forms the exp2 argument.
-        // maximum (not maxnum) chains lower to v_maximum3_f32 with no
-        // NaN-quieting of the accumulator inputs.
-        float mx = -INFINITY;
+        bool resc;
+        rebase(__builtin_elementwise_maximum(m0, m1), true, resc);  // O and l are still zero
+        const float muse = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int r = 0; r < 16; r += 2)
-                mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, sc[kk][r]), sc[kk][r + 1]);
-        mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32));
-        // The reference max only moves when some lane's tile max exceeds it
-        // by more than kRescaleSlack (log2 units).  O and l are both
-        // relative to the same reference, so a stale one changes nothing but
-        // the magnitude of p, which stays <= 2^kRescaleSlack; the O rescale
-        // thus runs a few times per row instead of nearly every step.
-        const float mt = mx * scale_log2;
-        if (__any(mt > m_run + kRescaleSlack)) {
-            const float mnew = fmaxf(m_run, mt);
-            const float alpha = fast_exp2(m_run - (mnew == -INFINITY ? 0.f : mnew));
+            for (int r = 0; r < 16; ++r) sa[kk][r] = __builtin_fmaf(sa[kk][r], scale_log2, -muse);
+    }
+    __syncthreads();  // every wave is done with K(0) and its subtree ends before K(2) replaces them
+
+#define TREEATTN_SCHED() __builtin_amdgcn_sched_barrier(0)
+    // One step.  On entry sc holds step st's exp2 arguments
+    // (scale log2e S - m, masked entries -inf).  The scores of step st + 1
+    // (independent of the exp work; after the last step they read a stale K
+    // buffer and are discarded) run as two chains, one per 32-key block,
+    // with this step's exponentials between their MFMAs; then O^T += V^T P^T
+    // runs with the VALU work that prepares step st + 1 between its MFMAs:
+    // this step's row sum, the next step's mask, row max and reference, and
+    // its exp2 arguments.  Scheduling barriers pin that order, and every LDS
+    // operand is read two MFMA groups before its use: left to itself the
+    // compiler fed one score chain through a single register quadruple, so
+    // each of its MFMAs waited a full LDS round trip, and it gathered the
+    // row sum and the row max into one serial chain at the top of each step,
+    // beside no MFMA at all.  Empty volatile asms hold each slot's results
+    // in place: without them the row sum and the exp2 arguments were sunk
+    // past the barriers to their uses.
+    auto step = [&](int st, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+        const bool has_next = st + 1 < nsteps;
+        // the next step's tile entry (its own for an even st), clamped to the
+        // row so that the read stays inside it after the last step
+        const int nent = row_ent[beg + min((st + 1) >> 1, (nsteps >> 1) - 1)];
+        const bool next_partial = has_next && (nent & 1);
+        if (st + 2 < nsteps) issue_k(st + 2);
+        if (has_next) issue_v(st + 1);
+        const lds_char* vt = vtile(st);
+        const lds_char* ktn = ktile(st + 1);
+        auto rd_k = [&](int x, int kk) { return T::frag_at(ktn + 32 * kk * T::kRowBytes, roff[x]); };
+        // A = 32 d x 16 keys of V^T, read transposed from the V tile in the
+        // P^T key order (rows 16 m + 4 h + {0..3, 8..11}); unit u = 4 t + m
+        auto rd_v = [&](int u) {
+            const int rb = 16 * (u & 3) * T::kRowBytes;
+            return join_tr(T::tr_at(vt + rb, toff[u >> 2][0]), T::tr_at(vt + rb, toff[u >> 2][1]));
+        };
+        constexpr int kE = 32 / NX;  // exponentials per k-step
+        bf16x8 kf[NX][2], va[4 * NT], pb[4];
+        // p = exp2(argument), and the P^T operand of k-step m (keys
+        // 16 m + {4 h + 0..3, 8 + 4 h + 0..3}) once its 8 are done
+        auto ex = [&](int e) {
+            const int kk = e >> 4, r = e & 15;
+            sc[kk][r] = fast_exp2(sc[kk][r]);
+            if ((e & 7) == 7) {
+                const f32x16& a = sc[kk];
+                const int b = 8 * ((e >> 3) & 1);
+                pb[e >> 3] = to_bf16x8(f32x4{a[b], a[b + 1], a[b + 2], a[b + 3]},
+                                       f32x4{a[b + 4], a[b + 5], a[b + 6], a[b + 7]});
+            }
+        };
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            kf[x][0] = rd_k(x, 0);
+            kf[x][1] = rd_k(x, 1);
+        }
+        TREEATTN_SCHED();
+#pragma unroll
+        for (int x = 0; x < NX; ++x) {
+            if (x + 2 < NX) {
+                kf[x + 2][0] = rd_k(x + 2, 0);
+                kf[x + 2][1] = rd_k(x + 2, 1);
+            } else {
+                va[x + 2 - NX] = rd_v(x + 2 - NX);
+            }
+            sn[0] = mfma32x32x16(kf[x][0], qf[x], x == 0 ? f32x16{} : sn[0]);
+#pragma unroll
+            for (int e = 0; e < kE / 2; ++e) ex(kE * x + e);
+            sn[1] = mfma32x32x16(kf[x][1], qf[x], x == 0 ? f32x16{} : sn[1]);
+#pragma unroll
+            for (int e = kE / 2; e < kE; ++e) ex(kE * x + e);
+            TREEATTN_SCHED();
+        }
+
+        // P V: the first quarter of its MFMAs carries the row sum (four
+        // partial sums), then the next step's mask (partial tiles), the
+        // second quarter its row max (two chains), and the second half the
+        // reference move and the exp2 arguments
+        constexpr int U = 4 * NT, UA = U / 4, UC = U / 2;
+        float rs[4] = {0.f, 0.f, 0.f, 0.f};
+        float m0 = -INFINITY, m1 = -INFINITY, alpha = 1.f, muse = 0.f;
+        bool resc = false;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (u + 2 < U) va[u + 2] = rd_v(u + 2);
+            oacc[u >> 2] = mfma32x32x16(va[u], pb[u & 3], oacc[u >> 2]);
+            if (u < UA) {
+                constexpr int n = 32 / UA;
+#pragma unroll
+                for (int i = 0; i < n; ++i) {
+                    const int e = n * u + i;
+                    rs[e & 3] += sc[e >> 4][e & 15];
+                }
+                asm volatile("" : "+v"(rs[0]), "+v"(rs[1]), "+v"(rs[2]), "+v"(rs[3]));
+            } else if (u < UC) {
+                constexpr int n = 16 / (UC - UA);  // per chain
+#pragma unroll
+                for (int i = 0; i < n; i += 2) {
+                    const int r = n * (u - UA) + i;
+                    m0 = max2(m0, sn[0][r], sn[0][r + 1]);
+                    m1 = max2(m1, sn[1][r], sn[1][r + 1]);
+                }
+                asm volatile("" : "+v"(m0), "+v"(m1));
+            } else {
+                if (u == UC) {
+                    alpha = rebase(__builtin_elementwise_maximum(m0, m1), has_next, resc);
+                    muse = m_run == -INFINITY ? 0.f : m_run;
+                }
+                constexpr int n = 32 / (U - UC);
+#pragma unroll
+                for (int i = 0; i < n; ++i) {
+                    const int e = n * (u - UC) + i;
+                    float a = __builtin_fmaf(sn[e >> 4][e & 15], scale_log2, -muse);
+                    asm volatile("" : "+v"(a));
+                    sn[e >> 4][e & 15] = a;
+                }
+            }
+            TREEATTN_SCHED();
+            if (u == UA - 1 && next_partial) mask(st + 1, sn);
+        }
+        l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+        if (resc) {
             l_run *= alpha;
 #pragma unroll
             for (int t = 0; t < NT; ++t) oacc[t] *= alpha;
-            m_run = mnew;
-        }
-        const float muse = m_run == -INFINITY ? 0.f : m_run;
-
-        // The next step's scores (independent of the exp work; after the
-        // last step they read a stale K buffer and are discarded) as two
-        // chains, one per 32-key block, with this step's exponentials
-        // between their MFMAs; then O^T += V^T P^T.  Scheduling barriers pin
-        // that order, and every LDS operand is read two MFMA groups before
-        // its use: left to itself the compiler fed one chain through a
-        // single register quadruple, so each of its MFMAs waited a full LDS
-        // round trip.
-        {
-            const lds_char* ktn = ktile(st + 1);
-            auto rd_k = [&](int x, int kk) { return T::frag_at(ktn + 32 * kk * T::kRowBytes, roff[x]); };
-            // A = 32 d x 16 keys of V^T, read transposed from the V tile in
-            // the P^T key order (rows 16 m + 4 h + {0..3, 8..11}); unit
-            // u = 4 t + m
-            auto rd_v = [&](int u) {
-                const int rb = 16 * (u & 3) * T::kRowBytes;
-                return join_tr(T::tr_at(vt + rb, toff[u >> 2][0]), T::tr_at(vt + rb, toff[u >> 2][1]));
-            };
-            constexpr int kE = 32 / NX;  // exponentials per k-step
-            bf16x8 kf[NX][2], va[4 * NT], pb[4];
-            float rs = 0.f;
-            // P = exp2(scale log2e S - m), and the P^T operand of k-step m
-            // (keys 16 m + {4 h + 0..3, 8 + 4 h + 0..3}) once its 8 are done
-            auto ex = [&](int e) {
-                const int kk = e >> 4, r = e & 15;
-                const float p = fast_exp2(__builtin_fmaf(sc[kk][r], scale_log2, -muse));
-                sc[kk][r] = p;
-                rs += p;
-                if ((e & 7) == 7) {
-                    const f32x16& a = sc[kk];
-                    const int b = 8 * ((e >> 3) & 1);
-                    pb[e >> 3] = to_bf16x8(f32x4{a[b], a[b + 1], a[b + 2], a[b + 3]},
-                                           f32x4{a[b + 4], a[b + 5], a[b + 6], a[b + 7]});
-                }
-            };
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                kf[x][0] = rd_k(x, 0);
-                kf[x][1] = rd_k(x, 1);
-            }
-            TREEATTN_SCHED();
-#pragma unroll
-            for (int x = 0; x < NX; ++x) {
-                if (x + 2 < NX) {
-                    kf[x + 2][0] = rd_k(x + 2, 0);
-                    kf[x + 2][1] = rd_k(x + 2, 1);
-                } else {
-                    va[x + 2 - NX] = rd_v(x + 2 - NX);
-                }
-                sn[0] = mfma32x32x16(kf[x][0], qf[x], x == 0 ? f32x16{} : sn[0]);
-#pragma unroll
-                for (int e = 0; e < kE / 2; ++e) ex(kE * x + e);
-                sn[1] = mfma32x32x16(kf[x][1], qf[x], x == 0 ? f32x16{} : sn[1]);
-#pragma unroll
-                for (int e = kE / 2; e < kE; ++e) ex(kE * x + e);
-                TREEATTN_SCHED();
-            }
-            l_run += rs;
-#pragma unroll
-            for (int u = 0; u < 4 * NT; ++u) {
-                if (u + 2 < 4 * NT) va[u + 2] = rd_v(u + 2);
-                oacc[u >> 2] = mfma32x32x16(va[u], pb[u & 3], oacc[u >> 2]);
-                TREEATTN_SCHED();
-            }
         }
 
         wait_vm_all();
