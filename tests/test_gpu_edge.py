@@ -7,7 +7,9 @@ tree_attn_bwd, elementwise against the oracle (bf16 and fp32):
 * three copies of one sequence (one chain, three sequence ids);
 * a trie filled to the last slot (n = L = 256, no pads);
 * a single 1000-token sequence (plain causal attention over 8 blocks, the
-  last one ragged).
+  last one ragged);
+* scores that grow along each row, so the forward's running max, and with
+  it the reference of O and the row sum, moves every step or two.
 """
 
 import math
@@ -74,3 +76,64 @@ def test_degenerate_layouts(name, dtype):
         assert np.allclose(o_ref[0], np.repeat(V[0], g, axis=0))  # O_0 = V_0 of each head's key/value head
         assert np.abs(dq_ref).max() < 1e-12 and np.abs(dk_ref).max() < 1e-12
         assert np.allclose(dv_ref[0], G[0].reshape(hkv, g, d).sum(1))  # dV_0 = sum of the group's dO_0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("name", ["causal-1000", "full-trie"])
+def test_forward_reference_moves_within_a_row(name, dtype):
+    """Scores that grow along the key axis, so the online softmax's running
+    max rises by 4 (1000-token sequence) to 16 (256-token trie) log2 units
+    per 64-key step, and the forward carries O and the row sum over to a new
+    reference every first or second step (it moves only past 8 log2 units);
+    with N(0, 1/D) inputs the max settles after the first step and that path
+    would go unexercised.  q = a u + noise, k_j = c_j u + noise with a fixed
+    unit vector u and c_j rising linearly to c_max, so S_ij ~ a c_j / sqrt(D)
+    reaches about 45 at the end of the row.  bf16 checks the forward; the
+    fp32 check mode checks the gradients as well."""
+    torch = torch_cuda()
+    seqs, M = _cases()[name]
+    ids, mask = workloads.pad_rows(seqs)
+    (pl,), _ = pta.pack(ids, mask, M)
+    (po,) = oracle.pack(ids, mask, M)
+    hq, hkv, d = (4, 2, 64) if dtype == "fp32" else (8, 2, 128)
+    L = pl.L
+    announce(f"reference moves {name} {dtype} L={L}")
+    g = torch.Generator().manual_seed(5150)
+    u = torch.randn(d, generator=g, dtype=torch.float64)
+    u /= u.norm()
+    a, c_max = 30.0, 1.5 * math.sqrt(d)
+    c = torch.linspace(0.0, c_max, L, dtype=torch.float64)
+    q = a * u + 0.5 * torch.randn(L, hq, d, generator=g, dtype=torch.float64)
+    k = c[:, None, None] * u + 0.5 * torch.randn(L, hkv, d, generator=g, dtype=torch.float64)
+    v = torch.randn(L, hkv, d, generator=g, dtype=torch.float64)
+    do = torch.randn(L, hq, d, generator=g, dtype=torch.float64)
+    tdt = torch.float32 if dtype == "fp32" else torch.bfloat16
+    q, k, v, do = (x.to(tdt) for x in (q, k, v, do))
+    meta = pta.tree_meta(pl.subtree_end)
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    o, lse = pta.attn_fwd(qd, kd, vd, meta)
+    torch.cuda.synchronize()
+    m = oracle.dense_ancestor_mask(po)
+    scale = 1.0 / math.sqrt(d)
+    Q, K, V, G = (bf16_ref(x) for x in (q, k, v, do))
+    o_ref, lse_ref = oracle.attention_forward(Q, K, V, m, scale)
+    n = po.n_tokens
+    # the scores really do span many rescale thresholds along each row
+    assert lse_ref[:, n - 1].min() > 30.0 and lse_ref[:, 0].max() < 10.0
+    atol, rtol = (F32_ATOL, F32_RTOL) if dtype == "fp32" else (BF16_ATOL, BF16_RTOL)
+    assert_close(bf16_ref(o.cpu()), o_ref, atol, rtol, f"{name} O")
+    assert_close(lse.cpu().numpy()[:, :n], lse_ref[:, :n], atol, rtol, f"{name} LSE")
+    if dtype == "bf16":
+        # The backward reads LSE and never rescales.  At these score
+        # magnitudes its bf16 dS operand (0.4% rounding) is multiplied by
+        # key rows many times longer than N(0, 1/D) ones, and
+        # sum_j dS_ij = 0 cancels in dQ = scale sum_j dS_ij k_j: the
+        # gradients' error follows the conditioning, not the kernel, so
+        # only the fp32 check mode compares them here.
+        return
+    dq, dk, dv = pta.attn_bwd(qd, kd, vd, o, lse, dod, meta)
+    torch.cuda.synchronize()
+    dq_ref, dk_ref, dv_ref = oracle.attention_backward(Q, K, V, o_ref, lse_ref, G, m, scale)
+    assert_close(bf16_ref(dq.cpu()), dq_ref, atol, rtol, f"{name} dQ")
+    assert_close(bf16_ref(dk.cpu()), dk_ref, atol, rtol, f"{name} dK")
+    assert_close(bf16_ref(dv.cpu()), dv_ref, atol, rtol, f"{name} dV")
