@@ -4,7 +4,7 @@
 One step is one pass of the whole path over one synthetic rollout batch:
   host   tree_pack (C++ FFD trie build, compression, pre-order layout)
   H2D    subtree ends of every trie (pinned, async)
-  device tree_meta, tree_attn_fwd, tree_attn_bwd (delta, dK/dV, dQ)
+  device tree_meta, tree_attn_fwd, tree_attn_bwd (dQ with Delta, then dK/dV)
 Q, K, V and dO are resident in HBM before the timed region.  The loop is a
 steady-state pipeline: step k's device work is enqueued, then the host packs
 step k+1 while the GPU runs (the trie-count all-reduce of a data-parallel
@@ -42,11 +42,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-PHASES = ("meta", "fwd", "delta", "dkdv", "dq")
-PHASE_KERNEL = {"meta": "meta_finish", "fwd": "fwd_bf16_kernel", "delta": "delta_bf16_kernel",
-                "dkdv": "dkdv_bf16_kernel", "dq": "dq_bf16_kernel"}
-PHASE_SOURCE = {"meta": "meta.hip", "fwd": "fwd_bf16.hip", "delta": "bwd_bf16.hip", "dkdv": "bwd_bf16.hip",
-                "dq": "bwd_bf16.hip"}
+PHASES = ("meta", "fwd", "dq", "dkdv")  # in launch order; "dq" forms Delta too
+PHASE_KERNEL = {"meta": "meta_finish", "fwd": "fwd_bf16_kernel", "dkdv": "dkdv_bf16_kernel", "dq": "dq_bf16_kernel"}
+PHASE_SOURCE = {"meta": "meta.hip", "fwd": "fwd_bf16.hip", "dkdv": "bwd_bf16.hip", "dq": "bwd_bf16.hip"}
 # algorithmic FLOPs per visible pair and query head, in units of D
 PHASE_FLOPS_PER_PAIR_D = {"fwd": 4, "dkdv": 8, "dq": 6}
 
@@ -257,7 +255,7 @@ def main(argv=None):
                                              _ptr(b["se"]), _ptr(b["mws"]), L, w.hq, w.hkv, w.d, scale, 0, sptr))
             if E:
                 E[2].record(stream)
-            for j, ph in enumerate((pta.BWD_DELTA, pta.BWD_DKDV, pta.BWD_DQ)):
+            for j, ph in enumerate((pta.BWD_DQ_DELTA, pta.BWD_DKDV)):
                 pta._lib.check(lib.tree_attn_bwd_phase(
                     ph, _ptr(b["q"]), _ptr(b["k"]), _ptr(b["v"]), _ptr(b["o"]), _ptr(b["lse"]), _ptr(b["do"]),
                     _ptr(b["dq"]), _ptr(b["dk"]), _ptr(b["dv"]), _ptr(b["se"]), _ptr(b["mws"]), _ptr(b["bws"]),

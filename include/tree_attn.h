@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define TREE_ATTN_ABI_VERSION 4
+#define TREE_ATTN_ABI_VERSION 5
 
 /* status codes */
 #define TREE_OK 0
@@ -253,15 +253,19 @@ int tree_attn_bwd(const void* q, const void* k, const void* v, const void* o,
 /* One phase of tree_attn_bwd, for callers that time or schedule the
  * backward's kernels separately: TREE_BWD_DELTA computes Delta_i =
  * dO_i . O_i (and, for bf16, LSE_i / scale) into d_ws, in an internal
- * layout; TREE_BWD_DKDV writes dk and dv;
- * TREE_BWD_DQ writes dq; TREE_BWD_ALL runs all three in that order (same
- * as tree_attn_bwd).  DKDV and DQ read what a DELTA phase left in the same
- * d_ws, so a DELTA phase must precede them on the stream.  Other arguments and
- * errors as tree_attn_bwd; an unknown phase gives TREE_E_ARG. */
+ * layout; TREE_BWD_DKDV writes dk and dv; TREE_BWD_DQ writes dq;
+ * TREE_BWD_DQ_DELTA writes dq and leaves in d_ws what a DELTA phase would
+ * (for bf16 the dQ kernel computes Delta itself from o and dout; in the
+ * fp32 check mode it is the DELTA then the DQ phase).  DKDV and DQ read what
+ * a DELTA or DQ_DELTA phase left in the same d_ws, so one of those must
+ * precede them on the stream.  TREE_BWD_ALL (same as tree_attn_bwd) runs
+ * DQ_DELTA then DKDV for bf16, and DELTA, DKDV, DQ for fp32.  Other arguments
+ * and errors as tree_attn_bwd; an unknown phase gives TREE_E_ARG. */
 #define TREE_BWD_ALL 0
 #define TREE_BWD_DELTA 1
 #define TREE_BWD_DKDV 2
 #define TREE_BWD_DQ 3
+#define TREE_BWD_DQ_DELTA 4
 int tree_attn_bwd_phase(int32_t phase, const void* q, const void* k, const void* v, const void* o,
                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
                         const int32_t* d_se, const void* d_meta_ws, void* d_ws, size_t ws_bytes,

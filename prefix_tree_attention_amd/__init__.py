@@ -9,7 +9,7 @@ arguments into it.
 """
 
 from ._lib import (TreeAttnError, lib, library_path, DTYPE_BF16, DTYPE_FP32, BLOCK,  # noqa: F401
-                   BWD_ALL, BWD_DELTA, BWD_DKDV, BWD_DQ)
+                   BWD_ALL, BWD_DELTA, BWD_DKDV, BWD_DQ, BWD_DQ_DELTA)
 from .api import (  # noqa: F401
     PackedTrie,
     TreeMeta,

@@ -84,7 +84,7 @@ SIGNATURES = {
                                             c_vp, c_vp, c_vp]),
     "tree_rope": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i32, c_i32, ctypes.c_double, c_i32, c_i32, c_vp]),
 }
-BWD_ALL, BWD_DELTA, BWD_DKDV, BWD_DQ = 0, 1, 2, 3
+BWD_ALL, BWD_DELTA, BWD_DKDV, BWD_DQ, BWD_DQ_DELTA = 0, 1, 2, 3, 4
 
 _lock = threading.Lock()
 _lib = None

@@ -283,7 +283,7 @@ def attn_bwd(q, k, v, o, lse, do, meta: TreeMeta, scale: float | None = None, wo
 
 def attn_bwd_phase(phase: int, q, k, v, o, lse, do, dq, dk, dv, meta: TreeMeta, workspace, scale=None):
     """``tree_attn_bwd_phase`` into caller-provided outputs and workspace
-    (BWD_DELTA, BWD_DKDV, BWD_DQ or BWD_ALL); used to time the backward's
+    (BWD_DELTA, BWD_DKDV, BWD_DQ, BWD_DQ_DELTA or BWD_ALL); used to time the backward's
     kernels separately."""
     L, hq, d = q.shape
     hkv = k.shape[1]

@@ -240,9 +240,10 @@ hipError_t launch_bwd_f32(int phase, const float* q, const float* k, const float
                           const float* dout, float* dq, float* dk, float* dv, const int32_t* se,
                           const MetaPtrs& mp, float* delta, const AttnShape& sh, hipStream_t stream) {
     const int rows = int(sh.L) * sh.Hq;
-    if (phase == kPhaseAll || phase == kPhaseDelta)
+    if (phase == kPhaseAll || phase == kPhaseDelta || phase == kPhaseDqDelta)
         delta_f32_kernel<<<(rows + 3) / 4, 256, 0, stream>>>(o, dout, delta, int(sh.L), sh.Hq, sh.D);
     if (phase == kPhaseDelta) return hipGetLastError();
+    if (phase == kPhaseDqDelta) phase = kPhaseDq;
     switch (sh.D) {
         case 32: launch_f32_bwd_d<32>(phase, q, k, v, dout, lse, delta, dq, dk, dv, se, mp, sh, stream); break;
         case 64: launch_f32_bwd_d<64>(phase, q, k, v, dout, lse, delta, dq, dk, dv, se, mp, sh, stream); break;

@@ -9,8 +9,9 @@
 // over every sequence below it (AREAL-DTA notes, §3 问题形式化) with no
 // extra work.
 //
-// Three kernels:
-//   delta: Delta for every (token, query head).
+// Three kernels; the whole backward runs dq, then dkdv:
+//   delta: Delta for every (token, query head), for callers that run the
+//          phases one by one (the whole backward computes it inside dq).
 //   dkdv:  one workgroup per (pair of 128-key blocks, key/value head);
 //          wave w owns 64 keys and keeps their V^T operands in vector
 //          registers and their dK^T, dV^T accumulators in the 256
@@ -26,7 +27,9 @@
 //          operand read feeds two 32-key MFMAs.
 //   dq:    one workgroup per (128-query block, query head) like the forward:
 //            S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T,
-//          K^T again by transposing reads of the K tile.
+//          K^T again by transposing reads of the K tile.  In the whole
+//          backward it first forms Delta of its rows from the dO it holds
+//          and one read of O, and leaves -Delta and -LSE / scale for dkdv.
 // Score block b of a 64-row step covers rows 16b..16b+15; the gradient
 // products' k-step c pairs blocks 2c and 2c+1, whose accumulator lanes hold
 // rows 32c + 4g + 0..3 and 32c + 16 + 4g + 0..3 -- exactly the rows the
@@ -542,13 +545,13 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool kDelta>
 __global__ __launch_bounds__(kThreads, 2) void dq_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
-    bf16* __restrict__ dQ, const int32_t* __restrict__ se, const int32_t* __restrict__ q_order,
-    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ row_ent, int L, int Hq, int Hkv,
-    float scale_log2, float scale) {
+    const bf16* __restrict__ dO, const bf16* __restrict__ O, const float* __restrict__ LSE,
+    float* __restrict__ Delta, float* __restrict__ NLS, bf16* __restrict__ dQ, const int32_t* __restrict__ se,
+    const int32_t* __restrict__ q_order, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ row_ent,
+    int L, int Hq, int Hkv, float scale_log2, float scale) {
     using T = Tile<D>;
     constexpr int NS = D / 32, NT = D / 16;
     // K and V tiles and the keys' subtree ends, double-buffered
@@ -567,15 +570,24 @@ __global__ __launch_bounds__(kThreads, 2) void dq_bf16_kernel(
 
     bf16x8 qf[2][NS], gf[2][NS];
     float lse2[2], dlt[2];
+    u32x4 of[2][NS];  // O chunks matching gf, for Delta (kDelta)
+    float lse_raw[2];
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
         const int qi = qrow0 + 16 * qs + n;
-        lse2[qs] = LSE[int64_t(h) * L + qi] * kLog2e;
-        dlt[qs] = -Delta[int64_t(h) * L + qi];  // stored negated
+        const int64_t hr = int64_t(h) * L + qi;
+        const float lse = LSE[hr];
+        lse2[qs] = lse * kLog2e;
+        if constexpr (!kDelta) dlt[qs] = -Delta[hr];  // stored negated
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             qf[qs][s] = __builtin_bit_cast(bf16x8, ld16(Q + int64_t(qi) * q_stride + int64_t(h) * D + 32 * s + 8 * g));
             gf[qs][s] = __builtin_bit_cast(bf16x8, ld16(dO + int64_t(qi) * q_stride + int64_t(h) * D + 32 * s + 8 * g));
+        }
+        if constexpr (kDelta) {
+            lse_raw[qs] = lse;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) of[qs][s] = ld16(O + int64_t(qi) * q_stride + int64_t(h) * D + 32 * s + 8 * g);
         }
     }
     f32x4 dq[2][NT];
@@ -603,6 +615,34 @@ __global__ __launch_bounds__(kThreads, 2) void dq_bf16_kernel(
         if (lane < 16) dma4(se + kbase + 16 * wave, 4u * lane, lds_addr(serow(buf) + 64 * wave));
     };
     if (nsteps > 0) issue(0, 0);
+    if constexpr (kDelta) {
+        // Delta_i = dO_i . O_i from the dO chunks this lane already holds
+        // and the matching O chunks, formed while the first tiles load: the
+        // four lanes n + 16 g of a query hold its D elements, so two
+        // exchanges finish the sum.  Lane g = 0 leaves -Delta and
+        // -LSE / scale for the dK/dV kernel.
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) {
+            float acc = 0.f;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const u32x4 a = of[qs][s], b = __builtin_bit_cast(u32x4, gf[qs][s]);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    acc += bf16_to_float(a[w] & 0xffffu) * bf16_to_float(b[w] & 0xffffu);
+                    acc += bf16_to_float(a[w] >> 16) * bf16_to_float(b[w] >> 16);
+                }
+            }
+            acc += __shfl_xor(acc, 16);
+            acc += __shfl_xor(acc, 32);
+            dlt[qs] = acc;
+            if (g == 0) {
+                const int64_t hr = int64_t(h) * L + qrow0 + 16 * qs + n;
+                Delta[hr] = -acc;
+                NLS[hr] = -lse_raw[qs] / scale;
+            }
+        }
+    }
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
         consume(lse2[qs]);
@@ -713,16 +753,24 @@ hipError_t launch_bwd_d(int phase, const bf16* Q, const bf16* K, const bf16* V, 
     const int64_t rows = int64_t(L) * sh.Hq;
     const float sl2 = sh.scale * kLog2e;
     float* nls = delta + rows;  // second half of the workspace
-    if (phase == kPhaseAll || phase == kPhaseDelta)
+    const unsigned dq_grid = unsigned(sh.nb) * unsigned(sh.Hq);
+    if (phase == kPhaseDelta)
         delta_bf16_kernel<D><<<dim3(unsigned((L + 256 / (D / 8) - 1) / (256 / (D / 8))), unsigned(sh.Hq)), 256, 0,
                                stream>>>(O, dO, lse, delta, nls, 1.0f / sh.scale, L, sh.Hq);
+    // the whole backward: dQ first, computing Delta itself and leaving it
+    // (with -LSE / scale) for dK/dV, which saves a pass over O and dO
+    if (phase == kPhaseAll || phase == kPhaseDqDelta)
+        dq_bf16_kernel<D, true><<<dq_grid, kThreads, 0, stream>>>(Q, K, V, dO, O, lse, delta, nls, dQ, se,
+                                                                   mp.q_order, mp.row_ptr, mp.row_ent, L, sh.Hq,
+                                                                   sh.Hkv, sl2, sh.scale);
     if (phase == kPhaseAll || phase == kPhaseDkdv)
         dkdv_bf16_kernel<D><<<unsigned((sh.nb + 1) / 2) * unsigned(sh.Hkv), kThreads, 0, stream>>>(
             Q, K, V, dO, nls, delta, dK, dV, se, mp.p_order, mp.blk_min, mp.blk_max, L, sh.Hq, sh.Hkv, sl2,
             sh.scale);
-    if (phase == kPhaseAll || phase == kPhaseDq)
-        dq_bf16_kernel<D><<<unsigned(sh.nb) * unsigned(sh.Hq), kThreads, 0, stream>>>(
-            Q, K, V, dO, lse, delta, dQ, se, mp.q_order, mp.row_ptr, mp.row_ent, L, sh.Hq, sh.Hkv, sl2, sh.scale);
+    if (phase == kPhaseDq)
+        dq_bf16_kernel<D, false><<<dq_grid, kThreads, 0, stream>>>(Q, K, V, dO, O, lse, delta, nls, dQ, se,
+                                                                    mp.q_order, mp.row_ptr, mp.row_ent, L, sh.Hq,
+                                                                    sh.Hkv, sl2, sh.scale);
     return hipGetLastError();
 }
 

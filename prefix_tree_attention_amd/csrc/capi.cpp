@@ -133,7 +133,7 @@ int tree_attn_bwd_phase(int32_t phase, const void* q, const void* k, const void*
                         const float* lse, const void* dout, void* dq, void* dk, void* dv, const int32_t* d_se,
                         const void* d_meta_ws, void* d_ws, size_t ws_bytes, int64_t L, int32_t Hq, int32_t Hkv,
                         int32_t D, float scale, int32_t dtype, void* stream) {
-    if (phase < TREE_BWD_ALL || phase > TREE_BWD_DQ)
+    if (phase < TREE_BWD_ALL || phase > TREE_BWD_DQ_DELTA)
         return set_error(TREE_E_ARG, "tree_attn_bwd: unknown phase %d", phase);
     if (int rc = check_attn("tree_attn_bwd", L, Hq, Hkv, D, scale, dtype)) return rc;
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !d_se || !d_meta_ws || !d_ws)

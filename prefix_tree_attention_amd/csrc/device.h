@@ -86,7 +86,7 @@ inline MetaPtrs meta_ptrs(const void* ws, int64_t L) {
 }
 
 // Backward phases (TREE_BWD_* of the public header).
-constexpr int kPhaseAll = 0, kPhaseDelta = 1, kPhaseDkdv = 2, kPhaseDq = 3;
+constexpr int kPhaseAll = 0, kPhaseDelta = 1, kPhaseDkdv = 2, kPhaseDq = 3, kPhaseDqDelta = 4;
 
 // Problem shape shared by the attention launchers.
 struct AttnShape {

@@ -99,3 +99,47 @@ def test_hip_graph_capture_and_replay():
         torch.cuda.synchronize()
         for name, x, y in zip(("O", "LSE", "dQ", "dK", "dV"), out, ref):
             assert torch.equal(x, y), f"replay {rep}: {name}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_phases_one_by_one_match_the_whole_backward(dtype):
+    """tree_attn_bwd_phase: DELTA, DKDV, DQ run one by one (dQ reading the
+    workspace the Delta kernel wrote) and DQ_DELTA, DKDV (the dQ kernel
+    forming Delta itself, as the whole backward does) leave the same
+    workspace and the same gradients as tree_attn_bwd.  Delta's two
+    summation orders differ in the last bits, so the workspaces agree to
+    fp32 rounding and the gradients to the bf16 bound (fp32: 1e-5)."""
+    import numpy as np
+    from gpu_common import BF16_ATOL, BF16_RTOL
+    torch = torch_cuda()
+    ids, mask, M = workloads.small_workload("multiturn-small")
+    (pl,), _ = pta.pack(ids, mask, M)
+    hq, hkv, d = (4, 2, 64) if dtype == "fp32" else (8, 2, 128)
+    std = 1.0 if dtype == "fp32" else 1.0 / math.sqrt(d)
+    q, k, v, do = workloads.attention_inputs(pl.L, hq, hkv, d, dtype, std, 4343)
+    announce(f"phases {dtype} L={pl.L}")
+    meta = pta.tree_meta(pl.subtree_end)
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    o, lse = pta.attn_fwd(qd, kd, vd, meta)
+    ref = pta.attn_bwd(qd, kd, vd, o, lse, dod, meta)
+    code = pta.DTYPE_FP32 if dtype == "fp32" else pta.DTYPE_BF16
+    nbytes = pta.bwd_workspace_bytes(pl.L, hq, d, code)
+    runs = {}
+    for name, phases in (("split", (pta.BWD_DELTA, pta.BWD_DKDV, pta.BWD_DQ)),
+                         ("fused", (pta.BWD_DQ_DELTA, pta.BWD_DKDV))):
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        for ph in phases:
+            pta.attn_bwd_phase(ph, qd, kd, vd, o, lse, dod, dq, dk, dv, meta, ws)
+        torch.cuda.synchronize()
+        runs[name] = (ws, (dq, dk, dv))
+    n = 2 * pl.L * hq if dtype == "bf16" else pl.L * hq  # bf16 keeps -Delta and -LSE / scale, fp32 Delta
+    wa = runs["split"][0][: 4 * n].view(torch.float32).cpu().numpy()
+    wb = runs["fused"][0][: 4 * n].view(torch.float32).cpu().numpy()
+    fin = np.isfinite(wa)
+    assert np.array_equal(fin, np.isfinite(wb)) and np.array_equal(wa[~fin], wb[~fin])
+    assert np.allclose(wb[fin], wa[fin], rtol=1e-5, atol=1e-6)
+    atol, rtol = (1e-5, 1e-5) if dtype == "fp32" else (BF16_ATOL, BF16_RTOL)
+    for run in ("split", "fused"):
+        for name, x, y in zip(("dQ", "dK", "dV"), runs[run][1], ref):
+            assert torch.allclose(x.float(), y.float(), atol=atol, rtol=rtol), f"{run} {name}"

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
     for n in sorted(names):
         assert hasattr(L, n), n
     assert set(_lib.SIGNATURES) == names
-    assert L.tree_abi_version() == 4
+    assert L.tree_abi_version() == 5
 
 
 def _compare(tries_lib, tries_or):
