@@ -43,7 +43,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PHASES = ("meta", "fwd", "dq", "dkdv")  # in launch order; "dq" forms Delta too
-PHASE_KERNEL = {"meta": "meta_finish", "fwd": "fwd_bf16_kernel", "dkdv": "dkdv_bf16_kernel", "dq": "dq_bf16_kernel"}
+PHASE_KERNEL = {"meta": "meta_lists", "fwd": "fwd_bf16_kernel", "dkdv": "dkdv_bf16_kernel", "dq": "dq_bf16_kernel"}
 PHASE_SOURCE = {"meta": "meta.hip", "fwd": "fwd_bf16.hip", "dkdv": "bwd_bf16.hip", "dq": "bwd_bf16.hip"}
 # algorithmic FLOPs per visible pair and query head, in units of D
 PHASE_FLOPS_PER_PAIR_D = {"fwd": 4, "dkdv": 8, "dq": 6}
@@ -200,10 +200,7 @@ def main(argv=None):
         se_i64 = tr.subtree_end.astype(np.int64)
         real = se_i64 >= 0
         pairs_per_trie.append(int((se_i64[real] - np.arange(tr.L)[real] + 1).sum()))
-    parts = [workloads.attention_inputs(tr.L, w.hq, w.hkv, w.d, "bf16", w.qkv_std, 1_000_000 + i)
-             for i, tr in enumerate(tries)]
-    q, k, v, do = (torch.cat([p_[j] for p_ in parts]) for j in range(4))
-    del parts
+    q, k, v, do = workloads.batch_attention_inputs(lengths, w.hq, w.hkv, w.d, "bf16", w.qkv_std)
     L = len(se_cat)
     nb = L // 128
     bufs.append({
@@ -305,6 +302,21 @@ def main(argv=None):
 
     n_pairs = stats["n_pairs"]
     tokens = stats["tree_tokens"]
+    # 128x128 tile accounting: the packer's host counts (tree_pack_stats),
+    # cross-checked against the classes tree_meta wrote on the device for the
+    # last step; the skip rate is against dense causal attention of each trie
+    tc = bufs[0]["tc"]
+    dev_full, dev_partial = int((tc == 2).sum()), int((tc == 1).sum())
+    if (dev_full, dev_partial) != (stats["tiles_full"], stats["tiles_partial"]):
+        raise SystemExit(f"tile classes on the device ({dev_full} full, {dev_partial} partial) differ from the "
+                         f"packer's counts ({stats['tiles_full']}, {stats['tiles_partial']})")
+    causal = stats["tiles_causal"]
+    tiles = {"full": stats["tiles_full"], "partial": stats["tiles_partial"],
+             "empty": causal - stats["tiles_full"] - stats["tiles_partial"], "dense_causal": causal,
+             "skip_rate_vs_causal": round(1.0 - (stats["tiles_full"] + stats["tiles_partial"]) / causal, 4),
+             "visible_fraction_of_nonempty_area": round(n_pairs / (128.0 * 128.0 * (stats["tiles_full"]
+                                                                                 + stats["tiles_partial"])), 4)}
+    log(f"tiles: {tiles}")
     useful_flop = 14.0 * w.d * w.hq * n_pairs
     useful_tflops = useful_flop / sec_per_step / 1e12
     dom = max(PHASES, key=lambda p: avg[p])
@@ -346,6 +358,7 @@ def main(argv=None):
                    "hkv": w.hkv, "head_dim": w.d, "max_tokens_per_mb": w.max_tokens_per_mb,
                    "tree_tokens": tokens, "pairs": n_pairs, "pack": a.pack, "parallelism": "single-gpu"},
         "roofline": roof,
+        "tiles": tiles,
     }
     if not a.no_cpu_baseline:
         log("cpu baseline (oracle) ...")

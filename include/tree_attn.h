@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define TREE_ATTN_ABI_VERSION 5
+#define TREE_ATTN_ABI_VERSION 6
 
 /* status codes */
 #define TREE_OK 0
@@ -101,6 +101,15 @@ typedef struct {
                                     section 指标与监控)                          */
     int64_t n_pairs;             /* visible (query,key) pairs, all tries        */
     int64_t unpacked_pairs;      /* sum over sequences of l*(l+1)/2             */
+    /* 128x128 tiles of the block mask (guide, section 两种注意力实现), summed
+       over tries: full (every query of the tile sees every key), partial
+       (some but not all), and the lower-triangular tile count of dense
+       causal attention over each trie, nb (nb + 1) / 2 with nb = L / 128.
+       The tile-skip rate against dense causal is
+       1 - (tiles_full + tiles_partial) / tiles_causal. */
+    int64_t tiles_full;
+    int64_t tiles_partial;
+    int64_t tiles_causal;
 } tree_pack_stats_t;
 
 /* Pack a padded batch.  ids [B,S] int32 and mask [B,S] uint8 are HOST

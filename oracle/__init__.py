@@ -47,6 +47,7 @@ from .packing import (  # noqa: F401
 from .attention import (  # noqa: F401
     attention_forward,
     attention_backward,
+    attention_delta,
     attention_forward_rows,
     attention_dq_rows,
     attention_dkdv_cols,

@@ -111,6 +111,16 @@ def attention_backward(q, k, v, o, lse, do, mask, scale, dtype=np.float64, row_c
     return dq, dk, dv
 
 
+def attention_delta(o, do, dtype=np.float64):
+    """The backward's row term Delta_i = dO_i . O_i for every token and
+    query head, laid out [Hq, L] like LSE.  It is the quantity the closed-form
+    gradient subtracts from dP (dS = P (dP - Delta)); by the softmax identity
+    it equals sum_j P[i, j] dP[i, j].  Pads (O = 0) give 0."""
+    o = np.asarray(o, dtype)
+    do = np.asarray(do, dtype)
+    return (o * do).sum(axis=2).T.copy()
+
+
 # ---------------------------------------------------------------------------
 # one-row / one-column forms, for sampled checks at sizes where the dense
 # problem does not fit a CPU budget.  Same definitions, one output at a time.

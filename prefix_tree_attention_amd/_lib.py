@@ -52,6 +52,7 @@ class PackStats(ctypes.Structure):
     _fields_ = [
         ("n_tries", c_i64), ("original_tokens", c_i64), ("tree_tokens", c_i64),
         ("tree_token_ratio", ctypes.c_double), ("n_pairs", c_i64), ("unpacked_pairs", c_i64),
+        ("tiles_full", c_i64), ("tiles_partial", c_i64), ("tiles_causal", c_i64),
     ]
 
 

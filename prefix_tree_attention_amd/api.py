@@ -245,22 +245,33 @@ def _check_qkv(q, k, v, meta):
         raise TreeAttnError(-5, "q/k/v shapes or dtypes disagree")
 
 
-def attn_fwd(q, k, v, meta: TreeMeta, scale: float | None = None):
-    """``tree_attn_fwd``: returns (o [L,Hq,D], lse [Hq,L] fp32)."""
+def _check_out(name, t, like_shape, like_dtype, device):
+    if t.shape != like_shape or t.dtype != like_dtype or not t.is_contiguous() or t.device != device:
+        raise TreeAttnError(-5, f"{name} must be a contiguous {like_dtype} tensor of shape {tuple(like_shape)} "
+                                f"on {device}")
+    return t
+
+
+def attn_fwd(q, k, v, meta: TreeMeta, scale: float | None = None, o=None, lse=None):
+    """``tree_attn_fwd``: returns (o [L,Hq,D], lse [Hq,L] fp32).  ``o`` and
+    ``lse`` may be given (caller-owned outputs, fully overwritten)."""
     torch = _torch()
     _check_qkv(q, k, v, meta)
     L, hq, d = q.shape
     hkv = k.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    o = torch.empty_like(q)
-    lse = torch.empty((hq, L), dtype=torch.float32, device=q.device)
+    o = torch.empty_like(q) if o is None else _check_out("o", o, q.shape, q.dtype, q.device)
+    lse = (torch.empty((hq, L), dtype=torch.float32, device=q.device) if lse is None
+           else _check_out("lse", lse, (hq, L), torch.float32, q.device))
     check(lib().tree_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(meta.se), _ptr(meta.ws), L, hq,
                               hkv, d, scale, _dtype_code(q), _stream(q.device)))
     return o, lse
 
 
-def attn_bwd(q, k, v, o, lse, do, meta: TreeMeta, scale: float | None = None, workspace=None):
-    """``tree_attn_bwd``: returns (dq, dk, dv)."""
+def attn_bwd(q, k, v, o, lse, do, meta: TreeMeta, scale: float | None = None, workspace=None, dq=None, dk=None,
+             dv=None):
+    """``tree_attn_bwd``: returns (dq, dk, dv).  The outputs may be given
+    (caller-owned, fully overwritten), and so may the workspace."""
     torch = _torch()
     _check_qkv(q, k, v, meta)
     for name, t in (("o", o), ("do", do)):
@@ -272,9 +283,11 @@ def attn_bwd(q, k, v, o, lse, do, meta: TreeMeta, scale: float | None = None, wo
     code = _dtype_code(q)
     nbytes = bwd_workspace_bytes(L, hq, d, code)
     ws = workspace if workspace is not None else torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    dq = torch.empty_like(q)
-    dk = torch.empty_like(k)
-    dv = torch.empty_like(v)
+    dq = torch.empty_like(q) if dq is None else _check_out("dq", dq, q.shape, q.dtype, q.device)
+    dk = torch.empty_like(k) if dk is None else _check_out("dk", dk, k.shape, k.dtype, k.device)
+    dv = torch.empty_like(v) if dv is None else _check_out("dv", dv, v.shape, v.dtype, v.device)
+    if ws.numel() < nbytes:
+        raise TreeAttnError(-6, f"workspace holds {ws.numel()} bytes, {nbytes} needed")
     check(lib().tree_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse.contiguous()), _ptr(do), _ptr(dq),
                               _ptr(dk), _ptr(dv), _ptr(meta.se), _ptr(meta.ws), _ptr(ws), ws.numel(), L, hq, hkv,
                               d, scale, code, _stream(q.device)))

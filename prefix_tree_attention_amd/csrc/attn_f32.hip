@@ -185,9 +185,10 @@ __global__ __launch_bounds__(kRows) void dkv_f32_kernel(const float* __restrict_
 // delta[h][i] = dO[i,h,:] . O[i,h,:]; one wave per (token, head) row.
 __global__ __launch_bounds__(256) void delta_f32_kernel(const float* __restrict__ O, const float* __restrict__ dO,
                                                         float* __restrict__ delta, int L, int Hq, int D) {
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-    if (row >= L * Hq) return;
-    const int i = row / Hq, h = row % Hq;
+    const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= int64_t(L) * Hq) return;
+    const int i = int(row / Hq), h = int(row % Hq);
     float acc = 0.f;
     for (int d = lane; d < D; d += 64) acc += O[int64_t(row) * D + d] * dO[int64_t(row) * D + d];
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
@@ -239,9 +240,9 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
 hipError_t launch_bwd_f32(int phase, const float* q, const float* k, const float* v, const float* o, const float* lse,
                           const float* dout, float* dq, float* dk, float* dv, const int32_t* se,
                           const MetaPtrs& mp, float* delta, const AttnShape& sh, hipStream_t stream) {
-    const int rows = int(sh.L) * sh.Hq;
+    const int64_t rows = sh.L * sh.Hq;
     if (phase == kPhaseAll || phase == kPhaseDelta || phase == kPhaseDqDelta)
-        delta_f32_kernel<<<(rows + 3) / 4, 256, 0, stream>>>(o, dout, delta, int(sh.L), sh.Hq, sh.D);
+        delta_f32_kernel<<<dim3(unsigned((rows + 3) / 4)), 256, 0, stream>>>(o, dout, delta, int(sh.L), sh.Hq, sh.D);
     if (phase == kPhaseDelta) return hipGetLastError();
     if (phase == kPhaseDqDelta) phase = kPhaseDq;
     switch (sh.D) {

@@ -43,6 +43,8 @@ int check_attn(const char* fn, int64_t L, int32_t Hq, int32_t Hkv, int32_t D, fl
     if (int rc = check_L(L, fn)) return rc;
     if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Hq > 4096)
         return set_error(TREE_E_ARG, "%s: bad head counts Hq=%d Hkv=%d (need Hq %% Hkv == 0)", fn, Hq, Hkv);
+    if (L * int64_t(Hq) >= (int64_t(1) << 31))
+        return set_error(TREE_E_ARG, "%s: L * Hq = %lld rows exceeds 2^31 - 1", fn, (long long)(L * int64_t(Hq)));
     if (dtype == TREE_DTYPE_BF16) {
         if (D != 64 && D != 128) return set_error(TREE_E_ARG, "%s: bf16 path supports D in {64,128}, got %d", fn, D);
     } else if (dtype == TREE_DTYPE_FP32) {

@@ -249,6 +249,30 @@ void flatten(const RadixTrie& t, const Seqs& S, int64_t L, int32_t pad_id, Packe
     }
 }
 
+// Nonempty 128x128 tiles of one trie, split into full and partial, from the
+// subtree ends alone.  Key j is visible to query i iff j <= i <= se[j], and
+// subtree intervals are laminar, so key block kb's nonempty tiles are the
+// query blocks kb .. max_se / 128 (the diagonal one partial), and the tile
+// of query block qb > kb is full exactly when every key of kb is visible to
+// every query of qb: min_se >= 128 qb + 127.  Pads (se = -1) sit after the
+// real tokens and make their blocks' minimum -1.
+void count_tiles(const PackedTrie& t, int64_t& full, int64_t& partial) {
+    const int64_t nb = t.L / TREE_BLOCK;
+    for (int64_t kb = 0; kb < nb; ++kb) {
+        int32_t lo = INT32_MAX, hi = -1;
+        for (int64_t j = kb * TREE_BLOCK; j < (kb + 1) * TREE_BLOCK; ++j) {
+            lo = std::min(lo, t.subtree_end[size_t(j)]);
+            hi = std::max(hi, t.subtree_end[size_t(j)]);
+        }
+        if (hi < 0) continue;  // no real key
+        const int64_t nonempty = hi / TREE_BLOCK - kb + 1;
+        const int64_t last_full = lo >= TREE_BLOCK - 1 ? (int64_t(lo) - (TREE_BLOCK - 1)) / TREE_BLOCK : -1;
+        const int64_t f = std::max<int64_t>(0, last_full - kb);
+        full += f;
+        partial += nonempty - f;
+    }
+}
+
 }  // namespace
 
 struct tree_pack {
@@ -338,7 +362,7 @@ int tree_pack_ordered(const int32_t* ids, const uint8_t* mask, int64_t B, int64_
         }
         std::unique_ptr<struct tree_pack> p(new struct tree_pack());
         p->tries.resize(tries.size());
-        int64_t tree_tokens = 0, pairs = 0, unpacked = 0;
+        int64_t tree_tokens = 0, pairs = 0, unpacked = 0, full = 0, partial = 0, causal = 0;
         for (size_t i = 0; i < tries.size(); ++i) {
             const int64_t n = tries[i]->tokens;
             const int64_t L = pad_to_maximum ? M : (n + block_size - 1) / block_size * block_size;
@@ -346,6 +370,8 @@ int tree_pack_ordered(const int32_t* ids, const uint8_t* mask, int64_t B, int64_
             tries[i].reset();
             tree_tokens += n;
             pairs += p->tries[i].n_pairs;
+            count_tiles(p->tries[i], full, partial);
+            causal += (L / block_size) * (L / block_size + 1) / 2;
         }
         for (int64_t r = 0; r < B; ++r) unpacked += seqs.len(int32_t(r)) * (seqs.len(int32_t(r)) + 1) / 2;
         p->stats.n_tries = int64_t(p->tries.size());
@@ -354,6 +380,9 @@ int tree_pack_ordered(const int32_t* ids, const uint8_t* mask, int64_t B, int64_
         p->stats.tree_token_ratio = original ? double(tree_tokens) / double(original) : 0.0;
         p->stats.n_pairs = pairs;
         p->stats.unpacked_pairs = unpacked;
+        p->stats.tiles_full = full;
+        p->stats.tiles_partial = partial;
+        p->stats.tiles_causal = causal;
         p->B = B;
         p->S = S;
         *out = p.release();

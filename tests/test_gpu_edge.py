@@ -20,21 +20,15 @@ import pytest
 import oracle
 import workloads
 import prefix_tree_attention_amd as pta
-from gpu_common import BF16_ATOL, BF16_RTOL, F32_ATOL, F32_RTOL, announce, assert_close, bf16_ref, torch_cuda
+from checks import assert_within_bound, conditioned_grad_bounds
+from gpu_common import (BF16_ATOL, BF16_RTOL, F32_ATOL, F32_RTOL, announce, assert_attn_close, assert_close, bf16_ref,
+                        grad_floor, run_attention, torch_cuda)
 
 pytestmark = pytest.mark.gpu
 
 
 def _cases():
-    rng = np.random.default_rng(77)
-    one = [np.array([5], np.int32)]
-    seq = rng.integers(1, 1000, 300).astype(np.int32)
-    copies = [seq, seq.copy(), seq.copy()]
-    a = rng.integers(1, 1000, 100).astype(np.int32)
-    full = [np.concatenate([a, rng.integers(1, 1000, 100)]).astype(np.int32),
-            np.concatenate([a[:44], rng.integers(1000, 2000, 56)]).astype(np.int32)]  # 200 + 56 = 256
-    long = [rng.integers(1, 1000, 1000).astype(np.int32)]
-    return {"one-token": (one, 128), "three-copies": (copies, 384), "full-trie": (full, 256), "causal-1000": (long, 1024)}
+    return workloads.edge_layouts()
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
@@ -55,8 +49,7 @@ def test_degenerate_layouts(name, dtype):
     q, k, v, do = workloads.attention_inputs(pl.L, hq, hkv, d, dtype, std, 31)
     meta = pta.tree_meta(pl.subtree_end)
     qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
-    o, lse = pta.attn_fwd(qd, kd, vd, meta)
-    dq, dk, dv = pta.attn_bwd(qd, kd, vd, o, lse, dod, meta)
+    o, lse, dq, dk, dv = run_attention(torch, qd, kd, vd, dod, meta)
     torch.cuda.synchronize()
     m = oracle.dense_ancestor_mask(po)
     scale = 1.0 / math.sqrt(d)
@@ -64,13 +57,20 @@ def test_degenerate_layouts(name, dtype):
     o_ref, lse_ref = oracle.attention_forward(Q, K, V, m, scale)
     dq_ref, dk_ref, dv_ref = oracle.attention_backward(Q, K, V, o_ref, lse_ref, G, m, scale)
     atol, rtol = (F32_ATOL, F32_RTOL) if dtype == "fp32" else (BF16_ATOL, BF16_RTOL)
-    assert_close(bf16_ref(o.cpu()), o_ref, atol, rtol, f"{name} O")
+    assert_attn_close(bf16_ref(o.cpu()), o_ref, atol, rtol, f"{name} O")
     n = po.n_tokens
     assert_close(lse.cpu().numpy()[:, :n], lse_ref[:, :n], atol, rtol, f"{name} LSE")
     assert np.isneginf(lse.cpu().numpy()[:, n:]).all()
-    assert_close(bf16_ref(dq.cpu()), dq_ref, atol, rtol, f"{name} dQ")
-    assert_close(bf16_ref(dk.cpu()), dk_ref, atol, rtol, f"{name} dK")
-    assert_close(bf16_ref(dv.cpu()), dv_ref, atol, rtol, f"{name} dV")
+    if name == "one-token":
+        # one visible key: P = 1, so dS = P (dP - Delta) = 0 and dQ = dK = 0
+        # exactly; the kernels leave only the rounding of dP - Delta (O is V_0
+        # rounded), far below any input's scale.  Nothing to normalise by.
+        assert np.abs(dq_ref).max() < 1e-12 and np.abs(dk_ref).max() < 1e-12
+        assert float(dq.abs().max()) < 1e-6 and float(dk.abs().max()) < 1e-6
+    else:
+        assert_attn_close(bf16_ref(dq.cpu()), dq_ref, atol, rtol, f"{name} dQ", grad_floor(dtype))
+        assert_attn_close(bf16_ref(dk.cpu()), dk_ref, atol, rtol, f"{name} dK", grad_floor(dtype))
+    assert_attn_close(bf16_ref(dv.cpu()), dv_ref, atol, rtol, f"{name} dV")
     if name == "one-token":
         g = hq // hkv
         assert np.allclose(o_ref[0], np.repeat(V[0], g, axis=0))  # O_0 = V_0 of each head's key/value head
@@ -98,17 +98,7 @@ def test_forward_reference_moves_within_a_row(name, dtype):
     hq, hkv, d = (4, 2, 64) if dtype == "fp32" else (8, 2, 128)
     L = pl.L
     announce(f"reference moves {name} {dtype} L={L}")
-    g = torch.Generator().manual_seed(5150)
-    u = torch.randn(d, generator=g, dtype=torch.float64)
-    u /= u.norm()
-    a, c_max = 30.0, 1.5 * math.sqrt(d)
-    c = torch.linspace(0.0, c_max, L, dtype=torch.float64)
-    q = a * u + 0.5 * torch.randn(L, hq, d, generator=g, dtype=torch.float64)
-    k = c[:, None, None] * u + 0.5 * torch.randn(L, hkv, d, generator=g, dtype=torch.float64)
-    v = torch.randn(L, hkv, d, generator=g, dtype=torch.float64)
-    do = torch.randn(L, hq, d, generator=g, dtype=torch.float64)
-    tdt = torch.float32 if dtype == "fp32" else torch.bfloat16
-    q, k, v, do = (x.to(tdt) for x in (q, k, v, do))
+    q, k, v, do = workloads.score_ramp_inputs(L, hq, hkv, d, dtype)
     meta = pta.tree_meta(pl.subtree_end)
     qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
     o, lse = pta.attn_fwd(qd, kd, vd, meta)
@@ -121,19 +111,23 @@ def test_forward_reference_moves_within_a_row(name, dtype):
     # the scores really do span many rescale thresholds along each row
     assert lse_ref[:, n - 1].min() > 30.0 and lse_ref[:, 0].max() < 10.0
     atol, rtol = (F32_ATOL, F32_RTOL) if dtype == "fp32" else (BF16_ATOL, BF16_RTOL)
-    assert_close(bf16_ref(o.cpu()), o_ref, atol, rtol, f"{name} O")
+    assert_attn_close(bf16_ref(o.cpu()), o_ref, atol, rtol, f"{name} O")
     assert_close(lse.cpu().numpy()[:, :n], lse_ref[:, :n], atol, rtol, f"{name} LSE")
-    if dtype == "bf16":
-        # The backward reads LSE and never rescales.  At these score
-        # magnitudes its bf16 dS operand (0.4% rounding) is multiplied by
-        # key rows many times longer than N(0, 1/D) ones, and
-        # sum_j dS_ij = 0 cancels in dQ = scale sum_j dS_ij k_j: the
-        # gradients' error follows the conditioning, not the kernel, so
-        # only the fp32 check mode compares them here.
-        return
     dq, dk, dv = pta.attn_bwd(qd, kd, vd, o, lse, dod, meta)
     torch.cuda.synchronize()
     dq_ref, dk_ref, dv_ref = oracle.attention_backward(Q, K, V, o_ref, lse_ref, G, m, scale)
-    assert_close(bf16_ref(dq.cpu()), dq_ref, atol, rtol, f"{name} dQ")
-    assert_close(bf16_ref(dk.cpu()), dk_ref, atol, rtol, f"{name} dK")
-    assert_close(bf16_ref(dv.cpu()), dv_ref, atol, rtol, f"{name} dV")
+    if dtype == "bf16":
+        # The backward reads LSE and never rescales.  At these score
+        # magnitudes every key shares a large component along u, so
+        # dQ = scale sum_j dS_ij k_j is a small difference of large terms
+        # (sum_j dS_ij = 0) and the bf16 rounding of dS shows through in
+        # proportion to that conditioning, not to |dQ|.  The bound per entry
+        # follows the kernel's roundings (checks.conditioned_grad_bounds).
+        bq, bk, bv = conditioned_grad_bounds(Q, K, V, G, o_ref, lse_ref, m, scale)
+        assert_within_bound(bf16_ref(dq.cpu()), dq_ref, bq, 3.0, f"{name} dQ")
+        assert_within_bound(bf16_ref(dk.cpu()), dk_ref, bk, 3.0, f"{name} dK")
+        assert_within_bound(bf16_ref(dv.cpu()), dv_ref, bv, 3.0, f"{name} dV")
+        return
+    assert_attn_close(bf16_ref(dq.cpu()), dq_ref, atol, rtol, f"{name} dQ")
+    assert_attn_close(bf16_ref(dk.cpu()), dk_ref, atol, rtol, f"{name} dK")
+    assert_attn_close(bf16_ref(dv.cpu()), dv_ref, atol, rtol, f"{name} dV")

@@ -13,8 +13,8 @@ import pytest
 import oracle
 import workloads
 import prefix_tree_attention_amd as pta
-from gpu_common import (BF16_ATOL, BF16_RTOL, F32_ATOL, F32_RTOL, announce, assert_close, bf16_ref,
-                        sample_rows, small_cases, torch_cuda)
+from gpu_common import (BF16_ATOL, BF16_RTOL, F32_ATOL, F32_RTOL, announce, assert_attn_close, assert_close, bf16_ref,
+                        run_attention, sample_rows, small_cases, torch_cuda)
 
 pytestmark = pytest.mark.gpu
 
@@ -23,7 +23,7 @@ def _run_fwd(torch, p_lib, hq, hkv, d, dtype, std, seed, scale=None):
     q, k, v, _ = workloads.attention_inputs(p_lib.L, hq, hkv, d, dtype, std, seed, backward=False)
     meta = pta.tree_meta(p_lib.subtree_end)
     qd, kd, vd = (t.cuda() for t in (q, k, v))
-    o, lse = pta.attn_fwd(qd, kd, vd, meta, scale)
+    o, lse = run_attention(torch, qd, kd, vd, None, meta, scale)
     torch.cuda.synchronize()
     return q, k, v, o.cpu(), lse.cpu()
 
@@ -39,7 +39,7 @@ def _full_check(torch, name, ids, mask, M, hq, hkv, d, dtype, seed):
         o_ref, lse_ref = oracle.attention_forward(bf16_ref(q), bf16_ref(k), bf16_ref(v), m, 1.0 / math.sqrt(d))
         atol, rtol = (F32_ATOL, F32_RTOL) if dtype == "fp32" else (BF16_ATOL, BF16_RTOL)
         assert np.isfinite(o.float().numpy()).all()
-        assert_close(bf16_ref(o), o_ref, atol, rtol, f"{name}[{t}] O")
+        assert_attn_close(bf16_ref(o), o_ref, atol, rtol, f"{name}[{t}] O")
         assert_close(lse.numpy(), lse_ref, atol, rtol, f"{name}[{t}] LSE")
         n = po.n_tokens
         assert (o[n:].float() == 0).all() and np.isneginf(lse[:, n:].numpy()).all()
@@ -81,7 +81,7 @@ def test_fwd_scale_argument():
     q, k, v, o, lse = _run_fwd(torch, pl, 4, 2, 128, "bf16", 0.09, 5, scale=0.37)
     m = oracle.dense_ancestor_mask(po)
     o_ref, lse_ref = oracle.attention_forward(bf16_ref(q), bf16_ref(k), bf16_ref(v), m, 0.37)
-    assert_close(bf16_ref(o), o_ref, BF16_ATOL, BF16_RTOL, "scaled O")
+    assert_attn_close(bf16_ref(o), o_ref, BF16_ATOL, BF16_RTOL, "scaled O")
     assert_close(lse.numpy(), lse_ref, BF16_ATOL, BF16_RTOL, "scaled LSE")
 
 
@@ -101,7 +101,7 @@ def test_fwd_full_size_sampled(config):
     anc = [oracle.ancestors_of(po, i) for i in rows]
     o_ref, lse_ref = oracle.attention_forward_rows(bf16_ref(q), bf16_ref(k), bf16_ref(v), rows, anc,
                                                    1.0 / math.sqrt(w.d), dtype=np.float32)
-    assert_close(bf16_ref(o[rows]), o_ref, BF16_ATOL, BF16_RTOL, f"config{config} O rows")
+    assert_attn_close(bf16_ref(o[rows]), o_ref, BF16_ATOL, BF16_RTOL, f"config{config} O rows")
     assert_close(lse[:, rows].numpy(), lse_ref, BF16_ATOL, BF16_RTOL, f"config{config} LSE rows")
     n = po.n_tokens
     assert (o[n:].float() == 0).all() and np.isneginf(lse[:, n:].numpy()).all()

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
     for n in sorted(names):
         assert hasattr(L, n), n
     assert set(_lib.SIGNATURES) == names
-    assert L.tree_abi_version() == 5
+    assert L.tree_abi_version() == 6
 
 
 def _compare(tries_lib, tries_or):
@@ -61,6 +61,14 @@ def test_worked_example(L):
     _compare(tl, to)
     assert st["n_pairs"] == 22 and st["unpacked_pairs"] == 26
     assert st["tree_token_ratio"] == pytest.approx(8 / 11)
+    assert (st["tiles_full"], st["tiles_partial"], st["tiles_causal"]) == (0, 1, 1)
+
+
+def _tiles_vs_oracle(st, masks):
+    tcs = [oracle.tile_classes(m) for m in masks]
+    assert st["tiles_full"] == sum(int((t == 2).sum()) for t in tcs)
+    assert st["tiles_partial"] == sum(int((t == 1).sum()) for t in tcs)
+    assert st["tiles_causal"] == sum(t.shape[0] * (t.shape[0] + 1) // 2 for t in tcs)
 
 
 @pytest.mark.parametrize("config", ["1", "2", "3", "4a", "4b"])
@@ -70,10 +78,16 @@ def test_configs_bit_exact(L, config):
     to = oracle.pack(w.ids, w.mask, w.max_tokens_per_mb)
     _compare(tl, to)
     _stats_vs_oracle(st, to, w.mask)
-    if config == "4a":
+    if config == "4a":  # closed forms: prefix 128 blocks, 64 leaves of 2 blocks
         assert st["n_pairs"] == 404_766_720
-    if config == "4b":
+        assert st["tiles_full"] == 128 * 127 // 2 + 64 * (2 * 128 + 1)
+        assert st["tiles_partial"] == 128 + 64 * 2 and st["tiles_causal"] == 256 * 257 // 2
+    if config == "4b":  # 16 disjoint causal sequences of 16 blocks
         assert st["n_pairs"] == 33_570_816
+        assert st["tiles_full"] == 16 * (16 * 15 // 2) and st["tiles_partial"] == 16 * 16
+        assert 1 - (st["tiles_full"] + st["tiles_partial"]) / st["tiles_causal"] == pytest.approx(0.93385, abs=1e-5)
+    if config in ("1", "2"):
+        _tiles_vs_oracle(st, [oracle.dense_ancestor_mask(p) for p in to])
 
 
 @pytest.mark.parametrize("L_,b", [(8192, 1), (8192, 8), (16384, 2), (16384, 4)])
@@ -108,6 +122,7 @@ def test_random_batches_bit_exact(L, seed):
     masks = [oracle.dense_ancestor_mask(p) for p in to]
     acc = oracle.accounting(to, masks, mask.sum(1))
     assert st["n_pairs"] == acc["n_pairs"]
+    _tiles_vs_oracle(st, masks)
 
 
 @pytest.mark.parametrize("config", ["1", "2", "3", "4a", "4b"])

@@ -189,3 +189,27 @@ def test_fp32_mode_close_to_fp64():
     o32, l32 = oracle.attention_forward(q.numpy(), k.numpy(), v.numpy(), m, 0.2, dtype=np.float32)
     assert o32.dtype == np.float32
     np.testing.assert_allclose(o32, o64, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_delta_is_the_softmax_weighted_row_of_dp(seed):
+    """Delta_i = dO_i . O_i equals sum_j P_ij dP_ij with P the softmax of the
+    masked scores (torch.softmax over -inf-filled scores, not the oracle's
+    forward) and dP_ij = dO_i . v_j; it is what makes every dS row sum to
+    zero.  Also pins the [Hq, L] layout and the zero on pads."""
+    p, seqs, q, k, v = _tree_case(seed + 200)
+    scale = 1.0 / np.sqrt(q.shape[-1])
+    m = torch.as_tensor(oracle.dense_ancestor_mask(p))
+    g = torch.Generator().manual_seed(seed)
+    do = torch.randn(q.shape, generator=g, dtype=torch.float64)
+    o, _ = oracle.attention_forward(q.numpy(), k.numpy(), v.numpy(), m.numpy(), scale)
+    delta = oracle.attention_delta(o, do.numpy())
+    assert delta.shape == (q.shape[1], p.L)
+    gq = q.shape[1] // k.shape[1]
+    n = p.n_tokens
+    for h in range(q.shape[1]):
+        s = (scale * q[:n, h] @ k[:n, h // gq].T).masked_fill(~m[:n, :n], -float("inf"))
+        pr = torch.softmax(s, dim=1)
+        dp = do[:n, h] @ v[:n, h // gq].T
+        np.testing.assert_allclose(delta[h, :n], (pr * dp).sum(1).numpy(), rtol=1e-10, atol=1e-12)
+    assert (delta[:, n:] == 0).all()

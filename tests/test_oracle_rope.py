@@ -83,3 +83,42 @@ def test_tree_positions_give_per_sequence_rope_attention(seed):
         vs = torch.from_numpy(v[idx]).repeat_interleave(hq // hkv, 1).transpose(0, 1)
         ref = torch.nn.functional.scaled_dot_product_attention(qs, ks, vs, is_causal=True, scale=scale)
         np.testing.assert_allclose(o[idx], ref.transpose(0, 1).numpy(), atol=1e-10)
+
+
+def test_matches_transformers_qwen3_rotary():
+    """The convention -- half-split pairs (j, j + D/2), the frequency schedule
+    base^(-2j/D), the sign of the rotation -- against the Qwen3 rotary
+    embedding of the transformers library (the model family the pages train;
+    built from a config, no weights), at rope_theta 1e6, head_dim 128 and
+    positions up to 65535.  transformers forms its angles in float32, so the
+    bound per entry is (|x_j| + |x_{j+D/2}|) (p 2^-22 + 1e-6): the angle of
+    position p is off by at most a few p 2^-24 rad there, exact in the oracle."""
+    qwen3 = pytest.importorskip("transformers.models.qwen3.modeling_qwen3")
+    from transformers import Qwen3Config
+
+    D, H, base = 128, 4, 1e6
+    cfg = Qwen3Config(hidden_size=32 * D, num_attention_heads=32, num_key_value_heads=8, head_dim=D,
+                      rope_theta=base, max_position_embeddings=65536)
+    rot = qwen3.Qwen3RotaryEmbedding(config=cfg)
+    rng = np.random.default_rng(21)
+    pos = np.concatenate([np.arange(0, 64), rng.integers(64, 65536, 192), [65535]]).astype(np.int64)
+    L = pos.size
+    q = torch.from_numpy(rng.normal(size=(1, H, L, D)))
+    k = torch.from_numpy(rng.normal(size=(1, 1, L, D)))
+    cos, sin = rot(q, torch.from_numpy(pos)[None])
+    qr, kr = qwen3.apply_rotary_pos_emb(q, k, cos, sin)
+    for x, ref in ((q, qr), (k, kr)):
+        xs = x[0].permute(1, 0, 2).numpy()  # [L, heads, D]
+        ours = oracle.rope(xs, pos, base)
+        got = ref[0].permute(1, 0, 2).numpy()
+        pair = np.abs(xs[..., :D // 2]) + np.abs(xs[..., D // 2:])
+        bound = np.concatenate([pair, pair], -1) * (pos[:, None, None] * 2.0 ** -22 + 1e-6)
+        assert (np.abs(ours - got) <= bound).all(), float((np.abs(ours - got) / bound).max())
+    # the bound is tight enough to tell the schedule apart: base 1e4 (the
+    # Llama-2 default) or interleaved pairs would fail it
+    assert not (np.abs(oracle.rope(xs, pos, 1e4) - got) <= bound).all()
+    a = pos[:, None, None] * base ** (-2.0 * np.arange(D // 2) / D)
+    yi = np.empty_like(xs)  # interleaved pairs (2j, 2j + 1)
+    yi[..., 0::2] = xs[..., 0::2] * np.cos(a) - xs[..., 1::2] * np.sin(a)
+    yi[..., 1::2] = xs[..., 1::2] * np.cos(a) + xs[..., 0::2] * np.sin(a)
+    assert not (np.abs(yi - got) <= bound).all()

@@ -12,4 +12,8 @@ from .generators import (  # noqa: F401
     pad_rows,
     small_workload,
     SMALL_KINDS,
+    edge_layouts,
+    score_ramp_inputs,
+    batch_attention_inputs,
+    device_attention_inputs,
 )

@@ -263,3 +263,72 @@ def small_workload(kind: str, seed: int = 0):
         raise ValueError(kind)
     ids, mask = pad_rows(seqs)
     return ids, mask, M
+
+
+def edge_layouts():
+    """Degenerate batches: name -> (list of sequences, max_tokens_per_mb).
+
+    one-token     a single one-token sequence (L = 128, 127 pads);
+    three-copies  one 300-token sequence three times (one chain, three ids);
+    full-trie     200 + 56 tokens filling L = 256 to the last slot;
+    causal-1000   one 1000-token sequence (8 blocks, the last ragged)."""
+    rng = np.random.default_rng(77)
+    one = [np.array([5], np.int32)]
+    seq = rng.integers(1, 1000, 300).astype(np.int32)
+    copies = [seq, seq.copy(), seq.copy()]
+    a = rng.integers(1, 1000, 100).astype(np.int32)
+    full = [np.concatenate([a, rng.integers(1, 1000, 100)]).astype(np.int32),
+            np.concatenate([a[:44], rng.integers(1000, 2000, 56)]).astype(np.int32)]  # 200 + 56 = 256
+    long = [rng.integers(1, 1000, 1000).astype(np.int32)]
+    return {"one-token": (one, 128), "three-copies": (copies, 384), "full-trie": (full, 256),
+            "causal-1000": (long, 1024)}
+
+
+def score_ramp_inputs(L: int, hq: int, hkv: int, d: int, dtype: str):
+    """Inputs whose scores grow along the key axis: q = 30 u + noise and
+    k_j = c_j u + noise with a fixed unit vector u and c_j rising linearly
+    from 0 to 1.5 sqrt(d), noise N(0, 0.25); v and dO ~ N(0, 1).  With
+    scale 1/sqrt(d) the scores reach about 45 at the end of a row, so an
+    online softmax's running max keeps rising.  Drawn in float64 from
+    torch.Generator(5150), rounded to ``dtype``; CPU tensors."""
+    import torch
+
+    g = torch.Generator().manual_seed(5150)
+    u = torch.randn(d, generator=g, dtype=torch.float64)
+    u /= u.norm()
+    a, c_max = 30.0, 1.5 * math.sqrt(d)
+    c = torch.linspace(0.0, c_max, L, dtype=torch.float64)
+    q = a * u + 0.5 * torch.randn(L, hq, d, generator=g, dtype=torch.float64)
+    k = c[:, None, None] * u + 0.5 * torch.randn(L, hkv, d, generator=g, dtype=torch.float64)
+    v = torch.randn(L, hkv, d, generator=g, dtype=torch.float64)
+    do = torch.randn(L, hq, d, generator=g, dtype=torch.float64)
+    tdt = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
+    return tuple(x.to(tdt) for x in (q, k, v, do))
+
+
+def batch_attention_inputs(lengths, hq: int, hkv: int, d: int, dtype: str, std: float, base_seed: int = 1_000_000):
+    """Q, K, V, dO of a batch laid end to end (the concatenated layout of
+    tree_pack_concat): trie t's rows are ``attention_inputs(L_t, ...)``
+    drawn with seed base_seed + t.  CPU tensors."""
+    import torch
+
+    parts = [attention_inputs(Lt, hq, hkv, d, dtype, std, base_seed + t) for t, Lt in enumerate(lengths)]
+    out = tuple(torch.cat([p[j] for p in parts]) for j in range(4))
+    del parts
+    return out
+
+
+def device_attention_inputs(L: int, hq: int, hkv: int, d: int, std: float, seed: int, device):
+    """bf16 Q, K, V ~ N(0, 1) * std and dO ~ N(0, 1), drawn on ``device``
+    from a seeded device generator (for launches too large to draw on the
+    host quickly).  Copy them to the host to give the oracle the same
+    values."""
+    import torch
+
+    g = torch.Generator(device=device).manual_seed(int(seed))
+    out = []
+    for shape, s in (((L, hq, d), std), ((L, hkv, d), std), ((L, hkv, d), std), ((L, hq, d), 1.0)):
+        t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        out.append((t * s).to(torch.bfloat16) if s != 1.0 else t.to(torch.bfloat16))
+        del t
+    return tuple(out)
