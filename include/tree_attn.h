@@ -281,6 +281,26 @@ int tree_attn_bwd_phase(int32_t phase, const void* q, const void* k, const void*
                         int64_t L, int32_t Hq, int32_t Hkv, int32_t D, float scale,
                         int32_t dtype, void* stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the
+ * backward of tree_attn_bwd (same kernels, same results bit for bit) with its
+ * workspace taken from a static array the library owns on each device,
+ * TREE_BWD_STATIC_SCRATCH_BYTES long, instead of d_ws.  The array is set up
+ * on the first call on a device (the device current on the calling thread,
+ * which the stream must belong to) and held until the process ends.  No
+ * device memory is allocated or freed.  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (concurrent streams, threads or
+ * graph replays) race and must be serialised by the caller.  Limit:
+ * tree_attn_bwd_workspace_bytes(L, Hq, D, dtype) <= TREE_BWD_STATIC_SCRATCH_BYTES,
+ * i.e. L * Hq <= 8388608 (L = 262144 at 32 query heads); a larger call fails
+ * with TREE_E_ARG before any device work.  Other arguments and errors as
+ * tree_attn_bwd (TREE_E_HIP if the array's address cannot be looked up). */
+#define TREE_BWD_STATIC_SCRATCH_BYTES (64u << 20)
+int tree_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv, const int32_t* d_se,
+                          const void* d_meta_ws, int64_t L, int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                          int32_t dtype, void* stream);
+
 /* ------------------------------------------------------------------------
  * Log-probabilities and entropies of packed logits (device).  Guide,
  * section "Log Probability 计算：树结构的特殊处理": labels cannot come from

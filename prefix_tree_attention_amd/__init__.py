@@ -9,7 +9,7 @@ arguments into it.
 """
 
 from ._lib import (TreeAttnError, lib, library_path, DTYPE_BF16, DTYPE_FP32, BLOCK,  # noqa: F401
-                   BWD_ALL, BWD_DELTA, BWD_DKDV, BWD_DQ, BWD_DQ_DELTA)
+                   BWD_ALL, BWD_DELTA, BWD_DKDV, BWD_DQ, BWD_DQ_DELTA, BWD_STATIC_SCRATCH_BYTES)
 from .api import (  # noqa: F401
     PackedTrie,
     TreeMeta,
@@ -23,6 +23,7 @@ from .api import (  # noqa: F401
     attn_fwd,
     attn_bwd,
     attn_bwd_phase,
+    attn_bwd_noalloc,
     tree_attention,
     logits_stats,
     gather_logprobs,

@@ -80,12 +80,15 @@ SIGNATURES = {
                                      c_sz, c_i64, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp]),
     "tree_attn_bwd_phase": (ctypes.c_int, [c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                            c_vp, c_sz, c_i64, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp]),
+    "tree_attn_bwd_noalloc": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                             c_i64, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp]),
     "tree_logits_stats": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp]),
     "tree_gather_logprobs": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_f32,
                                             c_vp, c_vp, c_vp]),
     "tree_rope": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i32, c_i32, ctypes.c_double, c_i32, c_i32, c_vp]),
 }
 BWD_ALL, BWD_DELTA, BWD_DKDV, BWD_DQ, BWD_DQ_DELTA = 0, 1, 2, 3, 4
+BWD_STATIC_SCRATCH_BYTES = 64 << 20  # TREE_BWD_STATIC_SCRATCH_BYTES
 
 _lock = threading.Lock()
 _lib = None

@@ -294,6 +294,27 @@ def attn_bwd(q, k, v, o, lse, do, meta: TreeMeta, scale: float | None = None, wo
     return dq, dk, dv
 
 
+def attn_bwd_noalloc(q, k, v, o, lse, do, meta: TreeMeta, scale: float | None = None, dq=None, dk=None, dv=None):
+    """``tree_attn_bwd_noalloc``: the backward with the library's static
+    per-device scratch as its workspace (no device allocation inside the
+    library; outputs are allocated here unless given).  Returns (dq, dk, dv)."""
+    torch = _torch()
+    _check_qkv(q, k, v, meta)
+    for name, t in (("o", o), ("do", do)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise TreeAttnError(-5, f"{name} must match q")
+    L, hq, d = q.shape
+    hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else _check_out("dq", dq, q.shape, q.dtype, q.device)
+    dk = torch.empty_like(k) if dk is None else _check_out("dk", dk, k.shape, k.dtype, k.device)
+    dv = torch.empty_like(v) if dv is None else _check_out("dv", dv, v.shape, v.dtype, v.device)
+    check(lib().tree_attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse.contiguous()), _ptr(do), _ptr(dq),
+                                      _ptr(dk), _ptr(dv), _ptr(meta.se), _ptr(meta.ws), L, hq, hkv, d, scale,
+                                      _dtype_code(q), _stream(q.device)))
+    return dq, dk, dv
+
+
 def attn_bwd_phase(phase: int, q, k, v, o, lse, do, dq, dk, dv, meta: TreeMeta, workspace, scale=None):
     """``tree_attn_bwd_phase`` into caller-provided outputs and workspace
     (BWD_DELTA, BWD_DKDV, BWD_DQ, BWD_DQ_DELTA or BWD_ALL); used to time the backward's

@@ -39,6 +39,8 @@ int check_L(int64_t L, const char* fn) {
     return TREE_OK;
 }
 
+}  // namespace
+
 int check_attn(const char* fn, int64_t L, int32_t Hq, int32_t Hkv, int32_t D, float scale, int32_t dtype) {
     if (int rc = check_L(L, fn)) return rc;
     if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Hq > 4096)
@@ -57,6 +59,8 @@ int check_attn(const char* fn, int64_t L, int32_t Hq, int32_t Hkv, int32_t D, fl
         return set_error(TREE_E_ARG, "%s: scale must be finite and positive", fn);
     return TREE_OK;
 }
+
+namespace {
 
 int hip_status(hipError_t e, const char* fn) {
     if (e != hipSuccess) return set_error(TREE_E_HIP, "%s: HIP error %d (%s)", fn, int(e), hipGetErrorString(e));

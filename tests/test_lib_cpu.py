@@ -219,6 +219,15 @@ def test_device_entry_points_validate_before_launch(L):
     assert need >= 1024 * 8 * 4
     assert L.tree_attn_bwd(*([p] * 12), need - 1, 1024, 8, 2, 128, 0.1, 0, None) == -6
     assert b"workspace" in L.tree_last_error()
+    # the static-scratch backward: its size limit and argument checks come
+    # before any device call
+    assert L.tree_attn_bwd_noalloc(*([p] * 11), 1 << 20, 16, 2, 128, 0.1, 0, None) == -5
+    assert b"static scratch" in L.tree_last_error()
+    limit = pta.BWD_STATIC_SCRATCH_BYTES // 8  # L * Hq rows that fit
+    assert L.tree_attn_bwd_workspace_bytes(limit // 32, 32, 128, 0) == pta.BWD_STATIC_SCRATCH_BYTES
+    assert L.tree_attn_bwd_noalloc(*([p] * 11), limit // 32 + 128, 32, 8, 128, 0.1, 0, None) == -5
+    assert L.tree_attn_bwd_noalloc(*([p] * 11), 1024, 6, 4, 128, 0.1, 0, None) == -5   # Hq % Hkv
+    assert L.tree_attn_bwd_noalloc(*([p] * 10), None, 1024, 8, 2, 128, 0.1, 0, None) == -5  # NULL
 
 
 def _oracle_concat(to):
