@@ -55,3 +55,4 @@ from .attention import (  # noqa: F401
 from .logprobs import gather_tree_logprobs_entropy, prediction_logprob_entropy  # noqa: F401
 from .partition import dfs_order, tree_cost, partition, partition_batch, dummy_tries  # noqa: F401
 from .rope import rope  # noqa: F401
+from .dfs import dfs_attention  # noqa: F401
