@@ -25,6 +25,10 @@ convention) and is compared with MI355X's dense bf16 MFMA peak.
                     split over K workers, its own JSON line)
     python bench.py --rope [--config 4a]   (rotary embedding of Q and K by
                     tree position ids, its own JSON line)
+    python bench.py --rope-fused [--config 4a]   (fwd+bwd with the rotation
+                    fused into the kernels vs separate passes)
+    python bench.py --dfs [--config 4a] [--chunk 2048]   (depth-first
+                    execution per trie vs the packed path)
 """
 
 from __future__ import annotations
@@ -71,6 +75,11 @@ def parse(argv=None):
                     help="time the DFS-order load-balanced split of the batch over this many workers instead")
     ap.add_argument("--rope", action="store_true",
                     help="time the rotary embedding of Q and K by tree position ids instead")
+    ap.add_argument("--rope-fused", action="store_true",
+                    help="time fwd+bwd with the rotary embedding fused into the kernels against separate passes")
+    ap.add_argument("--dfs", action="store_true",
+                    help="time the depth-first (DTA) execution of every trie against the packed path")
+    ap.add_argument("--chunk", type=int, default=2048, help="query chunk of the depth-first execution")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB elementwise copy kernel 3x (HBM counter calibration)")
     return ap.parse_args(argv)
@@ -167,6 +176,10 @@ def main(argv=None):
         return bench_partition(a)
     if a.rope:
         return bench_rope(a)
+    if a.rope_fused:
+        return bench_rope_fused(a)
+    if a.dfs:
+        return bench_dfs(a)
     import numpy as np
     import torch
     import workloads
@@ -561,6 +574,152 @@ def bench_rope(a):
                                   "sample": f"the first {n} tokens of Q and K, float64 numpy ({dt:.2f} s)"}
     else:
         result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def bench_rope_fused(a):
+    """Attention with the rotary embedding by tree position ids, forward and
+    backward, two ways on the same resident inputs: the rotation fused into
+    the kernels (tree_attn_fwd_rope / tree_attn_bwd_rope: Q rotated at the
+    forward's register load, K by one table pass, dQ / dK rotated back in the
+    backward epilogues), and as separate passes (tree_rope of Q and K, the
+    plain forward and backward, tree_rope inverse of dQ and dK).  value =
+    packed tokens/s of the fused step."""
+    import torch
+    import workloads
+    import prefix_tree_attention_amd as pta
+
+    w = workloads.sweep_workload(*(int(x) for x in a.sweep.split(","))) if a.sweep else workloads.make_workload(a.config)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    se, lengths, stats = pta.pack_concat(w.ids, w.mask, w.max_tokens_per_mb)
+    L = len(se)
+    meta = pta.tree_meta(se)
+    q, k, v, do = workloads.batch_attention_inputs(lengths, w.hq, w.hkv, w.d, "bf16", w.qkv_std)
+    q, k, v, do = (t.to(dev) for t in (q, k, v, do))
+    tab = pta.rope_table(L, w.d, 1e6)
+    o, lse = torch.empty_like(q), torch.empty((w.hq, L), dtype=torch.float32, device=dev)
+    qr, kr = torch.empty_like(q), torch.empty_like(k)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(pta.bwd_workspace_bytes(L, w.hq, w.d), dtype=torch.uint8, device=dev)
+
+    def fused():
+        pta.attn_fwd_rope(q, k, v, meta, tab, o=o, lse=lse)
+        pta.attn_bwd_rope(qr, kr, v, o, lse, do, meta, tab, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    def separate():
+        pta.rope(q, meta.pos, 1e6, out=qr)
+        pta.rope(k, meta.pos, 1e6, out=kr)
+        pta.attn_fwd(qr, kr, v, meta, o=o, lse=lse)
+        pta.attn_bwd(qr, kr, v, o, lse, do, meta, workspace=ws, dq=dq, dk=dk, dv=dv)
+        pta.rope(dq, meta.pos, 1e6, inverse=True, out=dq)
+        pta.rope(dk, meta.pos, 1e6, inverse=True, out=dk)
+
+    def timed(fn):
+        for _ in range(a.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(a.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / a.steps
+
+    # the fused forward writes q_rot / k_rot into qr / kr for its backward
+    _o, _l, qr0, kr0 = pta.attn_fwd_rope(q, k, v, meta, tab, o=o, lse=lse)
+    qr.copy_(qr0)
+    kr.copy_(kr0)
+    t_sep = timed(separate)
+    t_fused = timed(fused)
+    useful = 14.0 * w.d * w.hq * stats["n_pairs"]
+    result = {
+        "metric": "tree-attn fwd+bwd with rotary embedding by tree position ids, fused vs separate passes",
+        "value": round(stats["tree_tokens"] / (t_fused * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(t_fused, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "fused_ms_per_step": round(t_fused, 4), "separate_ms_per_step": round(t_sep, 4),
+        "useful_tflops": round(useful / (t_fused * 1e-3) / 1e12, 2),
+        "pct_of_bf16_peak": round(100.0 * useful / (t_fused * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": w.name, "launch_L": L, "hq": w.hq, "hkv": w.hkv, "head_dim": w.d, "base": 1e6},
+        "cpu_baseline": None,
+    }
+    log(f"fused {t_fused:.3f} ms, separate passes {t_sep:.3f} ms per step")
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def bench_dfs(a):
+    """Depth-first (DTA) execution of every trie of the batch (tree_attn_dfs,
+    forward and backward, chunk a.chunk) against the packed-trie path on the
+    same resident inputs, per trie.  value = packed tokens/s of the
+    depth-first step; also its device memory (the frame workspace, bounded
+    by the longest path) against the packed path's per-trie tensors."""
+    import torch
+    import workloads
+    import prefix_tree_attention_amd as pta
+
+    w = workloads.sweep_workload(*(int(x) for x in a.sweep.split(","))) if a.sweep else workloads.make_workload(a.config)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    tries, stats = pta.pack(w.ids, w.mask, w.max_tokens_per_mb)
+    items = []
+    for t, tr in enumerate(tries):
+        q, k, v, do = (x.to(dev) for x in workloads.attention_inputs(tr.L, w.hq, w.hkv, w.d, "bf16", w.qkv_std,
+                                                                      1_000_000 + t))
+        meta = pta.tree_meta(tr.subtree_end)
+        plan = pta.dfs_plan(tr, a.chunk)
+        outs = dict(o=torch.empty_like(q), lse=torch.empty((w.hq, tr.L), dtype=torch.float32, device=dev),
+                    dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v))
+        ws = torch.empty(pta.dfs_workspace_bytes(plan, w.hq, w.hkv, w.d), dtype=torch.uint8, device=dev)
+        items.append((tr, q, k, v, do, meta, plan, outs, ws))
+
+    def dfs():
+        for tr, q, k, v, do, meta, plan, outs, ws in items:
+            pta.attn_dfs(tr, q, k, v, do, meta, chunk=a.chunk, workspace=ws, **outs)
+
+    def packed():
+        for tr, q, k, v, do, meta, plan, outs, ws in items:
+            o, lse = pta.attn_fwd(q, k, v, meta, o=outs["o"], lse=outs["lse"])
+            pta.attn_bwd(q, k, v, o, lse, do, meta, dq=outs["dq"], dk=outs["dk"], dv=outs["dv"])
+
+    def timed(fn):
+        for _ in range(a.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(a.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / a.steps, (time.perf_counter() - t0) / a.steps * 1e3
+
+    t_dfs, wall_dfs = timed(dfs)
+    t_packed, _ = timed(packed)
+    useful = 14.0 * w.d * w.hq * stats["n_pairs"]
+    per_trie_tensors = max(tr.L for tr in tries) * (4 * w.hq + 4 * w.hkv) * w.d * 2
+    result = {
+        "metric": "depth-first (DTA) tree-attn fwd+bwd tokens/s and useful TFLOP/s, 1 GPU",
+        "value": round(stats["tree_tokens"] / (wall_dfs * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(wall_dfs, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "gpu_ms_per_step": round(t_dfs, 4), "packed_path_ms_per_step": round(t_packed, 4),
+        "useful_tflops": round(useful / (wall_dfs * 1e-3) / 1e12, 2),
+        "pct_of_bf16_peak": round(100.0 * useful / (wall_dfs * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "frame_workspace_bytes": max(int(x[8].numel()) for x in items),
+        "packed_trie_tensor_bytes": per_trie_tensors,
+        "plans": [x[6] for x in items][:8],
+        "config": {"workload": w.name, "tries": len(tries), "L": [tr.L for tr in tries], "chunk": a.chunk,
+                   "hq": w.hq, "hkv": w.hkv, "head_dim": w.d},
+        "cpu_baseline": None,
+    }
+    log(f"dfs {t_dfs:.3f} ms (wall {wall_dfs:.3f}), packed {t_packed:.3f} ms per step")
     print(json.dumps(result), flush=True)
     return 0
 

@@ -302,6 +302,59 @@ int tree_attn_bwd_noalloc(const void* q, const void* k, const void* v, const voi
                           int32_t dtype, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Depth-first execution (AREAL-DTA notes, §3.1 前缀树的深度优先搜索遍历 and
+ * §3.2 系统优化).  The same attention and gradients as tree_attn_fwd +
+ * tree_attn_bwd on one trie, computed the way the notes' DFS traversal does:
+ * a stack holds the keys/values of the current root-to-node path; entering
+ * an internal node pushes its tokens and runs their forward against the
+ * stack; leaves run forward and backward at once and are never pushed ("cut
+ * tail": no later token attends to them); leaving a node runs its backward,
+ * after every sequence below it has added its gradient to the node's keys,
+ * and pops it.  Nodes longer than `chunk` tokens run in chunks of at most
+ * `chunk` queries.  Device memory (the frame) is bounded by the longest
+ * path, not the tree.  Consecutive sibling leaves run together, up to the
+ * frame's leaf capacity (the longest leaf or `chunk`, whichever is more):
+ * the same computation as visiting them one by one.  bf16 only.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    int64_t rows;              /* frame length the kernels run on (multiple of 256) */
+    int64_t stack_rows;        /* most frame rows the stack occupies (each node from a
+                                  128-aligned row) */
+    int64_t leaf_rows;         /* frame rows for the leaves being run */
+    int64_t peak_stack_tokens; /* most real tokens on the stack at once: the longest
+                                  root-to-internal-node path */
+    int64_t max_path_tokens;   /* longest root-to-leaf path */
+    int64_t chunks;            /* query chunks (one forward and one backward each) */
+    int64_t leaf_groups;       /* launches of consecutive sibling leaves */
+    int64_t max_depth;         /* most internal nodes on the stack */
+} tree_dfs_plan_t;
+
+/* Plan of the depth-first execution of one trie, from its HOST node table
+ * (tree_trie_view's node_start / node_end / node_parent, n_nodes, and its
+ * n_tokens).  chunk must be a positive multiple of 128 (2048 in the notes).
+ * Errors: TREE_E_ARG (NULL pointers, a node table that is not the pre-order
+ * layout, a stack deeper than 240 internal nodes, a frame longer than
+ * 2^20 rows), TREE_E_NOMEM. */
+int tree_dfs_plan(const int32_t* node_start, const int32_t* node_end, const int32_t* node_parent, int64_t n_nodes,
+                  int64_t n_tokens, int32_t chunk, tree_dfs_plan_t* plan);
+
+/* Bytes of device workspace tree_attn_dfs needs for a plan (0 if invalid). */
+size_t tree_attn_dfs_workspace_bytes(const tree_dfs_plan_t* plan, int32_t Hq, int32_t Hkv, int32_t D);
+
+/* Forward and backward of one trie by depth-first execution.  The node table
+ * is on the HOST (as for tree_dfs_plan); q, k, v, dout, o, lse, dq, dk, dv
+ * are DEVICE tensors in the packed layout of tree_attn_fwd / tree_attn_bwd
+ * (L rows, bf16, LSE [Hq, L] float32), d_se the trie's subtree ends on the
+ * device.  All outputs are fully overwritten (pads: O = dQ = dK = dV = 0,
+ * LSE = -inf).  d_ws holds tree_attn_dfs_workspace_bytes(plan) bytes.  The
+ * host walks the trie and enqueues many small launches on `stream`; nothing
+ * synchronises.  Errors: those of tree_dfs_plan and tree_attn_bwd. */
+int tree_attn_dfs(const int32_t* node_start, const int32_t* node_end, const int32_t* node_parent, int64_t n_nodes,
+                  int64_t n_tokens, const void* q, const void* k, const void* v, const void* dout, void* o,
+                  float* lse, void* dq, void* dk, void* dv, const int32_t* d_se, void* d_ws, size_t ws_bytes,
+                  int64_t L, int32_t Hq, int32_t Hkv, int32_t D, float scale, int32_t chunk, void* stream);
+
+/* ------------------------------------------------------------------------
  * Log-probabilities and entropies of packed logits (device).  Guide,
  * section "Log Probability 计算：树结构的特殊处理": labels cannot come from
  * rolling the packed ids; each sequence's token k + 1 is predicted by the
@@ -357,6 +410,40 @@ int tree_gather_logprobs(const void* logits, int64_t L, int64_t V, int32_t dtype
  * or not finite, dtype, misalignment), TREE_E_HIP. */
 int tree_rope(const void* x, void* y, const int32_t* d_pos, int64_t L, int32_t H, int32_t D, double base,
               int32_t inverse, int32_t dtype, void* stream);
+
+/* The same rotary embedding fused into the attention kernels (bf16): Q is
+ * rotated as the forward kernel loads it into registers, K by a table-driven
+ * pass into k_rot, and the backward rotates dQ and dK back in its epilogues,
+ * so its outputs are gradients with respect to the unrotated q and k.
+ *
+ * tree_rope_table fills d_tab with (cos, sin) float pairs of p f_j for every
+ * position p < P and pair j < D/2 -- float64 angles rounded to float32, the
+ * values tree_rope uses -- [P, D/2, 2] float32, tree_rope_table_bytes(P, D)
+ * bytes (0 for a bad P or D; D a multiple of 16).  The attention calls need a
+ * table with P >= L (every position id is below L).  Errors: TREE_E_ARG,
+ * TREE_E_WORKSPACE (table too small), TREE_E_HIP. */
+size_t tree_rope_table_bytes(int64_t P, int32_t D);
+int tree_rope_table(double base, int64_t P, int32_t D, float* d_tab, size_t tab_bytes, void* stream);
+
+/* tree_attn_fwd on rotated q and k: O = attention(rot(q), rot(k), v), with
+ * rot by the position ids d_pos (tree_meta's) and the table d_tab.  Also
+ * writes q_rot = rot(q) [L, Hq, D] and k_rot = rot(k) [L, Hkv, D] (bf16), the
+ * operands tree_attn_bwd_rope needs.  Other arguments and errors as
+ * tree_attn_fwd. */
+int tree_attn_fwd_rope(const void* q, const void* k, const void* v, void* o, float* lse, void* q_rot, void* k_rot,
+                       const int32_t* d_pos, const float* d_tab, size_t tab_bytes, const int32_t* d_se,
+                       const void* d_meta_ws, int64_t L, int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                       void* stream);
+
+/* Backward of tree_attn_fwd_rope from its q_rot, k_rot, o, lse: dq and dk
+ * are the gradients with respect to the unrotated q and k (the rotation is
+ * orthogonal, so each is the inverse rotation of the gradient with respect
+ * to its rotated operand, applied before the bf16 rounding), dv as
+ * tree_attn_bwd.  Other arguments and errors as tree_attn_bwd. */
+int tree_attn_bwd_rope(const void* q_rot, const void* k_rot, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, const int32_t* d_pos, const float* d_tab,
+                       size_t tab_bytes, const int32_t* d_se, const void* d_meta_ws, void* d_ws, size_t ws_bytes,
+                       int64_t L, int32_t Hq, int32_t Hkv, int32_t D, float scale, void* stream);
 
 #ifdef __cplusplus
 }

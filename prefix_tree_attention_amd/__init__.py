@@ -24,10 +24,17 @@ from .api import (  # noqa: F401
     attn_bwd,
     attn_bwd_phase,
     attn_bwd_noalloc,
+    dfs_plan,
+    dfs_workspace_bytes,
+    attn_dfs,
     tree_attention,
     logits_stats,
     gather_logprobs,
     tree_logprobs,
     rope,
     tree_rope,
+    rope_table,
+    attn_fwd_rope,
+    attn_bwd_rope,
+    tree_attention_rope,
 )

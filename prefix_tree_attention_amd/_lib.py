@@ -56,6 +56,13 @@ class PackStats(ctypes.Structure):
     ]
 
 
+class DfsPlan(ctypes.Structure):
+    _fields_ = [
+        ("rows", c_i64), ("stack_rows", c_i64), ("leaf_rows", c_i64), ("peak_stack_tokens", c_i64),
+        ("max_path_tokens", c_i64), ("chunks", c_i64), ("leaf_groups", c_i64), ("max_depth", c_i64),
+    ]
+
+
 # name -> (restype, argtypes), in header order
 SIGNATURES = {
     "tree_abi_version": (ctypes.c_int, []),
@@ -82,9 +89,19 @@ SIGNATURES = {
                                            c_vp, c_sz, c_i64, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp]),
     "tree_attn_bwd_noalloc": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                              c_i64, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp]),
+    "tree_dfs_plan": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i32, ctypes.POINTER(DfsPlan)]),
+    "tree_attn_dfs_workspace_bytes": (c_sz, [ctypes.POINTER(DfsPlan), c_i32, c_i32, c_i32]),
+    "tree_attn_dfs": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                     c_vp, c_vp, c_vp, c_sz, c_i64, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp]),
     "tree_logits_stats": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp]),
     "tree_gather_logprobs": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_f32,
                                             c_vp, c_vp, c_vp]),
+    "tree_rope_table_bytes": (c_sz, [c_i64, c_i32]),
+    "tree_rope_table": (ctypes.c_int, [ctypes.c_double, c_i64, c_i32, c_vp, c_sz, c_vp]),
+    "tree_attn_fwd_rope": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp, c_vp,
+                                          c_i64, c_i32, c_i32, c_i32, c_f32, c_vp]),
+    "tree_attn_bwd_rope": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz,
+                                          c_vp, c_vp, c_vp, c_sz, c_i64, c_i32, c_i32, c_i32, c_f32, c_vp]),
     "tree_rope": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i32, c_i32, ctypes.c_double, c_i32, c_i32, c_vp]),
 }
 BWD_ALL, BWD_DELTA, BWD_DKDV, BWD_DQ, BWD_DQ_DELTA = 0, 1, 2, 3, 4

@@ -12,7 +12,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from ._lib import (BLOCK, DTYPE_BF16, DTYPE_FP32, PackStats, TrieView, TreeAttnError, check, lib)
+from ._lib import (BLOCK, DTYPE_BF16, DTYPE_FP32, DfsPlan, PackStats, TrieView, TreeAttnError, check, lib)
 
 
 # ---------------------------------------------------------------------------
@@ -360,6 +360,60 @@ def tree_attention(q, k, v, meta: TreeMeta, scale: float | None = None):
 
 
 # ---------------------------------------------------------------------------
+# depth-first (DTA) execution
+# ---------------------------------------------------------------------------
+def _node_table(trie: PackedTrie):
+    ns = np.ascontiguousarray(trie.node_start, dtype=np.int32)
+    ne = np.ascontiguousarray(trie.node_end, dtype=np.int32)
+    npar = np.ascontiguousarray(trie.node_parent, dtype=np.int32)
+    return ns, ne, npar
+
+
+def dfs_plan(trie: PackedTrie, chunk: int = 2048) -> dict:
+    """``tree_dfs_plan``: sizes of the depth-first execution of one trie."""
+    ns, ne, npar = _node_table(trie)
+    plan = DfsPlan()
+    check(lib().tree_dfs_plan(ns.ctypes.data, ne.ctypes.data, npar.ctypes.data, ns.size, int(trie.n_tokens),
+                              int(chunk), ctypes.byref(plan)))
+    return {k: getattr(plan, k) for k, _ in DfsPlan._fields_}
+
+
+def dfs_workspace_bytes(plan: dict, hq: int, hkv: int, d: int) -> int:
+    """``tree_attn_dfs_workspace_bytes`` of a plan from ``dfs_plan``."""
+    return int(lib().tree_attn_dfs_workspace_bytes(ctypes.byref(DfsPlan(**plan)), int(hq), int(hkv), int(d)))
+
+
+def attn_dfs(trie: PackedTrie, q, k, v, do, meta: TreeMeta, scale: float | None = None, chunk: int = 2048,
+             o=None, lse=None, dq=None, dk=None, dv=None, workspace=None):
+    """``tree_attn_dfs``: forward and backward of one trie by depth-first
+    execution (bf16).  Returns (o, lse, dq, dk, dv) in the packed layout."""
+    torch = _torch()
+    _check_qkv(q, k, v, meta)
+    if do.shape != q.shape or do.dtype != q.dtype or not do.is_contiguous():
+        raise TreeAttnError(-5, "do must match q")
+    L, hq, d = q.shape
+    hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    ns, ne, npar = _node_table(trie)
+    plan = DfsPlan()
+    check(lib().tree_dfs_plan(ns.ctypes.data, ne.ctypes.data, npar.ctypes.data, ns.size, int(trie.n_tokens),
+                              int(chunk), ctypes.byref(plan)))
+    nbytes = int(lib().tree_attn_dfs_workspace_bytes(ctypes.byref(plan), hq, hkv, d))
+    ws = workspace if workspace is not None else torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if o is None else _check_out("o", o, q.shape, q.dtype, q.device)
+    lse = (torch.empty((hq, L), dtype=torch.float32, device=q.device) if lse is None
+           else _check_out("lse", lse, (hq, L), torch.float32, q.device))
+    dq = torch.empty_like(q) if dq is None else _check_out("dq", dq, q.shape, q.dtype, q.device)
+    dk = torch.empty_like(k) if dk is None else _check_out("dk", dk, k.shape, k.dtype, k.device)
+    dv = torch.empty_like(v) if dv is None else _check_out("dv", dv, v.shape, v.dtype, v.device)
+    check(lib().tree_attn_dfs(ns.ctypes.data, ne.ctypes.data, npar.ctypes.data, ns.size, int(trie.n_tokens),
+                              _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(o), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                              _ptr(meta.se), _ptr(ws), ws.numel(), L, hq, hkv, d, scale, int(chunk),
+                              _stream(q.device)))
+    return o, lse, dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
 # log-probabilities of packed logits
 # ---------------------------------------------------------------------------
 def _check_logits(logits):
@@ -446,6 +500,92 @@ def _rope_fn():
             return rope(gy.contiguous(), pos, ctx.base, inverse=True), None, None
 
     return _Rope
+
+
+def rope_table(L: int, d: int, base: float = 1e6, device=None):
+    """``tree_rope_table``: (cos, sin) of every position < L, float32
+    [L, d/2, 2] on the device, for the fused-rotation attention calls."""
+    torch = _torch()
+    device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    nbytes = int(lib().tree_rope_table_bytes(int(L), int(d)))
+    if nbytes == 0:
+        raise TreeAttnError(-5, f"bad table shape L={L} D={d}")
+    tab = torch.empty(nbytes // 4, dtype=torch.float32, device=device)
+    check(lib().tree_rope_table(float(base), int(L), int(d), _ptr(tab), nbytes, _stream(device)))
+    return tab
+
+
+def attn_fwd_rope(q, k, v, meta: TreeMeta, tab, scale: float | None = None, o=None, lse=None):
+    """``tree_attn_fwd_rope``: attention of the rotated q, k (rotation fused
+    into the kernels).  Returns (o, lse, q_rot, k_rot)."""
+    torch = _torch()
+    _check_qkv(q, k, v, meta)
+    if q.dtype != torch.bfloat16:
+        raise TreeAttnError(-5, "the fused rotation runs in bf16")
+    L, hq, d = q.shape
+    hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if o is None else _check_out("o", o, q.shape, q.dtype, q.device)
+    lse = (torch.empty((hq, L), dtype=torch.float32, device=q.device) if lse is None
+           else _check_out("lse", lse, (hq, L), torch.float32, q.device))
+    q_rot, k_rot = torch.empty_like(q), torch.empty_like(k)
+    check(lib().tree_attn_fwd_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(q_rot), _ptr(k_rot),
+                                   _ptr(meta.pos), _ptr(tab), tab.numel() * 4, _ptr(meta.se), _ptr(meta.ws), L, hq,
+                                   hkv, d, scale, _stream(q.device)))
+    return o, lse, q_rot, k_rot
+
+
+def attn_bwd_rope(q_rot, k_rot, v, o, lse, do, meta: TreeMeta, tab, scale: float | None = None, dq=None, dk=None,
+                  dv=None, workspace=None):
+    """``tree_attn_bwd_rope``: gradients w.r.t. the unrotated q and k (and
+    v), from the forward's q_rot, k_rot, o and lse."""
+    torch = _torch()
+    _check_qkv(q_rot, k_rot, v, meta)
+    L, hq, d = q_rot.shape
+    hkv = k_rot.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    nbytes = bwd_workspace_bytes(L, hq, d)
+    ws = workspace if workspace is not None else torch.empty(nbytes, dtype=torch.uint8, device=q_rot.device)
+    dq = torch.empty_like(q_rot) if dq is None else _check_out("dq", dq, q_rot.shape, q_rot.dtype, q_rot.device)
+    dk = torch.empty_like(k_rot) if dk is None else _check_out("dk", dk, k_rot.shape, k_rot.dtype, k_rot.device)
+    dv = torch.empty_like(v) if dv is None else _check_out("dv", dv, v.shape, v.dtype, v.device)
+    check(lib().tree_attn_bwd_rope(_ptr(q_rot), _ptr(k_rot), _ptr(v), _ptr(o), _ptr(lse.contiguous()),
+                                   _ptr(do.contiguous()), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(meta.pos), _ptr(tab),
+                                   tab.numel() * 4, _ptr(meta.se), _ptr(meta.ws), _ptr(ws), ws.numel(), L, hq, hkv,
+                                   d, scale, _stream(q_rot.device)))
+    return dq, dk, dv
+
+
+def _attn_rope_fn():
+    torch = _torch()
+
+    class TreeAttentionRopeFn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, meta, tab, scale):
+            o, lse, q_rot, k_rot = attn_fwd_rope(q, k, v, meta, tab, scale)
+            ctx.save_for_backward(q_rot, k_rot, v, o, lse, tab)
+            ctx.meta, ctx.scale = meta, scale
+            return o
+
+        @staticmethod
+        def backward(ctx, do):
+            q_rot, k_rot, v, o, lse, tab = ctx.saved_tensors
+            dq, dk, dv = attn_bwd_rope(q_rot, k_rot, v, o, lse, do.contiguous(), ctx.meta, tab, ctx.scale)
+            return dq, dk, dv, None, None, None
+
+    return TreeAttentionRopeFn
+
+
+_ROPE_FN = None
+
+
+def tree_attention_rope(q, k, v, meta: TreeMeta, tab, scale: float | None = None):
+    """Differentiable tree attention with the rotary embedding by tree
+    position ids fused into the kernels: attention(rot(q), rot(k), v)."""
+    global _ROPE_FN
+    if _ROPE_FN is None:
+        _ROPE_FN = _attn_rope_fn()
+    return _ROPE_FN.apply(q, k, v, meta, tab, scale)
 
 
 def tree_rope(x, pos, base: float = 1e6):

@@ -29,8 +29,8 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["meta.hip", "fwd_bf16.hip", "bwd_bf16.hip", "attn_f32.hip", "logprob.hip", "rope.hip", "noalloc.hip"]
-CXX_SOURCES = ["capi.cpp", "pack.cpp"]
+HIP_SOURCES = ["meta.hip", "fwd_bf16.hip", "bwd_bf16.hip", "attn_f32.hip", "logprob.hip", "rope.hip", "noalloc.hip", "dfs.hip"]
+CXX_SOURCES = ["capi.cpp", "status.cpp", "pack.cpp", "dfs.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC]
 HIP_FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",

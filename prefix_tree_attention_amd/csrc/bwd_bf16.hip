@@ -110,13 +110,14 @@ __device__ __forceinline__ void mfma32_agpr(f32x16& acc, const bf16x8& a, const 
 
 // one workgroup per (pair of 128-key blocks, key/value head); wave w owns
 // 64 keys
-template <int D>
+template <int D, bool kAcc, bool kRope>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ NLS, const float* __restrict__ Delta,
-    bf16* __restrict__ dK, bf16* __restrict__ dV, const int32_t* __restrict__ se,
-    const int32_t* __restrict__ p_order, const int32_t* __restrict__ blk_min,
-    const int32_t* __restrict__ blk_max, int L, int Hq, int Hkv, float scale_log2, float scale) {
+    bf16* __restrict__ dK, bf16* __restrict__ dV, float* __restrict__ dKacc, float* __restrict__ dVacc,
+    const int32_t* __restrict__ se, const int32_t* __restrict__ p_order, const int32_t* __restrict__ blk_min,
+    const int32_t* __restrict__ blk_max, int L, int Hq, int Hkv, int qb_lo, int qb_hi, float scale_log2,
+    float scale, const int32_t* __restrict__ pos, const float* __restrict__ rope_tab) {
     using T = Tile<D>;
     constexpr int NX = D / 16;  // k-steps of S = Q K^T and dP = dO V^T
     constexpr int NT = D / 32;  // 32-row d-blocks of dK^T and dV^T
@@ -214,8 +215,9 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
     // starting at its own block).
     const int hi0 = blk_max[kb0], hi1 = has1 ? blk_max[kb1] : -1;
     const int hi = max(hi0, hi1);
-    const int qhi = hi >= 0 ? min(nb - 1, hi / kBlock) : -1;
-    const int qlo = hi0 >= 0 ? kb0 : kb1;
+    // (clipped to the launch's query blocks [qb_lo, qb_hi))
+    const int qhi = hi >= 0 ? min(min(nb, qb_hi) - 1, hi / kBlock) : -1;
+    const int qlo = max(hi0 >= 0 ? kb0 : kb1, qb_lo);
     const int nsteps = (qhi >= qlo ? qhi - qlo + 1 : 0) * 2 * G;
     const int kmax_w = kb0 * kBlock + 64 * wave + 63;
     int lo_w = min(sek[0], sek[1]);
@@ -529,6 +531,44 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
     for (int kk = 0; kk < 2; ++kk) {
         if (key[kk] >= L) continue;
         const int64_t off = int64_t(key[kk]) * kv_stride + hkv * D + 4 * h;
+        if constexpr (kRope) {
+            // the gradient w.r.t. the unrotated key: rotate back by the key's
+            // tree position; d = 32 t + 8 j + 4 h + r pairs with t + NT/2
+            const float* cs = rope_tab + (int64_t(pos[key[kk]]) * (D / 2) + 4 * h) * 2;
+#pragma unroll
+            for (int t = 0; t < NT / 2; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4* t4 = reinterpret_cast<const f32x4*>(cs + 2 * (32 * t + 8 * j));
+                    const f32x4 c0 = t4[0], c1 = t4[1];
+                    const float c[4] = {c0[0], c0[2], c1[0], c1[2]}, sn[4] = {c0[1], c0[3], c1[1], c1[3]};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float x1 = dk[kk][t][4 * j + r], x2 = dk[kk][t + NT / 2][4 * j + r];
+                        rope_pair<true>(x1, x2, c[r], sn[r]);
+                        dk[kk][t][4 * j + r] = x1;
+                        dk[kk][t + NT / 2][4 * j + r] = x2;
+                    }
+                }
+        }
+        if constexpr (kAcc) {
+            // add to float32 accumulators (this workgroup owns these keys'
+            // rows for the launch, so a plain read-modify-write)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int d0 = 32 * t + 8 * j;
+                    f32x4* ak = reinterpret_cast<f32x4*>(dKacc + off + d0);
+                    f32x4* av = reinterpret_cast<f32x4*>(dVacc + off + d0);
+                    const f32x4 xk = *ak, xv = *av;
+                    *ak = f32x4{xk[0] + dk[kk][t][4 * j] * scale, xk[1] + dk[kk][t][4 * j + 1] * scale,
+                                xk[2] + dk[kk][t][4 * j + 2] * scale, xk[3] + dk[kk][t][4 * j + 3] * scale};
+                    *av = f32x4{xv[0] + dv[kk][t][4 * j], xv[1] + dv[kk][t][4 * j + 1], xv[2] + dv[kk][t][4 * j + 2],
+                                xv[3] + dv[kk][t][4 * j + 3]};
+                }
+            continue;
+        }
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -545,13 +585,14 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
-template <int D, bool kDelta>
+template <int D, bool kDelta, bool kRope>
 __global__ __launch_bounds__(kThreads, 2) void dq_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const bf16* __restrict__ O, const float* __restrict__ LSE,
     float* __restrict__ Delta, float* __restrict__ NLS, bf16* __restrict__ dQ, const int32_t* __restrict__ se,
     const int32_t* __restrict__ q_order, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ row_ent,
-    int L, int Hq, int Hkv, float scale_log2, float scale) {
+    int L, int Hq, int Hkv, float scale_log2, float scale, const int32_t* __restrict__ pos,
+    const float* __restrict__ rope_tab) {
     using T = Tile<D>;
     constexpr int NS = D / 32, NT = D / 16;
     // K and V tiles and the keys' subtree ends, double-buffered
@@ -736,7 +777,26 @@ __global__ __launch_bounds__(kThreads, 2) void dq_bf16_kernel(
 
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
-        bf16* row = dQ + int64_t(qrow0 + 16 * qs + n) * q_stride + int64_t(h) * D + 4 * g;
+        const int qi = qrow0 + 16 * qs + n;
+        if constexpr (kRope) {
+            // the gradient w.r.t. the unrotated query: rotate back by the
+            // query's tree position; d = 16 t + 4 g + r pairs with t + NT/2
+            const float* cs = rope_tab + (int64_t(pos[qi]) * (D / 2) + 4 * g) * 2;
+#pragma unroll
+            for (int t = 0; t < NT / 2; ++t) {
+                const f32x4* t4 = reinterpret_cast<const f32x4*>(cs + 32 * t);
+                const f32x4 c0 = t4[0], c1 = t4[1];
+                const float c[4] = {c0[0], c0[2], c1[0], c1[2]}, sn[4] = {c0[1], c0[3], c1[1], c1[3]};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float x1 = dq[qs][t][r], x2 = dq[qs][t + NT / 2][r];
+                    rope_pair<true>(x1, x2, c[r], sn[r]);
+                    dq[qs][t][r] = x1;
+                    dq[qs][t + NT / 2][r] = x2;
+                }
+            }
+        }
+        bf16* row = dQ + int64_t(qi) * q_stride + int64_t(h) * D + 4 * g;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const f32x4 a = dq[qs][t] * scale;
@@ -748,29 +808,54 @@ __global__ __launch_bounds__(kThreads, 2) void dq_bf16_kernel(
 template <int D>
 hipError_t launch_bwd_d(int phase, const bf16* Q, const bf16* K, const bf16* V, const bf16* O, const float* lse,
                         const bf16* dO, bf16* dQ, bf16* dK, bf16* dV, const int32_t* se, const MetaPtrs& mp,
-                        float* delta, const AttnShape& sh, hipStream_t stream) {
+                        float* delta, const AttnShape& sh, hipStream_t stream, const RowSel& sel,
+                        const RopeArgs& rope) {
     const int L = int(sh.L);
     const int64_t rows = int64_t(L) * sh.Hq;
     const float sl2 = sh.scale * kLog2e;
     float* nls = delta + rows;  // second half of the workspace
-    const unsigned dq_grid = unsigned(sh.nb) * unsigned(sh.Hq);
+    // dQ work items: (query block of the list, query head); dK/dV: (key-block
+    // pair of the heaviest-first order, key/value head)
+    const int32_t* q_order = sel.q_list ? sel.q_list : mp.q_order;
+    const unsigned dq_grid = (sel.q_list ? unsigned(sel.n_q) : unsigned(sh.nb)) * unsigned(sh.Hq);
+    const unsigned n_pairs = sel.n_pairs >= 0 ? unsigned(sel.n_pairs) : unsigned((sh.nb + 1) / 2);
+    const int qb_lo = sel.qb_lo, qb_hi = sel.qb_hi;
     if (phase == kPhaseDelta)
         delta_bf16_kernel<D><<<dim3(unsigned((L + 256 / (D / 8) - 1) / (256 / (D / 8))), unsigned(sh.Hq)), 256, 0,
                                stream>>>(O, dO, lse, delta, nls, 1.0f / sh.scale, L, sh.Hq);
     // the whole backward: dQ first, computing Delta itself and leaving it
     // (with -LSE / scale) for dK/dV, which saves a pass over O and dO
-    if (phase == kPhaseAll || phase == kPhaseDqDelta)
-        dq_bf16_kernel<D, true><<<dq_grid, kThreads, 0, stream>>>(Q, K, V, dO, O, lse, delta, nls, dQ, se,
-                                                                   mp.q_order, mp.row_ptr, mp.row_ent, L, sh.Hq,
-                                                                   sh.Hkv, sl2, sh.scale);
-    if (phase == kPhaseAll || phase == kPhaseDkdv)
-        dkdv_bf16_kernel<D><<<unsigned((sh.nb + 1) / 2) * unsigned(sh.Hkv), kThreads, 0, stream>>>(
-            Q, K, V, dO, nls, delta, dK, dV, se, mp.p_order, mp.blk_min, mp.blk_max, L, sh.Hq, sh.Hkv, sl2,
-            sh.scale);
-    if (phase == kPhaseDq)
-        dq_bf16_kernel<D, false><<<dq_grid, kThreads, 0, stream>>>(Q, K, V, dO, O, lse, delta, nls, dQ, se,
-                                                                    mp.q_order, mp.row_ptr, mp.row_ent, L, sh.Hq,
-                                                                    sh.Hkv, sl2, sh.scale);
+    const bool fuse_rope = rope.tab != nullptr;
+    if (fuse_rope && (sel.dk_acc || phase == kPhaseDq)) return hipErrorInvalidValue;  // not combined
+    if ((phase == kPhaseAll || phase == kPhaseDqDelta) && dq_grid > 0) {
+        if (fuse_rope)
+            dq_bf16_kernel<D, true, true><<<dq_grid, kThreads, 0, stream>>>(
+                Q, K, V, dO, O, lse, delta, nls, dQ, se, q_order, mp.row_ptr, mp.row_ent, L, sh.Hq, sh.Hkv, sl2,
+                sh.scale, rope.pos, rope.tab);
+        else
+            dq_bf16_kernel<D, true, false><<<dq_grid, kThreads, 0, stream>>>(
+                Q, K, V, dO, O, lse, delta, nls, dQ, se, q_order, mp.row_ptr, mp.row_ent, L, sh.Hq, sh.Hkv, sl2,
+                sh.scale, nullptr, nullptr);
+    }
+    if ((phase == kPhaseAll || phase == kPhaseDkdv) && n_pairs > 0) {
+        const dim3 grid(n_pairs * unsigned(sh.Hkv));
+        if (sel.dk_acc)
+            dkdv_bf16_kernel<D, true, false><<<grid, kThreads, 0, stream>>>(
+                Q, K, V, dO, nls, delta, dK, dV, sel.dk_acc, sel.dv_acc, se, mp.p_order, mp.blk_min, mp.blk_max, L,
+                sh.Hq, sh.Hkv, qb_lo, qb_hi, sl2, sh.scale, nullptr, nullptr);
+        else if (fuse_rope)
+            dkdv_bf16_kernel<D, false, true><<<grid, kThreads, 0, stream>>>(
+                Q, K, V, dO, nls, delta, dK, dV, nullptr, nullptr, se, mp.p_order, mp.blk_min, mp.blk_max, L,
+                sh.Hq, sh.Hkv, qb_lo, qb_hi, sl2, sh.scale, rope.pos, rope.tab);
+        else
+            dkdv_bf16_kernel<D, false, false><<<grid, kThreads, 0, stream>>>(
+                Q, K, V, dO, nls, delta, dK, dV, nullptr, nullptr, se, mp.p_order, mp.blk_min, mp.blk_max, L,
+                sh.Hq, sh.Hkv, qb_lo, qb_hi, sl2, sh.scale, nullptr, nullptr);
+    }
+    if (phase == kPhaseDq && dq_grid > 0)
+        dq_bf16_kernel<D, false, false><<<dq_grid, kThreads, 0, stream>>>(
+            Q, K, V, dO, O, lse, delta, nls, dQ, se, q_order, mp.row_ptr, mp.row_ent, L, sh.Hq, sh.Hkv, sl2,
+            sh.scale, nullptr, nullptr);
     return hipGetLastError();
 }
 
@@ -778,7 +863,8 @@ hipError_t launch_bwd_d(int phase, const bf16* Q, const bf16* K, const bf16* V, 
 
 hipError_t launch_bwd_bf16(int phase, const void* q, const void* k, const void* v, const void* o, const float* lse,
                            const void* dout, void* dq, void* dk, void* dv, const int32_t* se, const MetaPtrs& mp,
-                           float* delta, const AttnShape& sh, hipStream_t stream) {
+                           float* delta, const AttnShape& sh, hipStream_t stream, const RowSel& sel,
+                           const RopeArgs& rope) {
     const auto* Q = static_cast<const bf16*>(q);
     const auto* K = static_cast<const bf16*>(k);
     const auto* V = static_cast<const bf16*>(v);
@@ -787,8 +873,8 @@ hipError_t launch_bwd_bf16(int phase, const void* q, const void* k, const void* 
     auto* dQ = static_cast<bf16*>(dq);
     auto* dK = static_cast<bf16*>(dk);
     auto* dV = static_cast<bf16*>(dv);
-    if (sh.D == 128) return launch_bwd_d<128>(phase, Q, K, V, O, lse, G, dQ, dK, dV, se, mp, delta, sh, stream);
-    if (sh.D == 64) return launch_bwd_d<64>(phase, Q, K, V, O, lse, G, dQ, dK, dV, se, mp, delta, sh, stream);
+    if (sh.D == 128) return launch_bwd_d<128>(phase, Q, K, V, O, lse, G, dQ, dK, dV, se, mp, delta, sh, stream, sel, rope);
+    if (sh.D == 64) return launch_bwd_d<64>(phase, Q, K, V, O, lse, G, dQ, dK, dV, se, mp, delta, sh, stream, sel, rope);
     return hipErrorInvalidValue;
 }
 

@@ -1,5 +1,5 @@
-// C ABI of libtreeattn: error state, argument validation and dispatch to the
-// device launchers.  See include/tree_attn.h for the contract.
+// C ABI of libtreeattn: argument validation and dispatch to the device
+// launchers.  See include/tree_attn.h for the contract.
 
 #include <cmath>
 #include <cstdarg>
@@ -11,22 +11,6 @@
 #include "status.h"
 
 namespace treeattn {
-
-namespace {
-thread_local std::string g_last_error;
-}
-
-int set_error(int code, const char* fmt, ...) {
-    char buf[512];
-    va_list ap;
-    va_start(ap, fmt);
-    vsnprintf(buf, sizeof buf, fmt, ap);
-    va_end(ap);
-    g_last_error = buf;
-    return code;
-}
-
-void clear_error() { g_last_error.clear(); }
 
 namespace {
 
@@ -78,8 +62,6 @@ using namespace treeattn;
 extern "C" {
 
 int tree_abi_version(void) { return TREE_ATTN_ABI_VERSION; }
-
-const char* tree_last_error(void) { return g_last_error.c_str(); }
 
 size_t tree_meta_workspace_bytes(int64_t L) {
     if (L <= 0 || L % kBlock != 0 || L > kMaxL) return 0;
@@ -164,6 +146,72 @@ int tree_attn_bwd_phase(int32_t phase, const void* q, const void* k, const void*
                            static_cast<const float*>(dout), static_cast<float*>(dq), static_cast<float*>(dk),
                            static_cast<float*>(dv), d_se, mp, delta, sh, s);
     return hip_status(e, "tree_attn_bwd");
+}
+
+size_t tree_rope_table_bytes(int64_t P, int32_t D) {
+    if (P <= 0 || P > kMaxL || D <= 0 || D % 16 != 0 || D > 4096) return 0;
+    return round256(size_t(P) * size_t(D / 2) * 2 * sizeof(float));
+}
+
+int tree_rope_table(double base, int64_t P, int32_t D, float* d_tab, size_t tab_bytes, void* stream) {
+    const size_t need = tree_rope_table_bytes(P, D);
+    if (need == 0) return set_error(TREE_E_ARG, "tree_rope_table: bad P=%lld or D=%d", (long long)P, D);
+    if (!std::isfinite(base) || !(base > 1.0)) return set_error(TREE_E_ARG, "tree_rope_table: base must be > 1");
+    if (!d_tab || !aligned16(d_tab)) return set_error(TREE_E_ARG, "tree_rope_table: NULL or misaligned table");
+    if (tab_bytes < need) return set_error(TREE_E_WORKSPACE, "tree_rope_table: %zu < %zu bytes", tab_bytes, need);
+    return hip_status(launch_rope_table(d_tab, P, D, base, static_cast<hipStream_t>(stream)), "tree_rope_table");
+}
+
+int tree_attn_fwd_rope(const void* q, const void* k, const void* v, void* o, float* lse, void* q_rot, void* k_rot,
+                       const int32_t* d_pos, const float* d_tab, size_t tab_bytes, const int32_t* d_se,
+                       const void* d_meta_ws, int64_t L, int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                       void* stream) {
+    if (int rc = check_attn("tree_attn_fwd_rope", L, Hq, Hkv, D, scale, TREE_DTYPE_BF16)) return rc;
+    if (!q || !k || !v || !o || !lse || !q_rot || !k_rot || !d_pos || !d_tab || !d_se || !d_meta_ws)
+        return set_error(TREE_E_ARG, "tree_attn_fwd_rope: NULL device pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(q_rot) || !aligned16(k_rot) ||
+        !aligned16(d_tab) || !aligned16(d_se) || !aligned16(d_meta_ws))
+        return set_error(TREE_E_ARG, "tree_attn_fwd_rope: tensors must be 16-byte aligned");
+    if (tab_bytes < tree_rope_table_bytes(L, D))
+        return set_error(TREE_E_WORKSPACE, "tree_attn_fwd_rope: the table must cover positions 0 .. L - 1");
+    const AttnShape sh{L, int(L / kBlock), Hq, Hkv, D, scale};
+    const MetaPtrs mp = meta_ptrs(d_meta_ws, L);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_rope_tab(k, k_rot, d_pos, d_tab, L, Hkv, D, s);
+    RopeArgs rope;
+    rope.pos = d_pos;
+    rope.tab = d_tab;
+    rope.q_rot = q_rot;
+    if (e == hipSuccess) e = launch_fwd_bf16(q, k_rot, v, o, lse, d_se, mp, sh, s, RowSel(), rope);
+    return hip_status(e, "tree_attn_fwd_rope");
+}
+
+int tree_attn_bwd_rope(const void* q_rot, const void* k_rot, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, const int32_t* d_pos, const float* d_tab,
+                       size_t tab_bytes, const int32_t* d_se, const void* d_meta_ws, void* d_ws, size_t ws_bytes,
+                       int64_t L, int32_t Hq, int32_t Hkv, int32_t D, float scale, void* stream) {
+    if (int rc = check_attn("tree_attn_bwd_rope", L, Hq, Hkv, D, scale, TREE_DTYPE_BF16)) return rc;
+    if (!q_rot || !k_rot || !v || !o || !lse || !dout || !dq || !dk || !dv || !d_pos || !d_tab || !d_se ||
+        !d_meta_ws || !d_ws)
+        return set_error(TREE_E_ARG, "tree_attn_bwd_rope: NULL device pointer");
+    if (!aligned16(q_rot) || !aligned16(k_rot) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+        !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(lse) || !aligned16(d_tab) ||
+        !aligned16(d_se) || !aligned16(d_meta_ws) || !aligned16(d_ws))
+        return set_error(TREE_E_ARG, "tree_attn_bwd_rope: tensors must be 16-byte aligned");
+    if (tab_bytes < tree_rope_table_bytes(L, D))
+        return set_error(TREE_E_WORKSPACE, "tree_attn_bwd_rope: the table must cover positions 0 .. L - 1");
+    const size_t need = tree_attn_bwd_workspace_bytes(L, Hq, D, TREE_DTYPE_BF16);
+    if (ws_bytes < need)
+        return set_error(TREE_E_WORKSPACE, "tree_attn_bwd_rope: workspace %zu < %zu bytes", ws_bytes, need);
+    const AttnShape sh{L, int(L / kBlock), Hq, Hkv, D, scale};
+    const MetaPtrs mp = meta_ptrs(d_meta_ws, L);
+    RopeArgs rope;
+    rope.pos = d_pos;
+    rope.tab = d_tab;
+    return hip_status(launch_bwd_bf16(kPhaseAll, q_rot, k_rot, v, o, lse, dout, dq, dk, dv, d_se, mp,
+                                      static_cast<float*>(d_ws), sh, static_cast<hipStream_t>(stream), RowSel(),
+                                      rope),
+                      "tree_attn_bwd_rope");
 }
 
 int tree_logits_stats(const void* logits, int64_t L, int64_t V, int32_t dtype, float* d_lse, float* d_ent,

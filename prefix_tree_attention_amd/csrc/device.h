@@ -95,16 +95,40 @@ struct AttnShape {
     float scale;
 };
 
+// Restriction of one attention launch to some query blocks, for the
+// depth-first variant, which runs one node's (or one chunk's) queries at a
+// time over a stack of its ancestors' keys.  The default runs everything.
+struct RowSel {
+    const int32_t* q_list = nullptr;  // fwd / dQ: the query blocks to run (null: all, heaviest first)
+    int n_q = 0;                      // entries of q_list
+    int qb_lo = 0, qb_hi = 1 << 30;   // dK/dV: only query blocks in [qb_lo, qb_hi) contribute
+    int n_pairs = -1;                 // dK/dV: run the first n_pairs key-block pairs of the
+                                      // heaviest-first order (-1: all)
+    float* dk_acc = nullptr;          // dK/dV: if set, add scale * dK and dV in float32 to
+    float* dv_acc = nullptr;          // these [L, Hkv, D] arrays instead of writing dK / dV
+};
+
+// Rotary embedding fused into the attention kernels: Q rotated at the
+// forward's register load (and written to q_rot for the backward), dQ and dK
+// rotated back in the backward's epilogues; pos = the trie's position ids,
+// tab = launch_rope_table's (cos, sin) rows.  The default fuses nothing.
+struct RopeArgs {
+    const int32_t* pos = nullptr;
+    const float* tab = nullptr;
+    void* q_rot = nullptr;  // forward only
+};
+
 hipError_t launch_meta(const int32_t* se, int64_t L, int32_t* pos, uint8_t* tile_class, void* ws,
                        hipStream_t stream);
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            const int32_t* se, const MetaPtrs& mp, const AttnShape& sh,
-                           hipStream_t stream);
+                           hipStream_t stream, const RowSel& sel = RowSel(), const RopeArgs& rope = RopeArgs());
 hipError_t launch_bwd_bf16(int phase, const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
                            const int32_t* se, const MetaPtrs& mp, float* delta,
-                           const AttnShape& sh, hipStream_t stream);
+                           const AttnShape& sh, hipStream_t stream, const RowSel& sel = RowSel(),
+                           const RopeArgs& rope = RopeArgs());
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                           const int32_t* se, const MetaPtrs& mp, const AttnShape& sh,
                           hipStream_t stream);
@@ -113,12 +137,37 @@ hipError_t launch_bwd_f32(int phase, const float* q, const float* k, const float
                           const int32_t* se, const MetaPtrs& mp, float* delta,
                           const AttnShape& sh, hipStream_t stream);
 
+// Depth-first execution: the node segments on the stack of one frame (rows
+// [row0, row0 + len) each, subtree end top_se) and the leaf rows being run
+// (frame rows [leaf_row0, leaf_row0 + leaf_len) = packed rows from leaf_p0).
+constexpr int kDfsMaxSegments = 240;
+struct DfsSegments {
+    int n, top_se;
+    int leaf_row0, leaf_len, leaf_p0;
+    int row0[kDfsMaxSegments];
+    int len[kDfsMaxSegments];
+};
+hipError_t launch_dfs_se(int32_t* se, int64_t rows, const int32_t* packed_se, const DfsSegments& a,
+                         hipStream_t stream);
+hipError_t launch_dfs_copy_rows(const void* src, void* dst, int64_t s0, int64_t d0, int64_t nrows, int64_t row_bytes,
+                                hipStream_t stream);
+hipError_t launch_dfs_copy_cols(const float* src, float* dst, int64_t Ls, int64_t Ld, int64_t s0, int64_t d0,
+                                int64_t n, int H, hipStream_t stream);
+hipError_t launch_dfs_fill(void* p, int64_t bytes, uint32_t pattern, hipStream_t stream);
+hipError_t launch_dfs_fill_cols(float* p, int64_t L, int64_t i0, int64_t n, int H, float value, hipStream_t stream);
+hipError_t launch_dfs_iota(int32_t* p, int n, hipStream_t stream);
+hipError_t launch_dfs_emit(const float* acc, void* out, int64_t s0, int64_t d0, int64_t nrows, int64_t width,
+                           hipStream_t stream);
+
 hipError_t launch_logits_stats(const void* logits, int64_t L, int64_t V, int dtype, float* lse, float* ent,
                                hipStream_t stream);
 hipError_t launch_gather_logprobs(const void* logits, int64_t L, int64_t V, int dtype, const float* lse,
                                   const float* ent, const int32_t* ids, const int32_t* row_pos, int64_t B, int64_t S,
                                   float pad_value, float* out_logp, float* out_ent, hipStream_t stream);
 
+hipError_t launch_rope_table(float* tab, int64_t P, int D, double base, hipStream_t stream);
+hipError_t launch_rope_tab(const void* x, void* y, const int32_t* pos, const float* tab, int64_t L, int H, int D,
+                           hipStream_t stream);
 hipError_t launch_rope(const void* x, void* y, const int32_t* pos, int64_t L, int H, int D, double base, int inverse,
                        int dtype, hipStream_t stream);
 

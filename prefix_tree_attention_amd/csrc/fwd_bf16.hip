@@ -38,12 +38,13 @@ constexpr int kThreads = 256;
 constexpr int kStep = kTileRows;  // keys per pipeline step
 constexpr float kRescaleSlack = 8.f;  // log2 units: p <= 256 between rescales
 
-template <int D>
+template <int D, bool kRope>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, const int32_t* __restrict__ se,
     const int32_t* __restrict__ q_order, const int32_t* __restrict__ row_ptr,
-    const int32_t* __restrict__ row_ent, int L, int Hq, int Hkv, float scale_log2) {
+    const int32_t* __restrict__ row_ent, int L, int Hq, int Hkv, float scale_log2,
+    const int32_t* __restrict__ pos, const float* __restrict__ rope_tab, bf16* __restrict__ Qrot) {
     using T = Tile<D>;
     constexpr int NX = D / 16;  // k-steps of S^T = K Q^T
     constexpr int NT = D / 32;  // 32-row d-blocks of O^T
@@ -70,6 +71,37 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 #pragma unroll
     for (int x = 0; x < NX; ++x)
         qf[x] = __builtin_bit_cast(bf16x8, ld16(Q + int64_t(qi) * q_stride + int64_t(h_q) * D + 16 * x + 8 * h));
+    if constexpr (kRope) {
+        // rotary embedding by the query's tree position, on the operand as it
+        // is loaded: chunk x holds d = 16 x + 8 h + u, its rotation partners
+        // d + D/2 are chunk x + NX/2 of the same lane; the rotated query also
+        // goes to Qrot for the backward
+        const float* cs = rope_tab + (int64_t(pos[qi]) * (D / 2) + 8 * h) * 2;
+#pragma unroll
+        for (int x = 0; x < NX / 2; ++x) {
+            const f32x4* t4 = reinterpret_cast<const f32x4*>(cs + 32 * x);
+            const f32x4 c0 = t4[0], c1 = t4[1], c2 = t4[2], c3 = t4[3];
+            const float c[8] = {c0[0], c0[2], c1[0], c1[2], c2[0], c2[2], c3[0], c3[2]};
+            const float sn[8] = {c0[1], c0[3], c1[1], c1[3], c2[1], c2[3], c3[1], c3[3]};
+            f32x4 a0, a1, b0, b1;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float x1 = float(qf[x][u]), x2 = float(qf[x + NX / 2][u]);
+                rope_pair<false>(x1, x2, c[u], sn[u]);
+                a0[u] = x1;
+                b0[u] = x2;
+                float y1 = float(qf[x][u + 4]), y2 = float(qf[x + NX / 2][u + 4]);
+                rope_pair<false>(y1, y2, c[u + 4], sn[u + 4]);
+                a1[u] = y1;
+                b1[u] = y2;
+            }
+            qf[x] = to_bf16x8(a0, a1);
+            qf[x + NX / 2] = to_bf16x8(b0, b1);
+        }
+        bf16* qr = Qrot + int64_t(qi) * q_stride + int64_t(h_q) * D + 8 * h;
+#pragma unroll
+        for (int x = 0; x < NX; ++x) st16(qr + 16 * x, __builtin_bit_cast(u32x4, qf[x]));
+    }
     // loop-invariant swizzled LDS offsets of this lane's operand reads
     int roff[NX];  // K rows: row j32, chunk 2 x + h
 #pragma unroll
@@ -358,19 +390,34 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            const int32_t* se, const MetaPtrs& mp, const AttnShape& sh,
-                           hipStream_t stream) {
-    const dim3 grid(unsigned(sh.nb) * unsigned(sh.Hq));
+                           hipStream_t stream, const RowSel& sel, const RopeArgs& rope) {
+    // the work items are (query block of the list, query head)
+    const int32_t* q_order = sel.q_list ? sel.q_list : mp.q_order;
+    const unsigned n_q = sel.q_list ? unsigned(sel.n_q) : unsigned(sh.nb);
+    if (n_q == 0) return hipSuccess;
+    const dim3 grid(n_q * unsigned(sh.Hq));
     const float sl2 = sh.scale * 1.4426950408889634f;
     const auto* Q = static_cast<const bf16*>(q);
     const auto* K = static_cast<const bf16*>(k);
     const auto* V = static_cast<const bf16*>(v);
     auto* O = static_cast<bf16*>(o);
-    if (sh.D == 128)
-        fwd_bf16_kernel<128><<<grid, kThreads, 0, stream>>>(Q, K, V, O, lse, se, mp.q_order, mp.row_ptr,
-                                                             mp.row_ent, int(sh.L), sh.Hq, sh.Hkv, sl2);
+    auto* Qr = static_cast<bf16*>(rope.q_rot);
+    if (sh.D == 128 && rope.tab)
+        fwd_bf16_kernel<128, true><<<grid, kThreads, 0, stream>>>(Q, K, V, O, lse, se, q_order, mp.row_ptr,
+                                                                   mp.row_ent, int(sh.L), sh.Hq, sh.Hkv, sl2,
+                                                                   rope.pos, rope.tab, Qr);
+    else if (sh.D == 128)
+        fwd_bf16_kernel<128, false><<<grid, kThreads, 0, stream>>>(Q, K, V, O, lse, se, q_order, mp.row_ptr,
+                                                                    mp.row_ent, int(sh.L), sh.Hq, sh.Hkv, sl2,
+                                                                    nullptr, nullptr, nullptr);
+    else if (sh.D == 64 && rope.tab)
+        fwd_bf16_kernel<64, true><<<grid, kThreads, 0, stream>>>(Q, K, V, O, lse, se, q_order, mp.row_ptr,
+                                                                  mp.row_ent, int(sh.L), sh.Hq, sh.Hkv, sl2,
+                                                                  rope.pos, rope.tab, Qr);
     else if (sh.D == 64)
-        fwd_bf16_kernel<64><<<grid, kThreads, 0, stream>>>(Q, K, V, O, lse, se, mp.q_order, mp.row_ptr,
-                                                            mp.row_ent, int(sh.L), sh.Hq, sh.Hkv, sl2);
+        fwd_bf16_kernel<64, false><<<grid, kThreads, 0, stream>>>(Q, K, V, O, lse, se, q_order, mp.row_ptr,
+                                                                   mp.row_ent, int(sh.L), sh.Hq, sh.Hkv, sl2,
+                                                                   nullptr, nullptr, nullptr);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -65,6 +65,22 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const f32x4& lo, const f32x4& hi) {
 
 __device__ __forceinline__ float bf16_to_float(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
+// Rotary embedding of N element pairs (x1[u], x2[u]) = (x_j, x_{j + D/2}),
+// j = j0 + u, by a table row of (cos, sin) float pairs cs[u]; the rotation
+// arithmetic of the standalone pass (rope.hip): forward
+//   (x1 c - x2 s, x2 c + x1 s), inverse (the gradient map) (x1 c + x2 s, x2 c - x1 s).
+template <bool kInverse>
+__device__ __forceinline__ void rope_pair(float& x1, float& x2, float c, float s) {
+    const float a = x1, b = x2;
+    if constexpr (kInverse) {
+        x1 = __builtin_fmaf(a, c, b * s);
+        x2 = __builtin_fmaf(b, c, -a * s);
+    } else {
+        x1 = __builtin_fmaf(a, c, -b * s);
+        x2 = __builtin_fmaf(b, c, a * s);
+    }
+}
+
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ void st8(void* p, const u32x2& v) { *reinterpret_cast<u32x2*>(p) = v; }

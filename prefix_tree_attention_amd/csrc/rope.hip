@@ -108,7 +108,74 @@ __global__ __launch_bounds__(256) void rope_vec_kernel(const T* x, T* y,  // may
     }
 }
 
+// (cos, sin) of p f_j for every position p < P and pair j < D/2, as the
+// rotation passes form them (float64 angle, rounded to float32): the
+// operand table of the attention kernels that rotate Q / K where they load
+// them and rotate dQ / dK back where they store them.
+__global__ __launch_bounds__(256) void rope_table_kernel(float* __restrict__ tab, int64_t P, int D, double log2_base) {
+    const int half = D / 2;
+    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= P * half) return;
+    const int64_t p = idx / half;
+    const int j = int(idx % half);
+    double sd, cd;
+    sincos(double(p) * exp2(-2.0 * double(j) / double(D) * log2_base), &sd, &cd);
+    tab[2 * idx] = float(cd);
+    tab[2 * idx + 1] = float(sd);
+}
+
+// Rotation of x [L, H, D] bf16 by a (cos, sin) table row per token, eight
+// pairs per lane, every head: the K operand of the fused forward.  Same
+// arithmetic as the Q rotation inside the forward kernel.
+__global__ __launch_bounds__(256) void rope_tab_kernel(const bf16* __restrict__ x, bf16* __restrict__ y,
+                                                       const int32_t* __restrict__ pos, const float* __restrict__ tab,
+                                                       int64_t L, int H, int D) {
+    const int half = D / 2, lanes = half / 8;
+    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= L * lanes) return;
+    const int64_t i = idx / lanes;
+    const int j0 = int(idx % lanes) * 8;
+    const f32x4* t4 = reinterpret_cast<const f32x4*>(tab + (int64_t(pos[i]) * half + j0) * 2);
+    const f32x4 c0 = t4[0], c1 = t4[1], c2 = t4[2], c3 = t4[3];
+    const float c[8] = {c0[0], c0[2], c1[0], c1[2], c2[0], c2[2], c3[0], c3[2]};
+    const float sn[8] = {c0[1], c0[3], c1[1], c1[3], c2[1], c2[3], c3[1], c3[3]};
+    for (int h = 0; h < H; ++h) {
+        const int64_t o = (i * H + h) * D + j0;
+        const bf16x8 a = __builtin_bit_cast(bf16x8, ld16(x + o)), b = __builtin_bit_cast(bf16x8, ld16(x + o + half));
+        f32x4 a0, a1, b0, b1;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            float x1 = float(a[u]), x2 = float(b[u]);
+            rope_pair<false>(x1, x2, c[u], sn[u]);
+            a0[u] = x1;
+            b0[u] = x2;
+            float y1 = float(a[u + 4]), y2 = float(b[u + 4]);
+            rope_pair<false>(y1, y2, c[u + 4], sn[u + 4]);
+            a1[u] = y1;
+            b1[u] = y2;
+        }
+        st16(y + o, __builtin_bit_cast(u32x4, to_bf16x8(a0, a1)));
+        st16(y + o + half, __builtin_bit_cast(u32x4, to_bf16x8(b0, b1)));
+    }
+}
+
 }  // namespace
+
+hipError_t launch_rope_tab(const void* x, void* y, const int32_t* pos, const float* tab, int64_t L, int H, int D,
+                           hipStream_t stream) {
+    const int64_t n = L * (D / 16);
+    if (n <= 0) return hipSuccess;
+    rope_tab_kernel<<<unsigned((n + 255) / 256), 256, 0, stream>>>(static_cast<const bf16*>(x), static_cast<bf16*>(y),
+                                                                   pos, tab, L, H, D);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_table(float* tab, int64_t P, int D, double base, hipStream_t stream) {
+    const int64_t n = P * (D / 2);
+    if (n <= 0) return hipSuccess;
+    rope_table_kernel<<<unsigned((n + 255) / 256), 256, 0, stream>>>(tab, P, D, log2(base));
+    return hipGetLastError();
+}
 
 hipError_t launch_rope(const void* x, void* y, const int32_t* pos, int64_t L, int H, int D, double base, int inverse,
                        int dtype, hipStream_t stream) {

@@ -392,3 +392,57 @@ def test_partition_errors(L):
     assert e.value.code == -5
     g, tau, costs = pta.partition(ids, mask, 5)  # more workers than rows
     assert tau == 4 and g.tolist() == [0, 1, 2] and costs.tolist() == [4, 4, 3, 0, 0]  # one row per worker
+
+
+def _dfs_cases():
+    ids, mask = workloads.worked_example()
+    yield "worked-example", ids, mask, 128
+    for kind in workloads.SMALL_KINDS:
+        ids, mask, M = workloads.small_workload(kind)
+        yield kind, ids, mask, M
+    for c in ("1", "2", "4a", "4b"):
+        w = workloads.make_workload(c)
+        yield f"config{c}", w.ids, w.mask, w.max_tokens_per_mb
+
+
+@pytest.mark.parametrize("chunk", [128, 2048])
+def test_dfs_plan_stack_matches_oracle(L, chunk):
+    """tree_dfs_plan's stack peak and longest path equal the depth-first
+    oracle's (the schedule's quantities that do not depend on how leaves are
+    batched); the frame holds the stack's node segments from 128-aligned
+    rows plus the leaf rows."""
+    for name, ids, mask, M in _dfs_cases():
+        tl, _ = pta.pack(ids, mask, M)
+        for t, (pl, po) in enumerate(zip(tl, oracle.pack(ids, mask, M))):
+            plan = pta.dfs_plan(pl, chunk)
+            z = np.zeros((po.L, 1, 2))
+            st = oracle.dfs_attention(po, z, z, z, z, 1.0, chunk=chunk)[5] if po.L <= 8192 else None
+            if st is not None:
+                assert plan["peak_stack_tokens"] == st["peak_stack_tokens"], (name, t)
+                assert plan["max_path_tokens"] == st["max_path_tokens"], (name, t)
+            assert plan["rows"] % 256 == 0 and plan["rows"] >= plan["stack_rows"]
+            assert plan["leaf_rows"] >= max(chunk, 1) and plan["leaf_rows"] % 128 == 0
+    w = workloads.make_workload("4a")
+    (pl,), _ = pta.pack(w.ids, w.mask, w.max_tokens_per_mb)
+    plan = pta.dfs_plan(pl, 2048)
+    assert plan["peak_stack_tokens"] == 16384 and plan["max_path_tokens"] == 16640 and plan["max_depth"] == 1
+    assert plan["rows"] == 16384 + 2048 and plan["leaf_groups"] == 8 and plan["chunks"] == 8 + 8
+
+
+def test_dfs_entry_points_validate(L):
+    ids, mask = workloads.worked_example()
+    (pl,), _ = pta.pack(ids, mask, 128)
+    with pytest.raises(pta.TreeAttnError, match="chunk"):
+        pta.dfs_plan(pl, 100)
+    bad = pta.PackedTrie(**{**pl.__dict__, "node_start": pl.node_start + 1})
+    with pytest.raises(pta.TreeAttnError, match="pre-order"):
+        pta.dfs_plan(bad, 2048)
+    bad = pta.PackedTrie(**{**pl.__dict__, "node_parent": np.full_like(pl.node_parent, 7)})
+    with pytest.raises(pta.TreeAttnError, match="parent"):
+        pta.dfs_plan(bad, 2048)
+    p = ctypes.c_void_p(256)
+    ns, ne, npar = (np.ascontiguousarray(x, np.int32) for x in (pl.node_start, pl.node_end, pl.node_parent))
+    args = [ns.ctypes.data, ne.ctypes.data, npar.ctypes.data, ns.size, pl.n_tokens]
+    # bad heads and a missing workspace are rejected before any device work
+    assert L.tree_attn_dfs(*args, *([p] * 10), None, 1 << 30, 128, 6, 4, 128, 0.1, 2048, None) == -5
+    assert L.tree_attn_dfs(*args, *([p] * 10), p, 0, 128, 8, 2, 128, 0.1, 2048, None) == -6
