@@ -310,21 +310,23 @@ int tree_attn_bwd_noalloc(const void* q, const void* k, const void* v, const voi
  * stack; leaves run forward and backward at once and are never pushed ("cut
  * tail": no later token attends to them); leaving a node runs its backward,
  * after every sequence below it has added its gradient to the node's keys,
- * and pops it.  Nodes longer than `chunk` tokens run in chunks of at most
- * `chunk` queries.  Device memory (the frame) is bounded by the longest
- * path, not the tree.  Consecutive sibling leaves run together, up to the
- * frame's leaf capacity (the longest leaf or `chunk`, whichever is more):
- * the same computation as visiting them one by one.  bf16 only.
+ * and pops it.  Internal nodes and leaves longer than `chunk` tokens run in
+ * chunks of at most `chunk` queries.  Device memory (the frame) is bounded by
+ * the longest path, not the tree.  Consecutive sibling leaves of at most
+ * `chunk` tokens run together in one launch, up to the frame's leaf rows
+ * (4 * chunk or the longest leaf, whichever is more): the same computation
+ * as visiting them one by one.  bf16 only.
  * ---------------------------------------------------------------------- */
 typedef struct {
     int64_t rows;              /* frame length the kernels run on (multiple of 256) */
     int64_t stack_rows;        /* most frame rows the stack occupies (each node from a
                                   128-aligned row) */
-    int64_t leaf_rows;         /* frame rows for the leaves being run */
+    int64_t leaf_rows;         /* most rows one launch of leaves may take: 4 * chunk, or
+                                  the longest leaf if longer */
     int64_t peak_stack_tokens; /* most real tokens on the stack at once: the longest
                                   root-to-internal-node path */
     int64_t max_path_tokens;   /* longest root-to-leaf path */
-    int64_t chunks;            /* query chunks (one forward and one backward each) */
+    int64_t chunks;            /* query launches (one forward and one backward each) */
     int64_t leaf_groups;       /* launches of consecutive sibling leaves */
     int64_t max_depth;         /* most internal nodes on the stack */
 } tree_dfs_plan_t;

@@ -6,8 +6,8 @@
 // their forward against the stack; a leaf runs forward and backward at once
 // and is never pushed (its keys serve no later token); leaving a node runs
 // its backward -- every descendant's gradient having been accumulated into its
-// keys meanwhile -- and pops it.  Long nodes run in chunks of at most `chunk`
-// query tokens.
+// keys meanwhile -- and pops it.  Internal nodes and leaves longer than
+// `chunk` run in chunks of at most `chunk` query tokens.
 //
 // On the GPU the stack is a "frame": a layout of Lc rows holding the path's
 // node segments (each from a 128-aligned row, in path order) and, above them,
@@ -19,7 +19,9 @@
 // row is on the stack).  Consecutive sibling leaves run together, up to the
 // frame's leaf capacity, so a launch has enough work for the chip; that is
 // the same computation as visiting them one by one (they share the stack and
-// touch disjoint rows).  Memory is bounded by the longest path, not the tree.
+// touch disjoint rows); the leaf rows hold four chunks' worth, so that a leaf
+// launch's dK/dV grid has enough key-block pairs.  Memory is bounded by the
+// longest path, not the tree.
 
 #include <algorithm>
 #include <cmath>
@@ -102,14 +104,22 @@ struct Walk {
         while (i < list.size()) {
             const int v = list[i];
             if (t.leaf(v)) {
-                size_t j = i;
-                int64_t G = 0;
-                while (j < list.size() && t.leaf(list[j]) && G + t.size(list[j]) <= leaf_cap) G += t.size(list[j++]);
+                // a leaf longer than the chunk runs alone, in chunks; shorter
+                // consecutive sibling leaves run together in one launch, up to
+                // the frame's leaf rows
+                size_t j = i + 1;
+                int64_t G = t.size(v);
+                const bool long_leaf = G > chunk;
+                if (!long_leaf)
+                    while (j < list.size() && t.leaf(list[j]) && t.size(list[j]) <= chunk &&
+                           G + t.size(list[j]) <= leaf_cap)
+                        G += t.size(list[j++]);
                 for (size_t k = i; k < j; ++k) max_path = std::max(max_path, stack_tokens + t.size(list[k]));
                 rows_needed = std::max(rows_needed, top + round_up(G, kBlock));
-                chunks += (G + chunk - 1) / chunk;
+                const int64_t launch_rows = long_leaf ? chunk : round_up(G, kBlock);
+                chunks += (G + launch_rows - 1) / launch_rows;
                 ++groups;
-                if (int rc = ex.group(*this, t.start[v], G)) return rc;
+                if (int rc = ex.group(*this, t.start[v], G, launch_rows)) return rc;
                 i = j;
                 continue;
             }
@@ -139,7 +149,7 @@ struct Walk {
 };
 
 struct NoExec {
-    int group(Walk&, int64_t, int64_t) { return TREE_OK; }
+    int group(Walk&, int64_t, int64_t, int64_t) { return TREE_OK; }
     int push(Walk&, int, int64_t) { return TREE_OK; }
     int pop(Walk&, int, int64_t) { return TREE_OK; }
 };
@@ -150,7 +160,9 @@ int plan_of(const Tree& t, int32_t chunk, tree_dfs_plan_t* out) {
     int64_t longest_leaf = 0;
     for (int64_t v = 0; v < t.n_nodes; ++v)
         if (t.leaf(int(v))) longest_leaf = std::max(longest_leaf, t.size(int(v)));
-    const int64_t cap = round_up(std::max<int64_t>(chunk, longest_leaf), kBlock);
+    // leaf rows: four chunks of short leaves per launch (enough key-block
+    // pairs for the dK/dV grid to fill the chip), or the longest leaf
+    const int64_t cap = round_up(std::max<int64_t>(4 * int64_t(chunk), longest_leaf), kBlock);
     Walk w(t, chunk, cap);
     NoExec none;
     if (int rc = w.run(none)) return rc;
@@ -246,12 +258,13 @@ struct Exec {
         return st(launch_meta(f.se, rows, f.pos, f.tc, f.meta, s));
     }
 
-    // frame rows [r0, r0 + n) in chunks: forward, and/or backward
-    int chunks(int64_t r0, int64_t n, int64_t last_real, bool fwd, bool bwd) {
+    // frame rows [r0, r0 + n) in launches of at most `per` rows (a multiple
+    // of 128): forward, and/or backward
+    int chunks(int64_t r0, int64_t n, int64_t last_real, bool fwd, bool bwd, int64_t per) {
         const AttnShape sh = shape();
         const MetaPtrs mp = meta_ptrs(f.meta, rows);
-        for (int64_t c = r0; c < r0 + n; c += chunk) {
-            const int64_t c1 = std::min(r0 + n, c + chunk);
+        for (int64_t c = r0; c < r0 + n; c += per) {
+            const int64_t c1 = std::min(r0 + n, c + per);
             RowSel sel;
             sel.q_list = f.iota + c / kBlock;
             sel.n_q = int((c1 + kBlock - 1) / kBlock - c / kBlock);
@@ -297,11 +310,11 @@ struct Exec {
         return st(launch_dfs_emit(f.accv, dv, r0, p0, n, w, s));
     }
 
-    int group(Walk& w, int64_t p0, int64_t G) {
+    int group(Walk& w, int64_t p0, int64_t G, int64_t per) {
         const int64_t r0 = w.top, last = r0 + G - 1;
         if (int rc = load(p0, r0, G)) return rc;
         if (int rc = frame(w, last, r0, G, p0)) return rc;
-        if (int rc = chunks(r0, G, last, true, true)) return rc;  // a leaf's backward starts at once
+        if (int rc = chunks(r0, G, last, true, true, per)) return rc;  // a leaf's backward starts at once
         if (int rc = store_fwd(r0, p0, G)) return rc;
         return store_bwd(r0, p0, G);
     }
@@ -309,14 +322,14 @@ struct Exec {
         const int64_t n = t.size(node), last = r0 + n - 1;
         if (int rc = load(t.start[node], r0, n)) return rc;
         if (int rc = frame(w, last, 0, 0, 0)) return rc;
-        if (int rc = chunks(r0, n, last, true, false)) return rc;
+        if (int rc = chunks(r0, n, last, true, false, chunk)) return rc;
         return store_fwd(r0, t.start[node], n);
     }
     int pop(Walk& w, int node, int64_t r0) {
         // every branch below has added its gradient to this node's keys
         const int64_t n = t.size(node), last = r0 + n - 1;
         if (int rc = frame(w, last, 0, 0, 0)) return rc;
-        if (int rc = chunks(r0, n, last, false, true)) return rc;
+        if (int rc = chunks(r0, n, last, false, true, chunk)) return rc;
         return store_bwd(r0, t.start[node], n);
     }
 };

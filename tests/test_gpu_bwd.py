@@ -140,7 +140,10 @@ def test_bwd_full_size_sampled(config):
                                                 scale, dtype=np.float32)
     assert_attn_close(bf16_ref(dk[cols]), dk_ref, BF16_ATOL, BF16_RTOL, f"config{config} dK cols", E2E_GRAD_VEC_FLOOR)
     assert_attn_close(bf16_ref(dv[cols]), dv_ref, BF16_ATOL, BF16_RTOL, f"config{config} dV cols")
-    # identities over every key, per key/value head
+    # identities over every key, per key/value head: a consistency check of
+    # the whole backward (its bound uses the GPU's own magnitudes; the
+    # elementwise checks above and tests/test_gpu_fullsize.py, which bounds
+    # the same identities by the oracle's magnitudes, are what bind)
     n = po.n_tokens
     grp = w.hq // w.hkv
     dk_sum = bf16_ref(dk[:n]).sum(axis=0)

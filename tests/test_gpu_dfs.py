@@ -154,3 +154,49 @@ def test_dfs_multiturn_3_every_trie_sampled():
         idx = [j for j, _ in cols]
         assert_attn_close(bf16_ref(dk[idx]), dk_ref, BF16_ATOL, BF16_RTOL, f"dfs 3[{t}] dK keys", E2E_GRAD_VEC_FLOOR)
         assert_attn_close(bf16_ref(dv[idx]), dv_ref, BF16_ATOL, BF16_RTOL, f"dfs 3[{t}] dV keys")
+
+
+def test_dfs_hip_graph_capture_and_replay():
+    """The depth-first execution is many small launches (frame metadata,
+    forward / backward over one node's query blocks, row copies) and no
+    allocation, memset, copy or synchronisation, so one trie's whole walk
+    captures into a HIP graph.  Each replay, with new values in the captured
+    inputs and eager work in between, equals the eager run bit for bit."""
+    torch = torch_cuda()
+    ids, mask, M = workloads.small_workload("multiturn-small")
+    (pl,), _ = pta.pack(ids, mask, M)
+    q, k, v, do = workloads.attention_inputs(pl.L, 8, 2, 128, "bf16", 1.0 / math.sqrt(128), 4321)
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    meta = pta.tree_meta(pl.subtree_end)
+    plan = pta.dfs_plan(pl, 256)
+    announce(f"dfs graph L={pl.L}: {plan}")
+    ws = torch.empty(pta.dfs_workspace_bytes(plan, 8, 2, 128), dtype=torch.uint8, device="cuda")
+    outs = dict(o=torch.empty_like(qd), lse=torch.empty((8, pl.L), device="cuda"), dq=torch.empty_like(qd),
+                dk=torch.empty_like(kd), dv=torch.empty_like(vd))
+
+    def walk():
+        return pta.attn_dfs(pl, qd, kd, vd, dod, meta, chunk=256, workspace=ws, **outs)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        walk()  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        walk()
+    gen = torch.Generator().manual_seed(7)
+    for rep in range(3):
+        for dst in (qd, kd, vd, dod):
+            dst.copy_((torch.randn(dst.shape, generator=gen) * 0.1).to(dst.dtype))
+        torch.cuda.synchronize()
+        ref = tuple(x.clone() for x in walk())  # eager, on the same inputs
+        for x in outs.values():
+            x.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, x, y in zip(("O", "LSE", "dQ", "dK", "dV"), (outs[n] for n in ("o", "lse", "dq", "dk", "dv")),
+                              ref):
+            assert torch.equal(x, y), f"replay {rep}: {name}"

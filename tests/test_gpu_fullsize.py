@@ -106,6 +106,15 @@ def _group_check(torch, res, po, off, kv, g, tag, alone=True):
     assert_attn_close(_host(res["dq"], a, b, hs), dq_ref, BF16_ATOL, BF16_RTOL, f"{tag} dQ", E2E_GRAD_VEC_FLOOR)
     assert_attn_close(_host(res["dk"], a, b, [kv]), dk_ref, BF16_ATOL, BF16_RTOL, f"{tag} dK", E2E_GRAD_VEC_FLOOR)
     assert_attn_close(_host(res["dv"], a, b, [kv]), dv_ref, BF16_ATOL, BF16_RTOL, f"{tag} dV")
+    # two exact identities over every key of the group, bounded by the
+    # oracle's magnitudes: sum_j dK_j = 0 (each dS row sums to zero) and
+    # sum_j dV_j = sum_i dO_i over real rows (each P row sums to one)
+    n = po.n_tokens
+    dk_sum = _host(res["dk"], a, b, [kv])[:n].sum(axis=0)
+    dv_sum = _host(res["dv"], a, b, [kv])[:n].sum(axis=0)
+    do_sum = sum(_host(res["do"], a, b, [h])[:n].sum(axis=0) for h in hs)
+    assert np.abs(dk_sum).max() <= 1e-2 * np.abs(dk_ref[:n]).sum(axis=0).max(), f"{tag} sum dK"
+    assert np.abs(dv_sum - do_sum).max() <= 1e-2 * np.abs(dv_ref[:n]).sum(axis=0).max(), f"{tag} sum dV"
     if not alone:
         return
     # the backward alone: heads hs get the oracle's O (bf16) and LSE, the

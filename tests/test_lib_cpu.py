@@ -426,7 +426,7 @@ def test_dfs_plan_stack_matches_oracle(L, chunk):
     (pl,), _ = pta.pack(w.ids, w.mask, w.max_tokens_per_mb)
     plan = pta.dfs_plan(pl, 2048)
     assert plan["peak_stack_tokens"] == 16384 and plan["max_path_tokens"] == 16640 and plan["max_depth"] == 1
-    assert plan["rows"] == 16384 + 2048 and plan["leaf_groups"] == 8 and plan["chunks"] == 8 + 8
+    assert plan["rows"] == 16384 + 8192 and plan["leaf_groups"] == 2 and plan["chunks"] == 8 + 2
 
 
 def test_dfs_entry_points_validate(L):
