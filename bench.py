@@ -20,7 +20,8 @@ convention) and is compared with MI355X's dense bf16 MFMA peak.
     python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--config 4a]
                     [--sweep L,b] [--no-cpu-baseline]
     python bench.py --logprobs [--vocab 151936] [--config 4a]   (the
-                    tree log-probability gather, its own JSON line)
+                    tree log-probability gather, its own JSON line, with
+                    --logprob-chunk 1024 times the chunked form beside it)
     python bench.py --partition K [--config 2]   (the host-side DFS-order
                     split over K workers, its own JSON line)
     python bench.py --rope [--config 4a]   (rotary embedding of Q and K by
@@ -80,6 +81,9 @@ def parse(argv=None):
     ap.add_argument("--dfs", action="store_true",
                     help="time the depth-first (DTA) execution of every trie against the packed path")
     ap.add_argument("--chunk", type=int, default=2048, help="query chunk of the depth-first execution")
+    ap.add_argument("--logprob-chunk", type=int, default=0,
+                    help="with --logprobs, also time the chunked form with this many rows per chunk "
+                         "(the guide's chunk_size is 1024)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB elementwise copy kernel 3x (HBM counter calibration)")
     return ap.parse_args(argv)
@@ -424,6 +428,25 @@ def bench_logprobs(a):
     sec = (time.perf_counter() - t0) / a.steps
     t_stats = sum(e[0].elapsed_time(e[1]) for e in ev) / a.steps
     t_gather = sum(e[1].elapsed_time(e[2]) for e in ev) / a.steps
+    # the chunked form: stats and the gather window per chunk of rows, as
+    # after an LM head run chunk by chunk (here the chunks are row slices of
+    # the resident logits, so only the per-chunk launches are added)
+    ch = int(a.logprob_chunk)
+    chunked = None
+    if ch > 0:
+        pta.tree_logprobs_chunked(lambda r0, r1: x[r0:r1], L, tok_d, rp_d, ch)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(a.steps):
+            pta.tree_logprobs_chunked(lambda r0, r1: x[r0:r1], L, tok_d, rp_d, ch)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_chunked = e0.elapsed_time(e1) / a.steps
+        chunked = {"rows_per_chunk": ch, "chunks": -(-L // ch), "gpu_ms_per_step": round(t_chunked, 4),
+                   "logits_bytes_per_chunk": 2 * ch * V}
+        log(f"stats {t_stats:.3f} ms, gather {t_gather:.3f} ms; chunked ({ch} rows, {-(-L // ch)} chunks) "
+            f"{t_chunked:.3f} ms per step")
     alg = 2.0 * L * V + 8.0 * L
     achieved = alg / (t_stats * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -435,6 +458,7 @@ def bench_logprobs(a):
         "warmup": a.warmup, "ms_per_step": round(sec * 1e3, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "kernel_ms_per_launch": {"logits_stats": round(t_stats, 4), "gather": round(t_gather, 4)},
+        "chunked": chunked,
         "config": {"workload": w.name, "L": L, "vocab": V, "batch": list(w.ids.shape), "predictions": n_pred},
         "roofline": roof,
     }

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define TREE_ATTN_ABI_VERSION 6
+#define TREE_ATTN_ABI_VERSION 7
 
 /* status codes */
 #define TREE_OK 0
@@ -393,6 +393,23 @@ int tree_logits_stats(const void* logits, int64_t L, int64_t V, int32_t dtype, f
 int tree_gather_logprobs(const void* logits, int64_t L, int64_t V, int32_t dtype, const float* d_lse,
                          const float* d_ent, const int32_t* d_ids, const int32_t* d_row_pos, int64_t B,
                          int64_t S, float pad_value, float* d_logp, float* d_out_ent, void* stream);
+
+/* The same gather over a window of rows, for logits produced chunk by chunk
+ * (the guide's chunk_size, 1024 rows by default, bounds peak memory the
+ * same way): logits_rows holds packed rows [row0, row0 + n_rows) of the
+ * [L, V] logits, row-major.  Entries predicted from a row in the window are
+ * written as tree_gather_logprobs writes them; entries predicted from a row
+ * outside it are left unchanged; pad entries (pad_value) and entries with
+ * a position outside [0, L) (NaN) are written by every call.  So calls whose
+ * windows cover [0, L) exactly once, in any order, leave d_logp /
+ * d_out_ent equal to one tree_gather_logprobs over the whole logits.  d_lse
+ * / d_ent are the whole [L] arrays (tree_logits_stats of each chunk written
+ * at d_lse + row0, d_ent + row0).  Errors: those of tree_gather_logprobs,
+ * and TREE_E_ARG for a window outside [0, L). */
+int tree_gather_logprobs_rows(const void* logits_rows, int64_t row0, int64_t n_rows, int64_t L, int64_t V,
+                              int32_t dtype, const float* d_lse, const float* d_ent, const int32_t* d_ids,
+                              const int32_t* d_row_pos, int64_t B, int64_t S, float pad_value, float* d_logp,
+                              float* d_out_ent, void* stream);
 
 /* ------------------------------------------------------------------------
  * Rotary position embedding by tree position ids (device).  Guide, section

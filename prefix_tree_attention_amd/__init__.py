@@ -31,6 +31,7 @@ from .api import (  # noqa: F401
     logits_stats,
     gather_logprobs,
     tree_logprobs,
+    tree_logprobs_chunked,
     rope,
     tree_rope,
     rope_table,

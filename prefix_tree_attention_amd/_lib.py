@@ -96,6 +96,8 @@ SIGNATURES = {
     "tree_logits_stats": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp]),
     "tree_gather_logprobs": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_f32,
                                             c_vp, c_vp, c_vp]),
+    "tree_gather_logprobs_rows": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp,
+                                                 c_i64, c_i64, c_f32, c_vp, c_vp, c_vp]),
     "tree_rope_table_bytes": (c_sz, [c_i64, c_i32]),
     "tree_rope_table": (ctypes.c_int, [ctypes.c_double, c_i64, c_i32, c_vp, c_sz, c_vp]),
     "tree_attn_fwd_rope": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp, c_vp,

@@ -463,6 +463,51 @@ def tree_logprobs(logits, token_ids, row_positions, pad_value: float = 0.0):
     return gather_logprobs(logits, lse, ent, token_ids, row_positions, pad_value)
 
 
+def tree_logprobs_chunked(logits_of, L: int, token_ids, row_positions, chunk: int = 1024,
+                          pad_value: float = 0.0):
+    """``tree_logprobs`` with the logits produced ``chunk`` packed rows at a
+    time, so that at most [chunk, V] of them exist at once (the guide's
+    chunk_size).  ``logits_of(r0, r1)`` returns the contiguous device
+    logits of rows [r0, r1), e.g. ``lambda a, b: hidden[a:b] @ w_head.t()``;
+    each chunk runs ``tree_logits_stats`` into its slice of the row
+    statistics and ``tree_gather_logprobs_rows`` over its window.  Same
+    results as ``tree_logprobs`` on the whole logits, bit for bit."""
+    torch = _torch()
+    if chunk <= 0:
+        raise TreeAttnError(-5, "chunk must be positive")
+    for name, t in (("token_ids", token_ids), ("row_positions", row_positions)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.int32:
+            raise TreeAttnError(-5, f"{name} must be a contiguous int32 device tensor")
+    if token_ids.numel() != L or row_positions.dim() != 2:
+        raise TreeAttnError(-5, "token_ids must have L entries, row_positions [B, S]")
+    dev = token_ids.device
+    B, S = row_positions.shape
+    lse = torch.empty(L, dtype=torch.float32, device=dev)
+    ent = torch.empty(L, dtype=torch.float32, device=dev)
+    logp = torch.empty((B, S), dtype=torch.float32, device=dev)
+    oent = torch.empty((B, S), dtype=torch.float32, device=dev)
+    stream = _stream(dev)
+    V = dt = None
+    for r0 in range(0, max(L, 1), chunk):
+        r1 = min(L, r0 + chunk)
+        lg = logits_of(r0, r1) if r1 > r0 else None
+        if lg is not None:
+            _check_logits(lg)
+            if lg.shape[0] != r1 - r0 or lg.device != dev or (V is not None and (lg.shape[1] != V
+                                                                                   or lg.dtype != dt)):
+                raise TreeAttnError(-5, f"logits_of({r0}, {r1}) must give [{r1 - r0}, V] on the same device, "
+                                        "with one V and dtype for every chunk")
+            V, dt = lg.shape[1], lg.dtype
+            check(lib().tree_logits_stats(_ptr(lg), r1 - r0, V, _dtype_code(lg),
+                                          ctypes.c_void_p(lse.data_ptr() + 4 * r0),
+                                          ctypes.c_void_p(ent.data_ptr() + 4 * r0), stream))
+        check(lib().tree_gather_logprobs_rows(_ptr(lg) if lg is not None else None, r0, r1 - r0, L, V or 1,
+                                              _dtype_code(lg) if lg is not None else 0, _ptr(lse), _ptr(ent),
+                                              _ptr(token_ids), _ptr(row_positions), B, S, float(pad_value),
+                                              _ptr(logp), _ptr(oent), stream))
+    return logp, oent
+
+
 # ---------------------------------------------------------------------------
 # rotary embedding by tree position ids
 # ---------------------------------------------------------------------------

@@ -54,6 +54,31 @@ int hip_status(hipError_t e, const char* fn) {
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
+// the gather of tree_gather_logprobs and tree_gather_logprobs_rows
+int gather_logprobs(const char* name, const void* logits, int64_t row0, int64_t n_rows, int64_t L, int64_t V,
+                    int32_t dtype, const float* d_lse, const float* d_ent, const int32_t* d_ids,
+                    const int32_t* d_row_pos, int64_t B, int64_t S, float pad_value, float* d_logp, float* d_out_ent,
+                    void* stream) {
+    if (L < 0 || L > (int64_t(1) << 31) - 1 || V <= 0 || V > (int64_t(1) << 31) - 1 || B < 0 || S < 0 ||
+        (S > 0 && B > ((int64_t(1) << 40) / S)))
+        return set_error(TREE_E_ARG, "%s: bad shape L=%lld V=%lld B=%lld S=%lld", name, (long long)L, (long long)V,
+                         (long long)B, (long long)S);
+    if (row0 < 0 || n_rows < 0 || row0 > L - n_rows)
+        return set_error(TREE_E_ARG, "%s: rows [%lld, %lld) outside [0, %lld)", name, (long long)row0,
+                         (long long)(row0 + n_rows), (long long)L);
+    if (dtype != TREE_DTYPE_BF16 && dtype != TREE_DTYPE_FP32)
+        return set_error(TREE_E_ARG, "%s: unknown dtype %d", name, dtype);
+    if (B * S == 0) {
+        clear_error();
+        return TREE_OK;
+    }
+    if (!d_row_pos || !d_logp || !d_out_ent || (L > 0 && (!d_lse || !d_ent || !d_ids)) || (n_rows > 0 && !logits))
+        return set_error(TREE_E_ARG, "%s: NULL device pointer", name);
+    return hip_status(launch_gather_logprobs(logits, row0, n_rows, L, V, dtype, d_lse, d_ent, d_ids, d_row_pos, B, S,
+                                             pad_value, d_logp, d_out_ent, static_cast<hipStream_t>(stream)),
+                      name);
+}
+
 }  // namespace
 }  // namespace treeattn
 
@@ -234,21 +259,16 @@ int tree_logits_stats(const void* logits, int64_t L, int64_t V, int32_t dtype, f
 int tree_gather_logprobs(const void* logits, int64_t L, int64_t V, int32_t dtype, const float* d_lse,
                          const float* d_ent, const int32_t* d_ids, const int32_t* d_row_pos, int64_t B, int64_t S,
                          float pad_value, float* d_logp, float* d_out_ent, void* stream) {
-    if (L < 0 || L > (int64_t(1) << 31) - 1 || V <= 0 || V > (int64_t(1) << 31) - 1 || B < 0 || S < 0 ||
-        (S > 0 && B > ((int64_t(1) << 40) / S)))
-        return set_error(TREE_E_ARG, "tree_gather_logprobs: bad shape L=%lld V=%lld B=%lld S=%lld", (long long)L,
-                         (long long)V, (long long)B, (long long)S);
-    if (dtype != TREE_DTYPE_BF16 && dtype != TREE_DTYPE_FP32)
-        return set_error(TREE_E_ARG, "tree_gather_logprobs: unknown dtype %d", dtype);
-    if (B * S == 0) {
-        clear_error();
-        return TREE_OK;
-    }
-    if (!d_row_pos || !d_logp || !d_out_ent || (L > 0 && (!logits || !d_lse || !d_ent || !d_ids)))
-        return set_error(TREE_E_ARG, "tree_gather_logprobs: NULL device pointer");
-    return hip_status(launch_gather_logprobs(logits, L, V, dtype, d_lse, d_ent, d_ids, d_row_pos, B, S, pad_value,
-                                             d_logp, d_out_ent, static_cast<hipStream_t>(stream)),
-                      "tree_gather_logprobs");
+    return gather_logprobs("tree_gather_logprobs", logits, 0, L, L, V, dtype, d_lse, d_ent, d_ids, d_row_pos, B, S,
+                           pad_value, d_logp, d_out_ent, stream);
+}
+
+int tree_gather_logprobs_rows(const void* logits_rows, int64_t row0, int64_t n_rows, int64_t L, int64_t V,
+                              int32_t dtype, const float* d_lse, const float* d_ent, const int32_t* d_ids,
+                              const int32_t* d_row_pos, int64_t B, int64_t S, float pad_value, float* d_logp,
+                              float* d_out_ent, void* stream) {
+    return gather_logprobs("tree_gather_logprobs_rows", logits_rows, row0, n_rows, L, V, dtype, d_lse, d_ent, d_ids,
+                           d_row_pos, B, S, pad_value, d_logp, d_out_ent, stream);
 }
 
 int tree_rope(const void* x, void* y, const int32_t* d_pos, int64_t L, int32_t H, int32_t D, double base,

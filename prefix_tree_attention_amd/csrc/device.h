@@ -161,9 +161,10 @@ hipError_t launch_dfs_emit(const float* acc, void* out, int64_t s0, int64_t d0, 
 
 hipError_t launch_logits_stats(const void* logits, int64_t L, int64_t V, int dtype, float* lse, float* ent,
                                hipStream_t stream);
-hipError_t launch_gather_logprobs(const void* logits, int64_t L, int64_t V, int dtype, const float* lse,
-                                  const float* ent, const int32_t* ids, const int32_t* row_pos, int64_t B, int64_t S,
-                                  float pad_value, float* out_logp, float* out_ent, hipStream_t stream);
+hipError_t launch_gather_logprobs(const void* logits, int64_t row0, int64_t n_rows, int64_t L, int64_t V, int dtype,
+                                  const float* lse, const float* ent, const int32_t* ids, const int32_t* row_pos,
+                                  int64_t B, int64_t S, float pad_value, float* out_logp, float* out_ent,
+                                  hipStream_t stream);
 
 hipError_t launch_rope_table(float* tab, int64_t P, int D, double base, hipStream_t stream);
 hipError_t launch_rope_tab(const void* x, void* y, const int32_t* pos, const float* tab, int64_t L, int H, int D,

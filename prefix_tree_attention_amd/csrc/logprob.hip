@@ -145,10 +145,14 @@ __global__ __launch_bounds__(kStatThreads) void logits_stats_kernel(const T* __r
     }
 }
 
+// `logits` holds the packed rows [row0, row0 + n_rows) of the [L, V] logits;
+// entries predicted from a row outside that window are left as they are, so
+// windows that cover [0, L) once write every entry once (pads and bad
+// positions are written by every call).
 template <typename T>
-__global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ logits, int64_t L, int64_t V,
-                                                     const float* __restrict__ lse, const float* __restrict__ ent,
-                                                     const int32_t* __restrict__ ids,
+__global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ logits, int64_t row0, int64_t n_rows,
+                                                     int64_t L, int64_t V, const float* __restrict__ lse,
+                                                     const float* __restrict__ ent, const int32_t* __restrict__ ids,
                                                      const int32_t* __restrict__ row_pos, int64_t B, int64_t S,
                                                      float pad_value, float* __restrict__ out_logp,
                                                      float* __restrict__ out_ent) {
@@ -163,8 +167,9 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ logit
     float lp = pad_value, en = pad_value;
     if (pos >= 0 && nxt >= 0) {
         if (pos < L && nxt < L) {
+            if (pos < row0 || pos >= row0 + n_rows) return;
             const int32_t label = ids[nxt];
-            lp = (label >= 0 && label < V) ? to_f32(logits[int64_t(pos) * V + label]) - lse[pos] : NAN;
+            lp = (label >= 0 && label < V) ? to_f32(logits[(pos - row0) * V + label]) - lse[pos] : NAN;
             en = ent[pos];
         } else {
             lp = en = NAN;
@@ -187,17 +192,18 @@ hipError_t launch_logits_stats(const void* logits, int64_t L, int64_t V, int dty
     return hipGetLastError();
 }
 
-hipError_t launch_gather_logprobs(const void* logits, int64_t L, int64_t V, int dtype, const float* lse,
-                                  const float* ent, const int32_t* ids, const int32_t* row_pos, int64_t B, int64_t S,
-                                  float pad_value, float* out_logp, float* out_ent, hipStream_t stream) {
+hipError_t launch_gather_logprobs(const void* logits, int64_t row0, int64_t n_rows, int64_t L, int64_t V, int dtype,
+                                  const float* lse, const float* ent, const int32_t* ids, const int32_t* row_pos,
+                                  int64_t B, int64_t S, float pad_value, float* out_logp, float* out_ent,
+                                  hipStream_t stream) {
     const int64_t n = B * S;
     const unsigned grid = unsigned((n + 255) / 256);
     if (dtype == 0)
-        gather_kernel<bf16><<<grid, 256, 0, stream>>>(static_cast<const bf16*>(logits), L, V, lse, ent, ids, row_pos,
-                                                      B, S, pad_value, out_logp, out_ent);
+        gather_kernel<bf16><<<grid, 256, 0, stream>>>(static_cast<const bf16*>(logits), row0, n_rows, L, V, lse, ent,
+                                                      ids, row_pos, B, S, pad_value, out_logp, out_ent);
     else
-        gather_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(logits), L, V, lse, ent, ids,
-                                                       row_pos, B, S, pad_value, out_logp, out_ent);
+        gather_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(logits), row0, n_rows, L, V, lse,
+                                                       ent, ids, row_pos, B, S, pad_value, out_logp, out_ent);
     return hipGetLastError();
 }
 

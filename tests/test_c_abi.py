@@ -71,7 +71,7 @@ def test_c_program_packs_the_worked_example(exe):
     assert r.returncode == 0, r.stdout + r.stderr
     lines = r.stdout.splitlines()
     g = json.load(open(GOLDEN))
-    assert lines[0] == f"abi 6 tries 1 n {g['n_tokens']} L {g['L']} nodes {len(g['node_start'])} seqs 3"
+    assert lines[0] == f"abi 7 tries 1 n {g['n_tokens']} L {g['L']} nodes {len(g['node_start'])} seqs 3"
     assert lines[1] == "ids " + " ".join(map(str, g["token_ids_real"]))
     assert lines[2] == "se " + " ".join(map(str, g["subtree_end_real"]))
     assert lines[3] == "pairs 22 unpacked 26 tree 8 original 11"

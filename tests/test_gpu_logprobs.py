@@ -9,7 +9,11 @@ against the oracle's node-walk gather, on the same logits:
   transition, plus the sharing invariant: every leaf's predictions inside
   the shared prefix are the same packed rows, hence identical;
 * -inf logits (probability 0, excluded from the entropy) and token ids
-  outside the vocabulary (NaN from the kernel's own range check).
+  outside the vocabulary (NaN from the kernel's own range check);
+* the chunked form (tree_logits_stats per chunk of rows, then
+  tree_gather_logprobs_rows over its window): bit-identical to the one-pass
+  form at every chunk size, in any window order, and at full size with
+  the guide's default chunk of 1024 rows.
 
 Tolerance: the GPU accumulates each row's V terms in float32, about V/256
 terms per lane then a 256-way tree, so the relative error of the sums is at
@@ -94,6 +98,60 @@ def test_token_ids_outside_vocabulary_give_nan():
     assert np.isfinite(lp[:, :-1][real & ~bad]).all()
 
 
+@pytest.mark.parametrize("kind,V,dt", [("grpo-small", 1003, "bf16"), ("nested", 517, "fp32")])
+def test_chunked_equals_one_pass(kind, V, dt):
+    torch = torch_cuda()
+    ids, mask, M = workloads.small_workload(kind)
+    ids = (np.asarray(ids) % (V - 1)).astype(np.int32)
+    se, tok, rp, _, _ = pta.pack_batch(ids, mask, M)
+    L = len(se)
+    announce(f"logprobs chunked {kind} L={L} V={V} {dt}")
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    g = torch.Generator().manual_seed(V + 1)
+    x = (torch.randn(L, V, generator=g) * 2.0).to(dtype).cuda()
+    tk, rpd = torch.from_numpy(tok).cuda(), torch.from_numpy(rp).cuda()
+    lp1, en1 = pta.tree_logprobs(x, tk, rpd, -3.0)
+    calls = []
+
+    def logits_of(a, b):
+        calls.append((a, b))
+        return x[a:b].contiguous()
+
+    for chunk in (1, 7, 128, 1000, L, L + 5):
+        calls.clear()
+        lp2, en2 = pta.tree_logprobs_chunked(logits_of, L, tk, rpd, chunk, -3.0)
+        torch.cuda.synchronize()
+        assert calls == [(a, min(L, a + chunk)) for a in range(0, L, chunk)]
+        assert torch.equal(lp1, lp2) and torch.equal(en1, en2), f"chunk {chunk}"
+    # windows in reverse order through the C entry point, onto NaN-filled outputs
+    lse, ent = pta.logits_stats(x)
+    B, S = rp.shape
+    lp3 = torch.full((B, S), float("nan"), device="cuda")
+    en3 = torch.full((B, S), float("nan"), device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    lib = pta.lib()
+    chunk = 300
+    for a in reversed(range(0, L, chunk)):
+        b = min(L, a + chunk)
+        xa = x[a:b].contiguous()
+        rc = lib.tree_gather_logprobs_rows(xa.data_ptr(), a, b - a, L, V, 0 if dt == "bf16" else 1,
+                                           lse.data_ptr(), ent.data_ptr(), tk.data_ptr(), rpd.data_ptr(), B, S,
+                                           -3.0, lp3.data_ptr(), en3.data_ptr(), stream)
+        assert rc == 0, lib.tree_last_error()
+    torch.cuda.synchronize()
+    assert torch.equal(lp1, lp3) and torch.equal(en1, en3)
+    # an empty window writes exactly the pad entries
+    lp4 = torch.full((B, S), float("nan"), device="cuda")
+    en4 = torch.full((B, S), float("nan"), device="cuda")
+    rc = lib.tree_gather_logprobs_rows(None, 0, 0, L, V, 0 if dt == "bf16" else 1, lse.data_ptr(), ent.data_ptr(),
+                                       tk.data_ptr(), rpd.data_ptr(), B, S, -3.0, lp4.data_ptr(), en4.data_ptr(),
+                                       stream)
+    assert rc == 0, lib.tree_last_error()
+    torch.cuda.synchronize()
+    pads = (lp1 == -3.0)
+    assert torch.equal(lp4[pads], lp1[pads]) and torch.isnan(lp4[~pads]).all()
+
+
 def test_deep_shared_full_vocabulary_sampled():
     torch = torch_cuda()
     w = workloads.make_workload("4a")
@@ -129,5 +187,9 @@ def test_deep_shared_full_vocabulary_sampled():
         ref_en.append(b)
     assert_close(np.array(got_lp), np.array(ref_lp), LP_ATOL, LP_RTOL, "4a sampled logp")
     assert_close(np.array(got_en), np.array(ref_en), LP_ATOL, LP_RTOL, "4a sampled entropy")
+    # the chunked form with the guide's default chunk: bit-identical everywhere
+    lp2, en2 = pta.tree_logprobs_chunked(lambda a, b: x[a:b], L, torch.from_numpy(tok).cuda(),
+                                         torch.from_numpy(rp).cuda(), 1024, -9.0)
+    assert torch.equal(logp, lp2) and torch.equal(ent, en2)
     del x
     torch.cuda.empty_cache()

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
     for n in sorted(names):
         assert hasattr(L, n), n
     assert set(_lib.SIGNATURES) == names
-    assert L.tree_abi_version() == 6
+    assert L.tree_abi_version() == 7
 
 
 def _compare(tries_lib, tries_or):
@@ -338,6 +338,14 @@ def test_logprob_entry_points_validate_before_launch(L):
     assert L.tree_gather_logprobs(p, 100, 50, 0, p, p, p, p, -1, 4, 0.0, p, p, None) == -5
     assert L.tree_gather_logprobs(p, 100, 50, 0, p, p, p, None, 2, 4, 0.0, p, p, None) == -5
     assert L.tree_gather_logprobs(None, 0, 50, 0, None, None, None, None, 0, 4, 0.0, None, None, None) == 0
+    g = L.tree_gather_logprobs_rows
+    assert g(p, 90, 20, 100, 50, 0, p, p, p, p, 2, 4, 0.0, p, p, None) == -5     # window past L
+    assert b"rows [90, 110) outside [0, 100)" in L.tree_last_error()
+    assert g(p, -1, 20, 100, 50, 0, p, p, p, p, 2, 4, 0.0, p, p, None) == -5     # negative start
+    assert g(p, 0, -1, 100, 50, 0, p, p, p, p, 2, 4, 0.0, p, p, None) == -5      # negative rows
+    assert g(None, 0, 20, 100, 50, 0, p, p, p, p, 2, 4, 0.0, p, p, None) == -5   # rows but no logits
+    assert g(p, 0, 20, 100, 50, 3, p, p, p, p, 2, 4, 0.0, p, p, None) == -5      # dtype
+    assert g(None, 0, 0, 100, 50, 0, p, p, p, p, 0, 4, 0.0, p, p, None) == 0     # empty batch
     h = ctypes.c_void_p()
     ids, mask = workloads.worked_example()
     ids = np.ascontiguousarray(ids, np.int32)
