@@ -56,17 +56,22 @@ int build_tree(const int32_t* s, const int32_t* e, const int32_t* par, int64_t n
     t.n_tokens = n_tokens;
     t.kids.assign(size_t(n_nodes), {});
     t.roots.clear();
-    // pre-order node table: contiguous token ranges, parents before children,
-    // a child's range inside its parent's subtree (checked as the nesting of
-    // consecutive ranges)
+    // pre-order node table: contiguous token ranges in node order, and each
+    // node's parent on the root path of the node before it (the path is kept
+    // as a stack while scanning), so that the parent links describe the tree
+    // the layout was written from
+    std::vector<int64_t> path;
     for (int64_t v = 0; v < n_nodes; ++v) {
         const int64_t lo = s[v], hi = e[v];
         if (lo != (v == 0 ? 0 : int64_t(e[v - 1]) + 1) || hi < lo || hi >= n_tokens)
             return set_error(TREE_E_ARG, "tree_attn_dfs: node %lld range [%lld, %lld] is not the pre-order layout",
                              (long long)v, (long long)lo, (long long)hi);
         const int64_t p = par[v];
-        if (p >= v || p < -1)
-            return set_error(TREE_E_ARG, "tree_attn_dfs: node %lld has parent %lld", (long long)v, (long long)p);
+        while (!path.empty() && path.back() != p) path.pop_back();
+        if (p >= v || p < -1 || (p >= 0 && path.empty()))
+            return set_error(TREE_E_ARG, "tree_attn_dfs: node %lld has parent %lld, not on the pre-order path",
+                             (long long)v, (long long)p);
+        path.push_back(v);
         (p < 0 ? t.roots : t.kids[size_t(p)]).push_back(int(v));
     }
     if (int64_t(e[n_nodes - 1]) + 1 != n_tokens)

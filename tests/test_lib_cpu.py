@@ -448,6 +448,14 @@ def test_dfs_entry_points_validate(L):
     bad = pta.PackedTrie(**{**pl.__dict__, "node_parent": np.full_like(pl.node_parent, 7)})
     with pytest.raises(pta.TreeAttnError, match="parent"):
         pta.dfs_plan(bad, 2048)
+    # worked example nodes {A} {B} {C,D} {E,F} {G,H}: parents -1 0 1 1 0.  {G,H}
+    # under {C,D}, or {E,F} under {B} after {C,D} moved to the root's children,
+    # names a parent that the pre-order walk has already left
+    assert list(pl.node_parent) == [-1, 0, 1, 1, 0]
+    for par in ([-1, 0, 1, 1, 2], [-1, 0, 0, 1, 0]):
+        bad = pta.PackedTrie(**{**pl.__dict__, "node_parent": np.array(par, np.int32)})
+        with pytest.raises(pta.TreeAttnError, match="pre-order path"):
+            pta.dfs_plan(bad, 2048)
     p = ctypes.c_void_p(256)
     ns, ne, npar = (np.ascontiguousarray(x, np.int32) for x in (pl.node_start, pl.node_end, pl.node_parent))
     args = [ns.ctypes.data, ne.ctypes.data, npar.ctypes.data, ns.size, pl.n_tokens]
