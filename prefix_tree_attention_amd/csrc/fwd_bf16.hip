@@ -193,7 +193,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     // (resc false: no move, alpha unused).  maximum (not maxnum) lowers to
     // v_maximum3_f32 with no NaN-quieting of the accumulator inputs.
     auto rebase = [&](float mx, bool ok, bool& resc) {
-        mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32));
+        const LanePair mp = lane_pair32(mx);
+        mx = __builtin_elementwise_maximum(mp.lo, mp.hi);
         const float mt = mx * scale_log2;
         resc = __any(ok & (mt > m_run + kRescaleSlack));
         const float mnew = resc ? fmaxf(m_run, mt) : m_run;
@@ -372,7 +373,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 #undef TREEATTN_SCHED
 
     // epilogue: normalise, write O (bf16) and LSE (natural log)
-    float l = l_run + __shfl_xor(l_run, 32);
+    const LanePair lp = lane_pair32(l_run);
+    float l = lp.lo + lp.hi;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     bf16* orow = O + int64_t(qi) * q_stride + int64_t(h_q) * D + 4 * h;
 #pragma unroll

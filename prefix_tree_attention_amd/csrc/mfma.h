@@ -57,6 +57,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
+// The value of lane l ^ 32 beside this lane's, by one v_permlane32_swap
+// (lanes 32-63 of the first copy trade places with lanes 0-31 of the
+// second): {x of lanes 0-31 in both halves, x of lanes 32-63 in both
+// halves}, so an elementwise max or sum of the two is the lane-pair result
+// with no LDS permute.
+struct LanePair {
+    float lo, hi;
+};
+__device__ __forceinline__ LanePair lane_pair32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
 // Eight floats -> one bf16x8 operand.
 __device__ __forceinline__ bf16x8 to_bf16x8(const f32x4& lo, const f32x4& hi) {
     const f32x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
