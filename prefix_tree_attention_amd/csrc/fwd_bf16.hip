@@ -135,9 +135,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const char* const Kh = reinterpret_cast<const char*>(K + int64_t(hkv) * D);
     const char* const Vh = reinterpret_cast<const char*>(V + int64_t(hkv) * D);
     const uint32_t kv_row_bytes = uint32_t(kv_stride) * 2u;
-    auto kbase_of = [&](int st) { return (row_ent[beg + (st >> 1)] >> 1) * kBlock + kStep * (st & 1); };
-    auto issue_k = [&](int st) {
-        const int kbase = kbase_of(st);
+    // key base of step st, whose tile entry is ent (two 64-key steps per entry)
+    auto kbase_at = [](int ent, int st) { return (ent >> 1) * kBlock + kStep * (st & 1); };
+    auto issue_k = [&](int st, int kbase) {
         const uint64_t off = uint64_t(uint32_t(kbase)) * kv_row_bytes;
         T::load_async(ktile(st), reinterpret_cast<const bf16*>(Kh + off), kvs, wave, lane);
         // the keys' subtree ends ride with the K tile (wave w stages 16 of
@@ -146,8 +146,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         // wait would also drain the prefetch
         if (lane < 16) dma4(se + kbase + 16 * wave, 4u * lane, lds_addr(serow(st) + 64 * wave));
     };
-    auto issue_v = [&](int st) {
-        const uint64_t off = uint64_t(uint32_t(kbase_of(st))) * kv_row_bytes;
+    auto issue_v = [&](int st, int kbase) {
+        const uint64_t off = uint64_t(uint32_t(kbase)) * kv_row_bytes;
         T::load_async(vtile(st), reinterpret_cast<const bf16*>(Vh + off), kvs, wave, lane);
     };
     // S^T = K Q^T (unscaled) of step st for its two 32-key blocks kk:
@@ -166,8 +166,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     };
     // partial tiles: key <= qi and qi <= se[key], i.e.
     // 8 (r / 4) + r % 4 <= qi - (kbase + 32 kk + 4 h) and qi <= se[key]
-    auto mask = [&](int st, f32x16 (&s)[2]) {
-        const int kbase = kbase_of(st);
+    auto mask = [&](int st, int kbase, f32x16 (&s)[2]) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const int k0 = kbase + 32 * kk + 4 * h, lim = qi - k0;
@@ -207,10 +206,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     };
 
     f32x16 sa[2], sb[2];
+    // The row's entries ride in scalar registers: a pair of steps (one
+    // entry) holds its own entry and the next, and requests the one after,
+    // so the steps never wait on a load of the list (one load per pair,
+    // a pair ahead, instead of three per step at the point of use).
+    const int nent = nsteps >> 1;
+    int ent_c = nent > 0 ? row_ent[beg] : 0, ent_n = nent > 1 ? row_ent[beg + 1] : ent_c;
     if (nsteps > 0) {
-        issue_k(0);
-        issue_v(0);
-        if (nsteps > 1) issue_k(1);
+        issue_k(0, kbase_at(ent_c, 0));
+        issue_v(0, kbase_at(ent_c, 0));
+        if (nsteps > 1) issue_k(1, kbase_at(ent_c, 1));
     }
 #pragma unroll
     for (int x = 0; x < NX; ++x) consume(qf[x]);
@@ -220,7 +225,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         // step 0's scores, mask, reference and exp2 arguments; the steps
         // below prepare each following step the same way beside their P V
         scores(0, sa);
-        if (row_ent[beg] & 1) mask(0, sa);
+        if (ent_c & 1) mask(0, kbase_at(ent_c, 0), sa);
         float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
@@ -255,12 +260,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     // past the barriers to their uses.
     auto step = [&](int st, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
         const bool has_next = st + 1 < nsteps;
-        // the next step's tile entry (its own for an even st), clamped to the
-        // row so that the read stays inside it after the last step
-        const int nent = row_ent[beg + min((st + 1) >> 1, (nsteps >> 1) - 1)];
-        const bool next_partial = has_next && (nent & 1);
-        if (st + 2 < nsteps) issue_k(st + 2);
-        if (has_next) issue_v(st + 1);
+        // the next step's entry: this pair's for an even st, the next pair's
+        // for an odd one (equal to it, or unused, past the last step)
+        const int ent1 = (st & 1) ? ent_n : ent_c;
+        const bool next_partial = has_next && (ent1 & 1);
+        if (st + 2 < nsteps) issue_k(st + 2, kbase_at(ent_n, st + 2));
+        if (has_next) issue_v(st + 1, kbase_at(ent1, st + 1));
         const lds_char* vt = vtile(st);
         const lds_char* ktn = ktile(st + 1);
         auto rd_k = [&](int x, int kk) { return T::frag_at(ktn + 32 * kk * T::kRowBytes, roff[x]); };
@@ -351,7 +356,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
                 }
             }
             TREEATTN_SCHED();
-            if (u == UA - 1 && next_partial) mask(st + 1, sn);
+            if (u == UA - 1 && next_partial) mask(st + 1, kbase_at(ent1, st + 1), sn);
         }
         l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
         if (resc) {
@@ -366,8 +371,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     // a query block's step count is even (two per 128-key tile), so the
     // score buffers alternate without copies
     for (int st = 0; st < nsteps; st += 2) {
+        const int ent_nn = row_ent[beg + min((st >> 1) + 2, nent - 1)];
         step(st, sa, sb);
         step(st + 1, sb, sa);
+        ent_c = ent_n;
+        ent_n = ent_nn;
     }
 
 #undef TREEATTN_SCHED
