@@ -26,8 +26,7 @@ constexpr int64_t kMaxL = 1 << 20;   // largest packed length accepted
 //   col_cnt  [nb]     nonempty tiles per key block
 //   col_ptr  [nb+1]
 //   col_ent  [T]      (query block << 1) | partial, ascending query block
-//   q_order  [nb]     query blocks in descending position (the forward's and
-//                     dQ's work order)
+//   q_order  [nb]     query blocks, most nonempty tiles first (ties: index)
 //   k_order  [nb]     key blocks, most nonempty tiles first (ties: index)
 //   blk_cnt  [nb]     real tokens per block, then their exclusive prefix
 //   blk_hsum [nb]     histogram mass per block, then its exclusive prefix

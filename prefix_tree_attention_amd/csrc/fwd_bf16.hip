@@ -58,8 +58,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     // 32x32x16 fragments: lane = MFMA column j32 (this lane's query) and k-half h
     const int j32 = lane & 31, h = lane >> 5;
     const int tr_e = 16 * ((lane >> 4) & 1), tr_i = lane & 15;
-    // work item: key/value-head major, then query blocks in the metadata's
-    // order (descending position), then the query heads of the group
+    // work item: key/value-head major, then query blocks heaviest first,
+    // then the query heads of the group
     const int G = Hq / Hkv, per_kv = (int(gridDim.x) / Hq) * G;
     const int work = xcd_logical_block();
     const int hkv = work / per_kv, rank = (work % per_kv) / G, h_q = hkv * G + work % G;

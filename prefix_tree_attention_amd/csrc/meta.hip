@@ -237,34 +237,38 @@ __global__ __launch_bounds__(1024) void meta_scan(const int32_t* __restrict__ bl
         }
     }
 
-    // The forward and dQ take query blocks in descending position: the
-    // workgroups in flight on an XCD then hold neighbouring blocks, whose
-    // row lists name mostly the same key tiles (read from its L2), and
-    // within a trie the later blocks have the longer lists, so long items
-    // still start first.  (Heaviest-first over the whole launch spread the
-    // blocks in flight over all tries and ran 6-8% slower on GRPO-shaped
-    // batches.)  The key-block order is heaviest first, ties by index: the
-    // keys ((nb - count) << 13) | index are unique, so sorting them ascending
+    // heaviest-first orders, ties by index: the keys
+    // ((nb - count) << 13) | index are unique, so sorting them ascending
     // with a bitonic network in LDS gives exactly that order in
     // O(nb log^2 nb) work (nb <= 8192 = 2^13 blocks).
     constexpr int kMaxNb = int(kMaxL / kBlock);
     constexpr int kMaxChunks = int(kMaxL / kChunk);
     static_assert(kMaxNb <= (1 << 13), "block index must fit 13 bits");
     static_assert(kMaxChunks <= (1 << 14), "chunk index must fit 14 bits");
-    __shared__ unsigned kk[kMaxNb], kg[kMaxChunks];
+    __shared__ unsigned kq[kMaxNb], kk[kMaxNb], kg[kMaxChunks];
     __shared__ unsigned char gflag[kMaxChunks];
     int n = 1;
     while (n < nb) n <<= 1;
     __syncthreads();  // col_cnt written by other threads above
-    for (int i = t; i < n; i += nt) kk[i] = i < nb ? (unsigned(nb - col_cnt[i]) << 13) | unsigned(i) : 0xffffffffu;
+    for (int i = t; i < n; i += nt) {
+        kq[i] = i < nb ? (unsigned(nb - row_cnt[i]) << 13) | unsigned(i) : 0xffffffffu;
+        kk[i] = i < nb ? (unsigned(nb - col_cnt[i]) << 13) | unsigned(i) : 0xffffffffu;
+    }
     __syncthreads();
     for (int k = 2; k <= n; k <<= 1)
         for (int j = k >> 1; j > 0; j >>= 1) {
             for (int i = t; i < n; i += nt) {
                 const int p = i ^ j;
                 if (p > i) {
-                    const unsigned x = kk[i], y = kk[p];
-                    if ((x > y) == ((i & k) == 0)) {
+                    const bool up = (i & k) == 0;
+                    unsigned x = kq[i], y = kq[p];
+                    if ((x > y) == up) {
+                        kq[i] = y;
+                        kq[p] = x;
+                    }
+                    x = kk[i];
+                    y = kk[p];
+                    if ((x > y) == up) {
                         kk[i] = y;
                         kk[p] = x;
                     }
@@ -273,7 +277,7 @@ __global__ __launch_bounds__(1024) void meta_scan(const int32_t* __restrict__ bl
             __syncthreads();
         }
     for (int i = t; i < nb; i += nt) {
-        q_order[i] = nb - 1 - i;
+        q_order[i] = int(kq[i] & 0x1fffu);
         k_order[i] = int(kk[i] & 0x1fffu);
     }
 

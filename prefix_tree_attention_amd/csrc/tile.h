@@ -154,7 +154,7 @@ __device__ __forceinline__ void wait_vm() {
 // logical work index returned here gives XCD x the contiguous range
 // [x W/8, (x+1) W/8) of a key/value-head-major order, so the workgroups
 // sharing K/V tiles (or Q/dO tiles) of one key/value head meet in one L2,
-// while each XCD still takes its range in the metadata's work order.
+// while each XCD still takes its range heaviest-first.
 constexpr int kXcds = 8;
 __device__ __forceinline__ int xcd_logical_block() {
     const int W = int(gridDim.x), b = int(blockIdx.x);

@@ -45,10 +45,11 @@ def _check_trie(torch, p_lib, p_or, tag):
         qbs = np.nonzero(tc_ref[:, kb])[0]
         assert (ent >> 1).tolist() == qbs.tolist()
         assert ((ent & 1) == (tc_ref[qbs, kb] == 1)).all()
+    rc = (tc_ref != 0).sum(1)
     cc = (tc_ref != 0).sum(0)
     qo = ws[lay["q_order"]:lay["q_order"] + nb]
     ko = ws[lay["k_order"]:lay["k_order"] + nb]
-    assert qo.tolist() == list(range(nb - 1, -1, -1))
+    assert qo.tolist() == sorted(range(nb), key=lambda x: (-rc[x], x))
     assert ko.tolist() == sorted(range(nb), key=lambda x: (-cc[x], x))
     # dK/dV key groups: the chunk maxima and the grouping rule, bit for bit,
     # and (from the oracle's mask) every query that sees a group's keys lies
