@@ -18,7 +18,7 @@ import oracle
 import workloads
 import prefix_tree_attention_amd as pta
 from gpu_common import (BF16_ATOL, BF16_RTOL, E2E_GRAD_VEC_FLOOR, announce, assert_attn_close, assert_close, bf16_ref,
-                        small_cases, torch_cuda)
+                        oracle_kv_group, small_cases, torch_cuda)
 
 pytestmark = pytest.mark.gpu
 
@@ -99,20 +99,10 @@ def test_dfs_deep_shared_4a_kv_group():
     scale = 1.0 / math.sqrt(w.d)
     K = bf16_ref(k[:, 0:1])
     V = bf16_ref(v[:, 0:1])
-    o_ref = np.zeros((pl.L, 4, w.d))
-    lse_ref = np.zeros((4, pl.L))
-    dq_ref = np.zeros((pl.L, 4, w.d))
-    dk_ref = np.zeros((pl.L, 1, w.d))
-    dv_ref = np.zeros((pl.L, 1, w.d))
-    for h in range(4):
-        Q = bf16_ref(q[:, h:h + 1])
-        G = bf16_ref(do[:, h:h + 1])
-        o1, l1 = oracle.attention_forward(Q, K, V, m, scale, dtype=np.float32)
-        q1, k1, v1 = oracle.attention_backward(Q, K, V, o1, l1, G, m, scale, dtype=np.float32)
-        o_ref[:, h], lse_ref[h], dq_ref[:, h] = o1[:, 0], l1[0], q1[:, 0]
-        dk_ref += k1
-        dv_ref += v1
-        announce(f"  oracle head {h} done")
+    Qs = [bf16_ref(q[:, h:h + 1]) for h in range(4)]
+    Gs = [bf16_ref(do[:, h:h + 1]) for h in range(4)]
+    # the same inputs as the packed path's full-size 4a check (seed 1_000_000)
+    o_ref, lse_ref, dq_ref, dk_ref, dv_ref = oracle_kv_group(m, Qs, K, V, Gs, scale, "dfs 4a kv0")
     assert_attn_close(bf16_ref(o[:, 0:4]), o_ref, BF16_ATOL, BF16_RTOL, "dfs 4a O")
     assert_close(lse.numpy()[0:4], lse_ref, BF16_ATOL, BF16_RTOL, "dfs 4a LSE")
     assert_attn_close(bf16_ref(dq[:, 0:4]), dq_ref, BF16_ATOL, BF16_RTOL, "dfs 4a dQ", E2E_GRAD_VEC_FLOOR)

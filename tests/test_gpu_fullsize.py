@@ -35,7 +35,7 @@ import oracle
 import workloads
 import prefix_tree_attention_amd as pta
 from gpu_common import (BF16_ATOL, BF16_RTOL, E2E_GRAD_VEC_FLOOR, announce, assert_attn_close, assert_close, bf16_ref,
-                        run_attention, torch_cuda)
+                        oracle_kv_group, run_attention, torch_cuda)
 
 pytestmark = pytest.mark.gpu
 
@@ -86,20 +86,9 @@ def _group_check(torch, res, po, off, kv, g, tag, alone=True):
     m = oracle.dense_ancestor_mask(po)
     K = _host(res["k"], a, b, [kv])
     V = _host(res["v"], a, b, [kv])
-    o_ref = np.zeros((po.L, g, 128))
-    lse_ref = np.zeros((g, po.L))
-    dq_ref = np.zeros((po.L, g, 128))
-    dk_ref = np.zeros((po.L, 1, 128))
-    dv_ref = np.zeros((po.L, 1, 128))
-    for x, h in enumerate(hs):
-        Q = _host(res["q"], a, b, [h])
-        G = _host(res["do"], a, b, [h])
-        o1, l1 = oracle.attention_forward(Q, K, V, m, SCALE, dtype=np.float32)
-        q1, k1, v1 = oracle.attention_backward(Q, K, V, o1, l1, G, m, SCALE, dtype=np.float32)
-        o_ref[:, x], lse_ref[x], dq_ref[:, x] = o1[:, 0], l1[0], q1[:, 0]
-        dk_ref += k1
-        dv_ref += v1
-        announce(f"  {tag}: oracle head {h} done")
+    Qs = [_host(res["q"], a, b, [h]) for h in hs]
+    Gs = [_host(res["do"], a, b, [h]) for h in hs]
+    o_ref, lse_ref, dq_ref, dk_ref, dv_ref = oracle_kv_group(m, Qs, K, V, Gs, SCALE, tag)
     assert_attn_close(_host(res["o"], a, b, hs), o_ref, BF16_ATOL, BF16_RTOL, f"{tag} O")
     n = po.n_tokens
     assert_close(_host(res["lse"].T, a, b, hs).T[:, :n], lse_ref[:, :n], BF16_ATOL, BF16_RTOL, f"{tag} LSE")
