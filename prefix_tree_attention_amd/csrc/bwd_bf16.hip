@@ -12,12 +12,15 @@
 // Three kernels; the whole backward runs dq, then dkdv:
 //   delta: Delta for every (token, query head), for callers that run the
 //          phases one by one (the whole backward computes it inside dq).
-//   dkdv:  one workgroup per (pair of 128-key blocks, key/value head);
-//          wave w owns 64 keys and keeps their V^T operands in vector
-//          registers and their dK^T, dV^T accumulators in the 256
-//          accumulation registers; K rows of the 256 keys sit in LDS.  It
-//          walks the query blocks of the pair's columns (a contiguous
-//          range) for each query head of the group, 64 queries per step;
+//   dkdv:  one workgroup per (key group, key/value head): a group is up
+//          to four consecutive 64-key chunks sharing one subtree-end maximum
+//          (the metadata's runs, cut every four chunks), so a group's keys
+//          see one contiguous range of queries with little of it invisible
+//          to some of them.  Wave w owns chunk w of the group and keeps its
+//          V^T operands in vector registers and its dK^T, dV^T accumulators
+//          in the 256 accumulation registers; K rows of the group's keys sit
+//          in LDS.  It walks the group's 64-query steps for each query head
+//          of the key/value head;
 //          Q and dO (and -LSE / scale, -Delta) of a step go HBM -> LDS by
 //          direct loads into double-buffered swizzled tiles.
 //            S = Q K^T, dP = dO V^T      (A = Q / dO rows of the tiles)
@@ -108,15 +111,15 @@ __device__ __forceinline__ void mfma32_agpr(f32x16& acc, const bf16x8& a, const 
                  : "v"(__builtin_bit_cast(i32x4, a)), "v"(__builtin_bit_cast(i32x4, b)));
 }
 
-// one workgroup per (pair of 128-key blocks, key/value head); wave w owns
-// 64 keys
+// one workgroup per (key group, key/value head); wave w owns the group's
+// 64-key chunk w
 template <int D, bool kAcc, bool kRope>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ NLS, const float* __restrict__ Delta,
     bf16* __restrict__ dK, bf16* __restrict__ dV, float* __restrict__ dKacc, float* __restrict__ dVacc,
-    const int32_t* __restrict__ se, const int32_t* __restrict__ p_order, const int32_t* __restrict__ blk_min,
-    const int32_t* __restrict__ blk_max, int L, int Hq, int Hkv, int qb_lo, int qb_hi, float scale_log2,
+    const int32_t* __restrict__ se, const int32_t* __restrict__ g_order, const int32_t* __restrict__ hi64,
+    const int32_t* __restrict__ hdr, int L, int Hq, int Hkv, int qb_lo, int qb_hi, float scale_log2,
     float scale, const int32_t* __restrict__ pos, const float* __restrict__ rope_tab) {
     using T = Tile<D>;
     constexpr int NX = D / 16;  // k-steps of S = Q K^T and dP = dO V^T
@@ -135,37 +138,49 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
     // transposing reads: 16-lane group gi takes 16 d values starting at
     // 16 (gi % 2) and query rows 4 h + 0..3 of a k-step
     const int tr_e = 16 * ((lane >> 4) & 1), tr_i = lane & 15;
-    // work item: key/value-head major, then key-block pairs heaviest first
-    const int npair = int(gridDim.x) / Hkv;
+    // work item: key/value-head major, then the key groups heaviest first
+    // (the metadata bounds their number by the launch's workgroups per head)
+    const int per_kv = int(gridDim.x) / Hkv;
     const int work = xcd_logical_block();
-    const int hkv = work / npair, rank = work % npair;
-    const int kp = p_order[rank];
+    const int hkv = work / per_kv, rank = work % per_kv;
     const int nb = L / kBlock;
-    const int kb0 = 2 * kp, kb1 = 2 * kp + 1;
-    const bool has1 = kb1 < nb;
     const int G = Hq / Hkv;
     const int64_t q_stride = int64_t(Hq) * D, kv_stride = int64_t(Hkv) * D;
+    if (rank >= hdr[3]) return;  // the launch's slack beyond the groups
+    // A group is nch (1..4) consecutive 64-key chunks from chunk c0; with
+    // hi the largest subtree end among them (one value for all of a run's
+    // chunks), its keys see the 64-query steps c0 .. hi / 64 (clipped to
+    // the launch's query blocks [qb_lo, qb_hi)).
+    const int gent = g_order[rank];
+    const int c0 = gent & 0x3fff, nch = (gent >> 14) + 1;
+    int ghi = hi64[c0];
+    for (int c = 1; c < nch; ++c) ghi = max(ghi, hi64[c0 + c]);
+    const int s_hi = ghi >= 0 ? min(2 * min(nb, qb_hi) - 1, ghi / kChunk) : -1;
+    const int s_lo = max(c0, 2 * qb_lo);
+    const int nsteps = (s_hi >= s_lo ? s_hi - s_lo + 1 : 0) * G;
+    if (kAcc && nsteps == 0) return;  // nothing to add
+    // wave w owns chunk c0 + w; a wave past the group's chunks shadows its
+    // first chunk (in-range reads) and stores nothing
+    const bool active = wave < nch;
+    const int cw = c0 + (active ? wave : 0);
 
     // V^T operands (B of dP) in registers: lane holds key
-    // 256 kp + 64 wave + 32 kk + j32, d = 16 x + 8 h .. +7 for k-step x.
+    // 64 cw + 32 kk + j32, d = 16 x + 8 h .. +7 for k-step x.
     // K^T operands (B of S) are read from the K rows in LDS with the same
-    // offsets as the Q rows.  Keys past L (the second block of the last
-    // pair at an odd block count) read in-range rows instead; their
-    // gradients are never stored.
+    // offsets as the Q rows.
     bf16x8 vf[2][NX];
     int key[2], sek[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-        key[kk] = kb0 * kBlock + 64 * wave + 32 * kk + j32;
-        const bool ok = key[kk] < L;
-        sek[kk] = ok ? se[key[kk]] : -1;
-        const int64_t base = int64_t(ok ? key[kk] : L - 1) * kv_stride + hkv * D + 8 * h;
+        key[kk] = kChunk * cw + 32 * kk + j32;
+        sek[kk] = se[key[kk]];
+        const int64_t base = int64_t(key[kk]) * kv_stride + hkv * D + 8 * h;
 #pragma unroll
         for (int x = 0; x < NX; ++x) vf[kk][x] = __builtin_bit_cast(bf16x8, ld16(V + base + 16 * x));
     }
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-        const int r0 = kb0 * kBlock + (has1 ? 64 * q4 : 64 * (q4 & 1));
+        const int r0 = kChunk * (c0 + (q4 < nch ? q4 : 0));
         T::load_async(ktile + q4 * T::kBytes, K + int64_t(r0) * kv_stride + hkv * D, int(kv_stride), wave, lane);
     }
     // Operand read offsets.  Chunk 2 x + h of row j32 sits at position
@@ -210,16 +225,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
     static_assert(NT == 4 || NT == 2, "D is 128 or 64");
     TREEATTN_FENCE_ACC("s_nop 1");  // zeroing writes -> first MFMA read
 
-    // The pair's nonempty query blocks are the contiguous range from its
-    // first block with a real token to hi / 128 (each column is a range
-    // starting at its own block).
-    const int hi0 = blk_max[kb0], hi1 = has1 ? blk_max[kb1] : -1;
-    const int hi = max(hi0, hi1);
-    // (clipped to the launch's query blocks [qb_lo, qb_hi))
-    const int qhi = hi >= 0 ? min(min(nb, qb_hi) - 1, hi / kBlock) : -1;
-    const int qlo = max(hi0 >= 0 ? kb0 : kb1, qb_lo);
-    const int nsteps = (qhi >= qlo ? qhi - qlo + 1 : 0) * 2 * G;
-    const int kmax_w = kb0 * kBlock + 64 * wave + 63;
+    const int kmax_w = kChunk * cw + 63;
     int lo_w = min(sek[0], sek[1]);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) lo_w = min(lo_w, __shfl_xor(lo_w, o));
@@ -229,22 +235,16 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
     auto gtile = [&](int buf) { return smem + buf * kStage + T::kBytes; };
     auto lsev = [&](int buf) { return smem + buf * kStage + 2 * T::kBytes; };
     auto dlv = [&](int buf) { return smem + buf * kStage + 2 * T::kBytes + 256; };
-    // Steps run over the query heads of the group fastest, then the two
-    // 64-query halves of a 128-query block, then the blocks from the last
-    // down, so the pairs in flight on an XCD read the same Q / dO tiles at
-    // about the same time.
+    // Steps run over the query heads of the group fastest, then the 64-query
+    // steps from the last down, so the groups in flight on an XCD read the
+    // same Q / dO tiles at about the same time.
     struct StepPos {
-        int qbase, head, half;
+        int qbase, head;
     };
     auto advance = [&](StepPos& p) {
         if (++p.head == G) {
             p.head = 0;
-            if (++p.half == 2) {
-                p.half = 0;
-                p.qbase -= 3 * kStep;
-            } else {
-                p.qbase += kStep;
-            }
+            p.qbase -= kStep;
         }
     };
     const uint32_t q_row_bytes = uint32_t(q_stride) * 2u;
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
         if (wave == 0) load_row64_async(lsev(buf), NLS + int64_t(hq) * L + p.qbase, lane);
         if (wave == 1) load_row64_async(dlv(buf), Delta + int64_t(hq) * L + p.qbase, lane);
     };
-    StepPos cur{qhi * kBlock, 0, 0}, nxt{qhi * kBlock, 0, 0};
+    StepPos cur{s_hi * kChunk, 0}, nxt{s_hi * kChunk, 0};
     // the first two steps' tiles; step st issues step st + 2's
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -529,7 +529,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
     // registers 4 j + 0..3
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-        if (key[kk] >= L) continue;
+        if (!active) continue;
         const int64_t off = int64_t(key[kk]) * kv_stride + hkv * D + 4 * h;
         if constexpr (kRope) {
             // the gradient w.r.t. the unrotated key: rotate back by the key's
@@ -814,11 +814,12 @@ hipError_t launch_bwd_d(int phase, const bf16* Q, const bf16* K, const bf16* V, 
     const int64_t rows = int64_t(L) * sh.Hq;
     const float sl2 = sh.scale * kLog2e;
     float* nls = delta + rows;  // second half of the workspace
-    // dQ work items: (query block of the list, query head); dK/dV: (key-block
-    // pair of the heaviest-first order, key/value head)
+    // dQ work items: (query block of the list, query head); dK/dV: (key
+    // group of the heaviest-first order, key/value head), with the slack of
+    // dkdv_workgroups over the groups' number
     const int32_t* q_order = sel.q_list ? sel.q_list : mp.q_order;
     const unsigned dq_grid = (sel.q_list ? unsigned(sel.n_q) : unsigned(sh.nb)) * unsigned(sh.Hq);
-    const unsigned n_pairs = sel.n_pairs >= 0 ? unsigned(sel.n_pairs) : unsigned((sh.nb + 1) / 2);
+    const unsigned n_wg = sel.n_wg >= 0 ? unsigned(sel.n_wg) : unsigned(dkdv_workgroups(int64_t(sh.nb) * 2));
     const int qb_lo = sel.qb_lo, qb_hi = sel.qb_hi;
     if (phase == kPhaseDelta)
         delta_bf16_kernel<D><<<dim3(unsigned((L + 256 / (D / 8) - 1) / (256 / (D / 8))), unsigned(sh.Hq)), 256, 0,
@@ -837,19 +838,19 @@ hipError_t launch_bwd_d(int phase, const bf16* Q, const bf16* K, const bf16* V, 
                 Q, K, V, dO, O, lse, delta, nls, dQ, se, q_order, mp.row_ptr, mp.row_ent, L, sh.Hq, sh.Hkv, sl2,
                 sh.scale, nullptr, nullptr);
     }
-    if ((phase == kPhaseAll || phase == kPhaseDkdv) && n_pairs > 0) {
-        const dim3 grid(n_pairs * unsigned(sh.Hkv));
+    if ((phase == kPhaseAll || phase == kPhaseDkdv) && n_wg > 0) {
+        const dim3 grid(n_wg * unsigned(sh.Hkv));
         if (sel.dk_acc)
             dkdv_bf16_kernel<D, true, false><<<grid, kThreads, 0, stream>>>(
-                Q, K, V, dO, nls, delta, dK, dV, sel.dk_acc, sel.dv_acc, se, mp.p_order, mp.blk_min, mp.blk_max, L,
+                Q, K, V, dO, nls, delta, dK, dV, sel.dk_acc, sel.dv_acc, se, mp.g_order, mp.hi64, mp.hdr, L,
                 sh.Hq, sh.Hkv, qb_lo, qb_hi, sl2, sh.scale, nullptr, nullptr);
         else if (fuse_rope)
             dkdv_bf16_kernel<D, false, true><<<grid, kThreads, 0, stream>>>(
-                Q, K, V, dO, nls, delta, dK, dV, nullptr, nullptr, se, mp.p_order, mp.blk_min, mp.blk_max, L,
+                Q, K, V, dO, nls, delta, dK, dV, nullptr, nullptr, se, mp.g_order, mp.hi64, mp.hdr, L,
                 sh.Hq, sh.Hkv, qb_lo, qb_hi, sl2, sh.scale, rope.pos, rope.tab);
         else
             dkdv_bf16_kernel<D, false, false><<<grid, kThreads, 0, stream>>>(
-                Q, K, V, dO, nls, delta, dK, dV, nullptr, nullptr, se, mp.p_order, mp.blk_min, mp.blk_max, L,
+                Q, K, V, dO, nls, delta, dK, dV, nullptr, nullptr, se, mp.g_order, mp.hi64, mp.hdr, L,
                 sh.Hq, sh.Hkv, qb_lo, qb_hi, sl2, sh.scale, nullptr, nullptr);
     }
     if (phase == kPhaseDq && dq_grid > 0)

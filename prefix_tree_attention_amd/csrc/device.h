@@ -26,16 +26,34 @@ constexpr int64_t kMaxL = 1 << 20;   // largest packed length accepted
 //   col_cnt  [nb]     nonempty tiles per key block
 //   col_ptr  [nb+1]
 //   col_ent  [T]      (query block << 1) | partial, ascending query block
-//   q_order  [nb]     query blocks, most nonempty tiles first (ties: index)
+//   q_order  [nb]     query blocks in descending position (the forward's and
+//                     dQ's work order)
 //   k_order  [nb]     key blocks, most nonempty tiles first (ties: index)
 //   blk_cnt  [nb]     real tokens per block, then their exclusive prefix
 //   blk_hsum [nb]     histogram mass per block, then its exclusive prefix
-//   p_order  [np]     key-block pairs (2p, 2p + 1), np = (nb + 1) / 2, most
-//                     nonempty query blocks first (ties: index)
+//   hi64     [n64]    max subtree end over each 64-key chunk (pads: -1),
+//                     n64 = L / 64
+//   g_order  [n64]    the dK/dV kernel's key groups, most 64-query steps
+//                     first (ties: index), as first chunk | (chunks - 1) << 14;
+//                     hdr[3] holds their number
+// Key groups: consecutive chunks with the same hi64 form a run (a node's
+// chunks share one subtree end), and each run is cut into groups of at
+// most four chunks from its start, so the groups tile the chunks.  A
+// group's keys see query steps (64 rows) from its first chunk to
+// hi64 / 64 at most.
+// If the runs would give more groups starting before the last real chunk
+// c_end than ceil(c_end / 4) + ceil(c_end / 16), every chunk is grouped by
+// four from chunk 0 instead (ceil(n64 / 4) groups), so a dK/dV launch of
+// dkdv_workgroups(c_end) workgroups per key/value head covers every group
+// with work (and, at c_end = n64, every group).
+constexpr int kChunk = 64;
+constexpr int kMaxGroupChunks = 4;
+__host__ __device__ inline int64_t dkdv_group_bound(int64_t c_end) { return (c_end + 3) / 4 + (c_end + 15) / 16; }
+__host__ __device__ inline int64_t dkdv_workgroups(int64_t c_end) { return dkdv_group_bound(c_end) + 2; }
 struct MetaLayout {
-    int64_t L, nb, T;
+    int64_t L, nb, T, n64;
     int64_t hdr, blk_min, blk_max, hist, row_cnt, row_ptr, row_ent, col_cnt, col_ptr, col_ent,
-        q_order, k_order, blk_cnt, blk_hsum, p_order, words;
+        q_order, k_order, blk_cnt, blk_hsum, hi64, g_order, words;
 };
 
 inline int64_t pad64(int64_t w) { return (w + 63) / 64 * 64; }
@@ -45,6 +63,7 @@ inline MetaLayout meta_layout(int64_t L) {
     m.L = L;
     m.nb = L / kBlock;
     m.T = m.nb * (m.nb + 1) / 2;
+    m.n64 = L / kChunk;
     int64_t o = 0;
     m.hdr = o;     o += 64;
     m.blk_min = o; o += pad64(m.nb);
@@ -60,7 +79,8 @@ inline MetaLayout meta_layout(int64_t L) {
     m.k_order = o; o += pad64(m.nb);
     m.blk_cnt = o; o += pad64(m.nb);
     m.blk_hsum = o; o += pad64(m.nb);
-    m.p_order = o; o += pad64((m.nb + 1) / 2);
+    m.hi64 = o;    o += pad64(m.n64);
+    m.g_order = o; o += pad64(m.n64);
     m.words = o;
     return m;
 }
@@ -75,14 +95,16 @@ struct MetaPtrs {
     const int32_t* k_order;
     const int32_t* blk_min;
     const int32_t* blk_max;
-    const int32_t* p_order;
+    const int32_t* hdr;
+    const int32_t* hi64;
+    const int32_t* g_order;
 };
 
 inline MetaPtrs meta_ptrs(const void* ws, int64_t L) {
     const MetaLayout m = meta_layout(L);
     const int32_t* w = static_cast<const int32_t*>(ws);
     return {w + m.row_ptr, w + m.row_ent, w + m.col_ptr, w + m.col_ent, w + m.q_order,
-            w + m.k_order, w + m.blk_min, w + m.blk_max, w + m.p_order};
+            w + m.k_order, w + m.blk_min, w + m.blk_max, w + m.hdr, w + m.hi64, w + m.g_order};
 }
 
 // Backward phases (TREE_BWD_* of the public header).
@@ -102,8 +124,8 @@ struct RowSel {
     const int32_t* q_list = nullptr;  // fwd / dQ: the query blocks to run (null: all, heaviest first)
     int n_q = 0;                      // entries of q_list
     int qb_lo = 0, qb_hi = 1 << 30;   // dK/dV: only query blocks in [qb_lo, qb_hi) contribute
-    int n_pairs = -1;                 // dK/dV: run the first n_pairs key-block pairs of the
-                                      // heaviest-first order (-1: all)
+    int n_wg = -1;                    // dK/dV: workgroups per key/value head, each taking every
+                                      // n_wg-th key group of the heaviest-first order (-1: nb / 2)
     float* dk_acc = nullptr;          // dK/dV: if set, add scale * dK and dV in float32 to
     float* dv_acc = nullptr;          // these [L, Hkv, D] arrays instead of writing dK / dV
 };

@@ -275,7 +275,7 @@ struct Exec {
             sel.n_q = int((c1 + kBlock - 1) / kBlock - c / kBlock);
             sel.qb_lo = int(c / kBlock);
             sel.qb_hi = int((c1 + kBlock - 1) / kBlock);
-            sel.n_pairs = int((last_real + 1 + 2 * kBlock - 1) / (2 * kBlock));
+            sel.n_wg = int(dkdv_workgroups((last_real + 1 + kChunk - 1) / kChunk));
             sel.dk_acc = f.acck;
             sel.dv_acc = f.accv;
             if (fwd)

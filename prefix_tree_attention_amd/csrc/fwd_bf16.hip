@@ -26,6 +26,7 @@
 // one FMA.
 
 #include <cmath>
+#include <type_traits>
 
 #include "device.h"
 #include "mfma.h"
@@ -57,8 +58,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     // 32x32x16 fragments: lane = MFMA column j32 (this lane's query) and k-half h
     const int j32 = lane & 31, h = lane >> 5;
     const int tr_e = 16 * ((lane >> 4) & 1), tr_i = lane & 15;
-    // work item: key/value-head major, then query blocks heaviest first,
-    // then the query heads of the group
+    // work item: key/value-head major, then query blocks in the metadata's
+    // order (descending position), then the query heads of the group
     const int G = Hq / Hkv, per_kv = (int(gridDim.x) / Hq) * G;
     const int work = xcd_logical_block();
     const int hkv = work / per_kv, rank = (work % per_kv) / G, h_q = hkv * G + work % G;
@@ -258,8 +259,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     // beside no MFMA at all.  Empty volatile asms hold each slot's results
     // in place: without them the row sum and the exp2 arguments were sunk
     // past the barriers to their uses.
-    auto step = [&](int st, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-        const bool has_next = st + 1 < nsteps;
+    auto step = [&](int st, f32x16 (&sc)[2], f32x16 (&sn)[2], auto last_t) {
+        constexpr bool kLast = decltype(last_t)::value;
+        const bool has_next = !kLast;
         // the next step's entry: this pair's for an even st, the next pair's
         // for an odd one (equal to it, or unused, past the last step)
         const int ent1 = (st & 1) ? ent_n : ent_c;
@@ -270,10 +272,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         const lds_char* ktn = ktile(st + 1);
         auto rd_k = [&](int x, int kk) { return T::frag_at(ktn + 32 * kk * T::kRowBytes, roff[x]); };
         // A = 32 d x 16 keys of V^T, read transposed from the V tile in the
-        // P^T key order (rows 16 m + 4 h + {0..3, 8..11}); unit u = 4 t + m
+        // P^T key order (rows 16 m + 4 h + {0..3, 8..11}); unit u = NT m + t, so
+        // consecutive MFMAs update different accumulators
         auto rd_v = [&](int u) {
-            const int rb = 16 * (u & 3) * T::kRowBytes;
-            return join_tr(T::tr_at(vt + rb, toff[u >> 2][0]), T::tr_at(vt + rb, toff[u >> 2][1]));
+            const int rb = 16 * (u / NT) * T::kRowBytes;
+            return join_tr(T::tr_at(vt + rb, toff[u % NT][0]), T::tr_at(vt + rb, toff[u % NT][1]));
         };
         constexpr int kE = 32 / NX;  // exponentials per k-step
         bf16x8 kf[NX][2], va[4 * NT], pb[4];
@@ -289,6 +292,26 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
                                        f32x4{a[b + 4], a[b + 5], a[b + 6], a[b + 7]});
             }
         };
+        if constexpr (kLast) {
+            // The last step has no next scores to compute.  Its keys come
+            // after every query of a wave whose queries all precede them
+            // (the second half of the diagonal tile for the first two
+            // waves): every p is then exactly 0, and the wave skips the
+            // exponentials and P V altogether.
+            if (kbase_at(ent_c, st) <= qb * kBlock + 32 * wave + 31) {
+#pragma unroll
+                for (int e = 0; e < 32; ++e) ex(e);
+#pragma unroll
+                for (int u = 0; u < 4 * NT; ++u) va[u] = rd_v(u);
+                float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int e = 0; e < 32; ++e) rs[e & 3] += sc[e >> 4][e & 15];
+#pragma unroll
+                for (int u = 0; u < 4 * NT; ++u) oacc[u % NT] = mfma32x32x16(va[u], pb[u / NT], oacc[u % NT]);
+                l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+            }
+            return;
+        }
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
             kf[x][0] = rd_k(x, 0);
@@ -323,7 +346,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (u + 2 < U) va[u + 2] = rd_v(u + 2);
-            oacc[u >> 2] = mfma32x32x16(va[u], pb[u & 3], oacc[u >> 2]);
+            oacc[u % NT] = mfma32x32x16(va[u], pb[u / NT], oacc[u % NT]);
             if (u < UA) {
                 constexpr int n = 32 / UA;
 #pragma unroll
@@ -370,12 +393,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     };
     // a query block's step count is even (two per 128-key tile), so the
     // score buffers alternate without copies
-    for (int st = 0; st < nsteps; st += 2) {
+    for (int st = 0; st + 2 < nsteps; st += 2) {
         const int ent_nn = row_ent[beg + min((st >> 1) + 2, nent - 1)];
-        step(st, sa, sb);
-        step(st + 1, sb, sa);
+        step(st, sa, sb, std::false_type{});
+        step(st + 1, sb, sa, std::false_type{});
         ent_c = ent_n;
         ent_n = ent_nn;
+    }
+    if (nsteps > 0) {
+        step(nsteps - 2, sa, sb, std::false_type{});
+        step(nsteps - 1, sb, sa, std::true_type{});
     }
 
 #undef TREEATTN_SCHED

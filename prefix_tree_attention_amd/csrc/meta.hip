@@ -40,7 +40,7 @@ __global__ void meta_init(int32_t* __restrict__ hist, int64_t n_hist, int32_t* _
 __global__ __launch_bounds__(128) void meta_blocks(const int32_t* __restrict__ se, int32_t* __restrict__ hist,
                                                    int32_t* __restrict__ blk_min, int32_t* __restrict__ blk_max,
                                                    int32_t* __restrict__ blk_cnt, int32_t* __restrict__ hdr,
-                                                   int L) {
+                                                   int32_t* __restrict__ hi64, int L) {
     const int b = blockIdx.x;
     const int j = b * kBlock + threadIdx.x;
     int s = se[j];
@@ -67,6 +67,7 @@ __global__ __launch_bounds__(128) void meta_blocks(const int32_t* __restrict__ s
         smn[wave] = mn;
         smx[wave] = mx;
         sreal[wave] = __popcll(real);
+        hi64[2 * b + wave] = mx;  // each wave holds one 64-key chunk
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -151,16 +152,46 @@ __device__ inline long long block_exclusive_scan(long long x, long long* sh, lon
     return res;
 }
 
+// Exclusive max-scan of one int per thread across the workgroup, in thread
+// order (-1 for thread 0).  Uses `sh` (>= 17 ints of shared memory).
+__device__ inline int block_exclusive_max(int x, int* sh) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    int inc = x;
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(inc, off);
+        if (lane >= off) inc = max(inc, y);
+    }
+    if (lane == 63) sh[wave] = inc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = -1;
+        for (int w = 0; w < nw; ++w) {
+            const int v = sh[w];
+            sh[w] = run;
+            run = max(run, v);
+        }
+    }
+    __syncthreads();
+    int ex = __shfl_up(inc, 1);
+    if (lane == 0) ex = -1;
+    const int res = max(sh[wave], ex);
+    __syncthreads();
+    return res;
+}
+
 // Single workgroup over per-block values: column counts (closed form),
 // exclusive prefixes of (real tokens, histogram mass) per block and of
-// (row, column) counts (the CSR pointers), and the heaviest-first orders.
+// (row, column) counts (the CSR pointers), the heaviest-first orders and the
+// dK/dV kernel's key groups.
 __global__ __launch_bounds__(1024) void meta_scan(const int32_t* __restrict__ blk_max,
                                                   int32_t* __restrict__ blk_cnt, int32_t* __restrict__ blk_hsum,
                                                   const int32_t* __restrict__ row_cnt, int32_t* __restrict__ col_cnt,
                                                   int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_ptr,
                                                   int32_t* __restrict__ q_order, int32_t* __restrict__ k_order,
-                                                  int32_t* __restrict__ p_order, int nb) {
+                                                  const int32_t* __restrict__ hi64, int32_t* __restrict__ g_order,
+                                                  int32_t* __restrict__ hdr, int nb) {
     __shared__ long long sh[32];
+    __shared__ int shi[32];
     const int t = threadIdx.x, nt = blockDim.x;
     const int chunk = (nb + nt - 1) / nt;
     const int a = min(nb, t * chunk), e = min(nb, a + chunk);
@@ -206,71 +237,128 @@ __global__ __launch_bounds__(1024) void meta_scan(const int32_t* __restrict__ bl
         }
     }
 
-    // heaviest-first orders, ties by index: the keys
-    // ((nb - count) << 13) | index are unique, so sorting them ascending
+    // The forward and dQ take query blocks in descending position: the
+    // workgroups in flight on an XCD then hold neighbouring blocks, whose
+    // row lists name mostly the same key tiles (read from its L2), and
+    // within a trie the later blocks have the longer lists, so long items
+    // still start first.  (Heaviest-first over the whole launch spread the
+    // blocks in flight over all tries and ran 6-8% slower on GRPO-shaped
+    // batches.)  The key-block order is heaviest first, ties by index: the
+    // keys ((nb - count) << 13) | index are unique, so sorting them ascending
     // with a bitonic network in LDS gives exactly that order in
-    // O(nb log^2 nb) work (nb <= 8192 = 2^13 blocks).  A key-block pair's
-    // count is the number of query blocks in the union of its two columns:
-    // each column is a contiguous range starting at its own block, so the
-    // union is the range from the first block with a real token to the
-    // larger of the two ends.
+    // O(nb log^2 nb) work (nb <= 8192 = 2^13 blocks).
     constexpr int kMaxNb = int(kMaxL / kBlock);
+    constexpr int kMaxChunks = int(kMaxL / kChunk);
     static_assert(kMaxNb <= (1 << 13), "block index must fit 13 bits");
-    __shared__ unsigned kq[kMaxNb], kk[kMaxNb], kpr[kMaxNb / 2];
+    static_assert(kMaxChunks <= (1 << 14), "chunk index must fit 14 bits");
+    __shared__ unsigned kk[kMaxNb], kg[kMaxChunks];
+    __shared__ unsigned char gflag[kMaxChunks];
     int n = 1;
     while (n < nb) n <<= 1;
-    const int np = (nb + 1) / 2, npp = (n + 1) / 2;
     __syncthreads();  // col_cnt written by other threads above
-    for (int i = t; i < n; i += nt) {
-        kq[i] = i < nb ? (unsigned(nb - row_cnt[i]) << 13) | unsigned(i) : 0xffffffffu;
-        kk[i] = i < nb ? (unsigned(nb - col_cnt[i]) << 13) | unsigned(i) : 0xffffffffu;
-    }
-    for (int i = t; i < npp; i += nt) {
-        unsigned key = 0xffffffffu;
-        if (i < np) {
-            const int b0 = 2 * i, b1 = 2 * i + 1;
-            const int c0 = col_cnt[b0], c1 = b1 < nb ? col_cnt[b1] : 0;
-            const int end = max(c0 ? b0 + c0 : 0, c1 ? b1 + c1 : 0);  // one past the last query block
-            const int cnt = c0 ? end - b0 : (c1 ? end - b1 : 0);
-            key = (unsigned(nb - cnt) << 13) | unsigned(i);
-        }
-        kpr[i] = key;
-    }
+    for (int i = t; i < n; i += nt) kk[i] = i < nb ? (unsigned(nb - col_cnt[i]) << 13) | unsigned(i) : 0xffffffffu;
     __syncthreads();
     for (int k = 2; k <= n; k <<= 1)
         for (int j = k >> 1; j > 0; j >>= 1) {
             for (int i = t; i < n; i += nt) {
                 const int p = i ^ j;
                 if (p > i) {
-                    const bool up = (i & k) == 0;
-                    unsigned x = kq[i], y = kq[p];
-                    if ((x > y) == up) {
-                        kq[i] = y;
-                        kq[p] = x;
-                    }
-                    x = kk[i];
-                    y = kk[p];
-                    if ((x > y) == up) {
+                    const unsigned x = kk[i], y = kk[p];
+                    if ((x > y) == ((i & k) == 0)) {
                         kk[i] = y;
                         kk[p] = x;
-                    }
-                    if (p < npp && k <= npp) {
-                        x = kpr[i];
-                        y = kpr[p];
-                        if ((x > y) == up) {
-                            kpr[i] = y;
-                            kpr[p] = x;
-                        }
                     }
                 }
             }
             __syncthreads();
         }
     for (int i = t; i < nb; i += nt) {
-        q_order[i] = int(kq[i] & 0x1fffu);
+        q_order[i] = nb - 1 - i;
         k_order[i] = int(kk[i] & 0x1fffu);
     }
-    for (int i = t; i < np; i += nt) p_order[i] = int(kpr[i] & 0x1fffu);
+
+    // Key groups of the dK/dV kernel: a run of chunks with one subtree-end
+    // maximum, cut every four chunks from the run's start.  Each thread
+    // walks a contiguous range of chunks, starting from the last run start
+    // before it; groups are then compacted in chunk order, keyed
+    // ((n64 - steps) << 14) | first chunk with steps = the 64-query steps
+    // the group's keys can see (first chunk .. the largest hi64 / 64), and
+    // sorted.
+    // If that gives more groups starting before c_end (one past the last
+    // chunk holding a real token) than dkdv_group_bound(c_end), the chunks
+    // are grouped by four from chunk 0 instead, which bounds the dK/dV
+    // launch (dkdv_workgroups).
+    const int n64 = 2 * nb;
+    const int gch = (n64 + nt - 1) / nt;
+    const int ga = min(n64, t * gch), ge = min(n64, ga + gch);
+    auto run_start = [&](int c) { return c == 0 || hi64[c - 1] != hi64[c]; };
+    int last = -1, lreal = 0;
+    for (int c = ga; c < ge; ++c) {
+        if (run_start(c)) last = c;
+        if (hi64[c] >= 0) lreal = c + 1;
+    }
+    __shared__ int s_cend;
+    if (t == 0) s_cend = 0;
+    int rs = block_exclusive_max(last, shi);  // (its barriers order s_cend's initialisation)
+    if (lreal) atomicMax(&s_cend, lreal);
+    __syncthreads();
+    const int c_end = s_cend;
+    int ng = 0, ngr = 0;
+    for (int c = ga; c < ge; ++c) {
+        if (run_start(c)) rs = c;
+        const bool g = ((c - rs) & (kMaxGroupChunks - 1)) == 0;
+        gflag[c] = g;
+        ng += g;
+        ngr += g && c < c_end;
+    }
+    long long ngt;
+    block_exclusive_scan(ngr, sh, &ngt);
+    if (ngt > dkdv_group_bound(c_end)) {
+        ng = 0;
+        for (int c = ga; c < ge; ++c) {
+            const bool g = (c & (kMaxGroupChunks - 1)) == 0;
+            gflag[c] = g;
+            ng += g;
+        }
+    }
+    const int gbase = int(block_exclusive_scan(ng, sh, &ngt));
+    const int n_groups = int(ngt);
+    __syncthreads();  // gflag complete (the fallback rewrote it)
+    {
+        int g = gbase;
+        for (int c = ga; c < ge; ++c)
+            if (gflag[c]) {
+                int hi = hi64[c];  // the group's largest subtree end
+                for (int e = c + 1; e < min(n64, c + kMaxGroupChunks) && !gflag[e]; ++e) hi = max(hi, hi64[e]);
+                const int steps = hi >= 0 ? hi / kChunk - c + 1 : 0;
+                kg[g++] = (unsigned(n64 - steps) << 14) | unsigned(c);
+            }
+    }
+    int ngp = 1;
+    while (ngp < n_groups) ngp <<= 1;
+    for (int i = n_groups + t; i < ngp; i += nt) kg[i] = 0xffffffffu;
+    __syncthreads();
+    for (int k = 2; k <= ngp; k <<= 1)
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = t; i < ngp; i += nt) {
+                const int p = i ^ j;
+                if (p > i) {
+                    const unsigned x = kg[i], y = kg[p];
+                    if ((x > y) == ((i & k) == 0)) {
+                        kg[i] = y;
+                        kg[p] = x;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    for (int i = t; i < n_groups; i += nt) {
+        const int c = int(kg[i] & 0x3fffu);
+        int m = 1;
+        while (m < kMaxGroupChunks && c + m < n64 && !gflag[c + m]) ++m;
+        g_order[i] = c | ((m - 1) << 14);
+    }
+    if (t == 0) hdr[3] = n_groups;
 }
 
 // One workgroup (256 threads) per block b: the position ids of its tokens,
@@ -358,12 +446,12 @@ hipError_t launch_meta(const int32_t* se, int64_t L, int32_t* pos, uint8_t* tile
     const int nb = int(m.nb);
     meta_init<<<64, 256, 0, stream>>>(w + m.hist, L + 1, w + m.hdr, L, nb);
     meta_blocks<<<nb, kBlock, 0, stream>>>(se, w + m.hist, w + m.blk_min, w + m.blk_max, w + m.blk_cnt, w + m.hdr,
-                                          int(L));
+                                          w + m.hi64, int(L));
     meta_tiles<<<nb, 256, 0, stream>>>(w + m.blk_min, w + m.blk_max, w + m.hist, tile_class, w + m.row_cnt,
                                       w + m.blk_hsum, nb);
     meta_scan<<<1, 1024, 0, stream>>>(w + m.blk_max, w + m.blk_cnt, w + m.blk_hsum, w + m.row_cnt, w + m.col_cnt,
-                                     w + m.row_ptr, w + m.col_ptr, w + m.q_order, w + m.k_order, w + m.p_order,
-                                     nb);
+                                     w + m.row_ptr, w + m.col_ptr, w + m.q_order, w + m.k_order, w + m.hi64,
+                                     w + m.g_order, w + m.hdr, nb);
     meta_lists<<<nb, 256, 0, stream>>>(se, w + m.hist, w + m.blk_min, w + m.blk_max, w + m.blk_cnt, w + m.blk_hsum,
                                       w + m.row_ptr, w + m.col_ptr, pos, w + m.row_ent, w + m.col_ent, int(L), nb);
     return hipGetLastError();

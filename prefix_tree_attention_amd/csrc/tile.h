@@ -48,19 +48,24 @@ __device__ __forceinline__ uint32_t lds_addr(const lds_char* p) { return uint32_
 // buffer being filled from the one being read, and would otherwise wait for
 // the prefetch to land before the first transposing LDS read of a step.
 // Completion is the caller's s_waitcnt vmcnt followed by a workgroup
-// barrier.  M0 carries the LDS address (one wait state before its use); no
-// compiler-generated code in these kernels uses M0.
+// barrier.  M0 carries the LDS address (one wait state before its use).
+// Both M0 and, for the scalar add, SCC are declared clobbered: with SCC
+// undeclared the compiler once kept a compare's result in SCC across a run
+// of these loads and selected on the carry of the M0 add instead.
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds));
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+                 : "m0");
 }
 // same, LDS address lds + IMM (one scalar add into M0)
 template <int IMM>
 __device__ __forceinline__ void dma16_at(const void* base, uint32_t voff, uint32_t lds) {
     asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base),
-                 "s"(lds), "n"(IMM));
+                 "s"(lds), "n"(IMM)
+                 : "m0", "scc");
 }
 __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds));
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+                 : "m0");
 }
 
 template <int D>

@@ -98,11 +98,44 @@ def meta_layout(L: int) -> dict:
                        ("row_cnt", pad(nb)), ("row_ptr", pad(nb + 1)), ("row_ent", pad(T)),
                        ("col_cnt", pad(nb)), ("col_ptr", pad(nb + 1)), ("col_ent", pad(T)),
                        ("q_order", pad(nb)), ("k_order", pad(nb)), ("blk_cnt", pad(nb)), ("blk_hsum", pad(nb)),
-                       ("p_order", pad((nb + 1) // 2))):
+                       ("hi64", pad(2 * nb)), ("g_order", pad(2 * nb))):
         out[name] = o
         o += size
     out["nb"] = nb
     return out
+
+
+def key_groups_ref(se):
+    """The dK/dV key groups the metadata forms (the rule stated in the
+    library's internal device header), in plain Python: (per-64-key-chunk
+    maximum subtree end, first chunk of each group in chunk order, whether
+    the four-chunk fallback applied)."""
+    se = np.asarray(se, np.int64)
+    n64 = len(se) // 64
+    hi = np.full(n64, -1, np.int64)
+    for c in range(n64):
+        s = se[64 * c:64 * c + 64]
+        s = s[s >= 0]
+        if s.size:
+            hi[c] = s.max()
+    starts, rs = [], 0
+    for c in range(n64):
+        if c == 0 or hi[c - 1] != hi[c]:
+            rs = c
+        if (c - rs) % 4 == 0:
+            starts.append(c)
+    real = np.nonzero(hi >= 0)[0]
+    c_end = int(real[-1]) + 1 if real.size else 0
+    fallback = sum(c < c_end for c in starts) > (c_end + 3) // 4 + (c_end + 15) // 16
+    if fallback:
+        starts = list(range(0, n64, 4))
+    return hi, starts, fallback
+
+
+def dkdv_workgroups(c_end: int) -> int:
+    """The dK/dV launch's workgroups per key/value head for groups before
+    chunk c_end (the library's bound plus its slack of 2)."""
+    return (c_end + 3) // 4 + (c_end + 15) // 16 + 2
 
 
 def small_cases():

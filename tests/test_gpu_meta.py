@@ -7,7 +7,7 @@ import pytest
 import oracle
 import workloads
 import prefix_tree_attention_amd as pta
-from gpu_common import announce, meta_layout, small_cases, torch_cuda
+from gpu_common import announce, dkdv_workgroups, key_groups_ref, meta_layout, small_cases, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
@@ -19,6 +19,11 @@ def _check_trie(torch, p_lib, p_or, tag):
     m = oracle.dense_ancestor_mask(p_or)
     pos_ref = oracle.position_ids(m)
     tc_ref = oracle.tile_classes(m)
+    # per 64-key chunk: first and last query that sees any of its keys
+    n64 = p_lib.L // 64
+    seen_by = m.reshape(p_lib.L, n64, 64).any(2)  # [query, chunk]
+    seen = [np.nonzero(seen_by[:, c])[0] for c in range(n64)]
+    del seen_by
     del m
     pos = meta.pos.cpu().numpy()
     tc = meta.tile_class.cpu().numpy()
@@ -40,22 +45,30 @@ def _check_trie(torch, p_lib, p_or, tag):
         qbs = np.nonzero(tc_ref[:, kb])[0]
         assert (ent >> 1).tolist() == qbs.tolist()
         assert ((ent & 1) == (tc_ref[qbs, kb] == 1)).all()
-    rc = (tc_ref != 0).sum(1)
     cc = (tc_ref != 0).sum(0)
     qo = ws[lay["q_order"]:lay["q_order"] + nb]
     ko = ws[lay["k_order"]:lay["k_order"] + nb]
-    assert qo.tolist() == sorted(range(nb), key=lambda x: (-rc[x], x))
+    assert qo.tolist() == list(range(nb - 1, -1, -1))
     assert ko.tolist() == sorted(range(nb), key=lambda x: (-cc[x], x))
-    # key-block pairs (2p, 2p + 1): the union of their columns is one
-    # contiguous run of query blocks, and the pairs come heaviest first
-    npair = (nb + 1) // 2
-    pc = []
-    for p in range(npair):
-        qbs = np.nonzero((tc_ref[:, 2 * p:2 * p + 2] != 0).any(1))[0]
-        assert len(qbs) == 0 or qbs[-1] - qbs[0] + 1 == len(qbs), f"pair {p} columns not contiguous"
-        pc.append(len(qbs))
-    po = ws[lay["p_order"]:lay["p_order"] + npair]
-    assert po.tolist() == sorted(range(npair), key=lambda x: (-pc[x], x))
+    # dK/dV key groups: the chunk maxima and the grouping rule, bit for bit,
+    # and (from the oracle's mask) every query that sees a group's keys lies
+    # in the query steps the kernel walks for it, first chunk .. hi / 64
+    hi_ref, starts, _ = key_groups_ref(p_lib.subtree_end)
+    assert ws[lay["hi64"]:lay["hi64"] + n64].tolist() == hi_ref.tolist()
+    ng = int(ws[lay["hdr"] + 3])
+    assert ng == len(starts) and ng <= dkdv_workgroups(n64)
+    ends = starts[1:] + [n64]
+    ghi = {c: int(hi_ref[c:e].max()) for c, e in zip(starts, ends)}
+    steps = {c: (ghi[c] // 64 - c + 1 if ghi[c] >= 0 else 0) for c in starts}
+    want = [c | ((e - c - 1) << 14) for c, e in sorted(zip(starts, ends), key=lambda g: (-steps[g[0]], g[0]))]
+    assert ws[lay["g_order"]:lay["g_order"] + ng].tolist() == want
+    for c, e in zip(starts, ends):
+        assert 1 <= e - c <= 4
+        q = np.concatenate(seen[c:e])
+        if q.size:
+            assert q.min() >= 64 * c and q.max() <= 64 * (ghi[c] // 64) + 63, f"group at chunk {c}"
+        else:
+            assert ghi[c] == -1, f"group at chunk {c} has keys but no query sees them"
     assert ws[lay["hdr"] + 2] == p_or.n_tokens
 
 
