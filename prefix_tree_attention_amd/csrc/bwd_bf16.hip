@@ -121,14 +121,16 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
     const int32_t* __restrict__ se, const int32_t* __restrict__ g_order, const int32_t* __restrict__ hi64,
     const int32_t* __restrict__ hdr, int L, int Hq, int Hkv, int qb_lo, int qb_hi, float scale_log2,
     float scale, const int32_t* __restrict__ pos, const float* __restrict__ rope_tab) {
-    using T = Tile<D>;
+    using T = PairTile<D>;
     constexpr int NX = D / 16;  // k-steps of S = Q K^T and dP = dO V^T
     constexpr int NT = D / 32;  // 32-row d-blocks of dK^T and dV^T
     constexpr int kStage = 2 * T::kBytes + 512;  // Q tile, dO tile, -LSE / scale [64], -Delta [64]
     constexpr int kKBytes = 4 * T::kBytes;       // K rows of the 256 keys
-    __shared__ __attribute__((aligned(1024))) char smem_raw[kKBytes + 2 * kStage];
-    lds_char* const ktile = (lds_char*)smem_raw;
-    lds_char* const smem = ktile + kKBytes;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[2 * kStage + kKBytes];
+    // the two Q / dO stages first: a stage read then sits at a small
+    // immediate from its per-step base
+    lds_char* const smem = (lds_char*)smem_raw;
+    lds_char* const ktile = smem + 2 * kStage;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
     const int j32 = lane & 31, h = lane >> 5;
     // transposing reads: 16-lane group gi takes 16 d values starting at
     // 16 (gi % 2) and query rows 4 h + 0..3 of a k-step
-    const int tr_e = 16 * ((lane >> 4) & 1), tr_i = lane & 15;
+    const int tr_i = lane & 15;
     // work item: key/value-head major, then the key groups heaviest first
     // (the metadata bounds their number by the launch's workgroups per head)
     const int per_kv = int(gridDim.x) / Hkv;
@@ -183,22 +185,15 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
         const int r0 = kChunk * (c0 + (q4 < nch ? q4 : 0));
         T::load_async(ktile + q4 * T::kBytes, K + int64_t(r0) * kv_stride + hkv * D, int(kv_stride), wave, lane);
     }
-    // Operand read offsets.  Chunk 2 x + h of row j32 sits at position
-    // (2 x + h) ^ s = 2 (x ^ (s / 2)) + ((h ^ s) & 1), s = swz(j32), so the
-    // row-major read of k-step x is at (32 x ^ ru) + rbase; likewise the
-    // transposing read of d-block t (rows 4 h + 8 v + ..) is at
-    // (64 t ^ tx[v]) + tbase[v].  One v_xad_u32 per use instead of a
-    // register per offset.
-    int ru = 32 * (T::swz(j32) >> 1);
-    int rbase = T::slot(j32, h) - ru;
-    int tx[2], tbase[2];
-#pragma unroll
-    for (int v = 0; v < 2; ++v) {
-        tx[v] = 64 * (T::swz(4 * h + 8 * v + (tr_i >> 2)) >> 2);
-        tbase[v] = T::tr_offset(4 * h + 8 * v, tr_e, tr_i) - tx[v];
-    }
-    auto roff = [&](int x) { return ((32 * x) ^ ru) + rbase; };
-    auto toff = [&](int t, int v) { return ((64 * t) ^ tx[v]) + tbase[v]; };
+    // Operand read offsets, one base per lane and pattern: the row-major
+    // read of k-step x (chunk 2 x + h of row j32) is at rlane + PS x; the
+    // transposing read of d-block t (rows 4 h + 8 v + 0..3 of a 16-row
+    // k-step, elements 32 t + 16 ((lane / 16) % 2) + ..) at
+    // tlane + R8 v + 2 PS t.  Every other term is an immediate.
+    int rlane = T::rb(j32) + 16 * h;
+    int tlane = T::rb(4 * h) + T::kPs * ((lane >> 4) & 1) + 8 * tr_i;
+    auto roff = [&](int x) { return rlane + T::kPs * x; };
+    auto toff = [&](int t, int v) { return tlane + T::kR8 * v + 2 * T::kPs * t; };
     // dK^T, dV^T accumulators of key block kk: d-block t, register r =
     // d 32 t + 8 (r / 4) + 4 h + r % 4
     f32x16 dk[2][NT], dv[2][NT];
@@ -275,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
     wait_vm_all();
     __syncthreads();
 
-    const lds_char* kt = ktile + 64 * wave * T::kRowBytes;
+    const lds_char* kt = ktile + wave * T::kBytes;
     struct SOps {
         bf16x8 aq, k0, k1;
     };
@@ -283,8 +278,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
     // 32-key K blocks
     auto rd_s = [&](int buf, int c, int x) {
         const int ro = roff(x);
-        return SOps{T::frag_at(qtile(buf) + 32 * c * T::kRowBytes, ro), T::frag_at(kt, ro),
-                    T::frag_at(kt + 32 * T::kRowBytes, ro)};
+        return SOps{T::frag_at(qtile(buf) + 2 * c * T::kGs, ro), T::frag_at(kt, ro),
+                    T::frag_at(kt + 2 * T::kGs, ro)};
     };
     // S starts at -LSE / scale and dP at -Delta, so they leave
     // S - LSE / scale and dP - Delta; register r of a score accumulator
@@ -328,12 +323,11 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
         const lds_char* gt = gtile(buf);
 
         // k-step x of dP: dO rows of the half
-        auto rd_g = [&](int c, int x) { return T::frag_at(gt + 32 * c * T::kRowBytes, roff(x)); };
+        auto rd_g = [&](int c, int x) { return T::frag_at(gt + 2 * c * T::kGs, roff(x)); };
         // d-block t, k-step m of the gradients from the dO tile (dO^T) or
-        // the Q tile (Q^T): rows 32 c + 16 m + 4 h + {0..3, 8..11} (a 16-row
-        // move keeps the swizzle phase, so it is a plain offset)
+        // the Q tile (Q^T): rows 32 c + 16 m + 4 h + {0..3, 8..11}
         auto rd_tr = [&](const lds_char* tile, int c, int t, int m) {
-            const int rb = (32 * c + 16 * m) * T::kRowBytes;
+            const int rb = (2 * c + m) * T::kGs;
             return join_tr(T::tr_at(tile + rb, toff(t, 0)), T::tr_at(tile + rb, toff(t, 1)));
         };
         auto cvt8 = [](const f32x16& s, int m) {
@@ -345,7 +339,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
         constexpr int kDs = 16 / NT / 2;  // dS products per gradient MFMA pair
         // opaque per step, so the offsets are formed at each use rather than
         // hoisted out of the loop into one register each
-        asm volatile("" : "+v"(ru), "+v"(rbase), "+v"(tx[0]), "+v"(tx[1]), "+v"(tbase[0]), "+v"(tbase[1]));
+        asm volatile("" : "+v"(rlane), "+v"(tlane));
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             f32x16 sc[2], dp[2];
@@ -389,11 +383,9 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
                 // of reach of the dP MFMAs.
                 float sl = scale_log2;
                 if constexpr (kMasked)
-                    asm volatile("; partial half" : "+v"(ru), "+v"(rbase), "+v"(tx[0]), "+v"(tx[1]),
-                                 "+v"(tbase[0]), "+v"(tbase[1]), "+s"(sl));
+                    asm volatile("; partial half" : "+v"(rlane), "+v"(tlane), "+s"(sl));
                 else
-                    asm volatile("; full half" : "+v"(ru), "+v"(rbase), "+v"(tx[0]), "+v"(tx[1]), "+v"(tbase[0]),
-                                 "+v"(tbase[1]), "+s"(sl));
+                    asm volatile("; full half" : "+v"(rlane), "+v"(tlane), "+s"(sl));
                 TREEATTN_SCHED();
                 int lo_k[2] = {0, 0}, hi_k[2] = {0, 0};
                 if constexpr (kMasked) {
