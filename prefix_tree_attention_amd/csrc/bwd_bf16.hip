@@ -585,7 +585,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_bf16_kernel(
     const int32_t* __restrict__ q_order, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ row_ent,
     int L, int Hq, int Hkv, float scale_log2, float scale, const int32_t* __restrict__ pos,
     const float* __restrict__ rope_tab) {
-    using T = Tile<D>;
+    using T = PairTile<D>;
     constexpr int NS = D / 32, NT = D / 16;
     // K and V tiles and the keys' subtree ends, double-buffered
     __shared__ __attribute__((aligned(1024))) char smem_raw[4 * T::kBytes + 2 * 4 * kStep];
@@ -689,6 +689,12 @@ __global__ __launch_bounds__(kThreads, 2) void dq_bf16_kernel(
     wait_vm_all();
     __syncthreads();
 
+    // LDS offsets of this lane's operand reads (pair-major tiles): K and V
+    // rows 16 b + n, chunk 4 x + g, at rlane + 16-row moves + 2 PS x; K^T
+    // rows 4 g + 0..3 of each 16-row k-half, elements 16 t + 4 (n % 4) ..,
+    // at tlane + 16-row moves + PS t
+    const int rlane = T::rb(n) + 16 * (g & 1) + T::kPs * (g >> 1);
+    const int tlane = T::rb(4 * g) + 8 * n;
     for (int st = 0; st < nsteps; ++st) {
         const int buf = st & 1;
         const int ent = row_ent[beg + (st >> 1)];
@@ -708,8 +714,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_bf16_kernel(
                 bf16x8 ak[NS], av[NS];
 #pragma unroll
                 for (int x = 0; x < NS; ++x) {
-                    ak[x] = T::row_frag(kt, 16 * b + n, 4 * x + g);
-                    av[x] = T::row_frag(vt, 16 * b + n, 4 * x + g);
+                    ak[x] = T::frag_at(kt + b * T::kGs, rlane + 2 * T::kPs * x);
+                    av[x] = T::frag_at(vt + b * T::kGs, rlane + 2 * T::kPs * x);
                 }
 #pragma unroll
                 for (int qs = 0; qs < 2; ++qs) {
@@ -756,8 +762,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_bf16_kernel(
                 elementwise(std::false_type{});
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                const bf16x8 a = join_tr(T::tr_frag(kt, 32 * c + 4 * g, 16 * t, n),
-                                         T::tr_frag(kt, 32 * c + 16 + 4 * g, 16 * t, n));
+                const bf16x8 a = join_tr(T::tr_at(kt + 2 * c * T::kGs, tlane + T::kPs * t),
+                                         T::tr_at(kt + (2 * c + 1) * T::kGs, tlane + T::kPs * t));
 #pragma unroll
                 for (int qs = 0; qs < 2; ++qs) dq[qs][t] = mfma16x16x32(a, db[qs], dq[qs][t]);
             }

@@ -137,7 +137,7 @@ struct Tile {
     }
 };
 
-// 64-row tiles in pair-major blocks, for a kernel whose per-lane operand
+// 64-row tiles in pair-major blocks, for kernels whose per-lane operand
 // offsets must not cost address arithmetic at every read.
 //
 // Rows are grouped by RPB (4 for D = 128, 8 for D = 64): one 1 KB direct
@@ -147,31 +147,37 @@ struct Tile {
 //   - a transposing read of rows r0..r0+3 (r0 % 4 == 0) and elements
 //     16x..16x+15 gives lane i of the 16-lane group 8 bytes at
 //     rb(r0) + PS x + 8 i (the group's 128 bytes are contiguous),
-// with PS = 32 RPB: each lane keeps one base and every step of x, every
-// 16-row move (+GS) and every 8-row move inside a 16-row group (+R8) is an
-// immediate.  The blocks of a 16-row group start at offsets whose 16-byte
-// bank slots differ (D = 128: 0, 1040, 2176, 3216; D = 64: 0, 1040), which
-// makes a 16-lane row-major read of 16 consecutive rows touch 16 different
-// 16-byte bank slots, and 32 lanes of transposing reads (4 rows, 32
-// elements) one contiguous 256 bytes.
+// with PS = 32 RPB: each lane keeps one base per pattern, and every step of
+// x, every 16-row move (+GS) and every 8-row move inside a 16-row group
+// (+R8) is an immediate.  For D = 128 the four blocks of a 16-row group
+// start at 0, 1152, 2192 and 3344 bytes, i.e. at 16-byte bank slots 0, 8,
+// 9 and 1 (mod 16).  Then
+//   - a 16-lane row-major read of 16 consecutive rows touches 16 different
+//     bank slots,
+//   - 32 lanes of transposing reads over rows r0..r0+3 and 32 elements are
+//     256 contiguous bytes,
+//   - 32 lanes over rows r0..r0+7 and 16 elements (blocks 0 and 1, or 2
+//     and 3) fall on the two halves of the banks.
+// For D = 64 (blocks 0 and 1040 of a 16-row group) the first and third
+// hold; in the second, the two chunk pairs share banks.
 template <int D>
 struct PairTile {
     static_assert(D == 128 || D == 64, "D is 128 or 64");
     static constexpr int kRpb = D == 128 ? 4 : 8;         // rows per 1 KB block
     static constexpr int kPs = 32 * kRpb;                 // chunk-pair stride
     static constexpr int kBlocks = 16 / kRpb;             // blocks per 16-row group
-    static constexpr int kGs = D == 128 ? 4240 : 2064;    // 16-row group stride
-    static constexpr int kR8 = D == 128 ? 2176 : 1040;    // 8-row move inside a group
+    static constexpr int kGs = D == 128 ? 4368 : 2064;    // 16-row group stride
+    static constexpr int kR8 = D == 128 ? 2192 : 1040;    // 8-row move inside a group
     static constexpr int kBytes = 4 * kGs;
     __host__ __device__ static constexpr int block_base(int b) {
-        return D == 128 ? (b == 0 ? 0 : b == 1 ? 1040 : b == 2 ? 2176 : 3216) : (b == 0 ? 0 : 1040);
+        return D == 128 ? (b == 0 ? 0 : b == 1 ? 1152 : b == 2 ? 2192 : 3344) : (b == 0 ? 0 : 1040);
     }
     static_assert(D != 128 || (block_base(2) - block_base(0) == kR8 && block_base(3) - block_base(1) == kR8),
                   "8-row moves are one immediate");
     static_assert(block_base(kBlocks - 1) + 1024 <= kGs && kGs % 16 == 0, "blocks fit the group");
 
     // offset of row r's first chunk pair (r in 0..63)
-    __device__ static __forceinline__ int rb(int r) {
+    __host__ __device__ static __forceinline__ int rb(int r) {
         return kGs * (r >> 4) + (D == 128 ? block_base((r >> 2) & 3) + 32 * (r & 3)
                                           : block_base((r >> 3) & 1) + 32 * (r & 7));
     }
@@ -198,7 +204,7 @@ struct PairTile {
     // byte offset (from g0) of the 16 bytes lane `lane` fills in block J of
     // group `wave`: slot s = lane holds chunk 2 (s / 2RPB) + s % 2 of row
     // (s / 2) % RPB of the block
-    __device__ static __forceinline__ uint32_t lane_offset(int j, int stride, int wave, int lane) {
+    __host__ __device__ static __forceinline__ uint32_t lane_offset(int j, int stride, int wave, int lane) {
         const int r = 16 * wave + kRpb * j + ((lane >> 1) & (kRpb - 1));
         const int c = 2 * (lane / (2 * kRpb)) + (lane & 1);
         return uint32_t(r * stride + 8 * c) * 2u;

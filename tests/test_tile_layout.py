@@ -1,0 +1,123 @@
+"""The pair-major LDS tile layout of the dK/dV and dQ kernels, from the
+library's own layout functions (a host program built with hipcc evaluates
+them; no GPU needed):
+  - the direct loads' lane -> (row, chunk) mapping and the operand reads'
+    (row, chunk) -> LDS offset formula describe the same bijection;
+  - a model of the LDS (64 banks of 4 bytes; a b128 read served 16 lanes
+    at a time, a b64 transposing read 32 lanes at a time) finds no bank
+    conflict in any read pattern of the D = 128 kernels, and for D = 64
+    exactly the one 2-way conflict the header states."""
+
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "prefix_tree_attention_amd", "csrc")
+
+SOURCE = r"""
+#include <cstdio>
+#include "tile.h"
+template <int D> void dump() {
+    using T = treeattn::PairTile<D>;
+    std::printf("D %d %d %d %d %d %d\n", D, T::kPs, T::kGs, T::kR8, T::kBytes, T::kBlocks);
+    for (int r = 0; r < 64; ++r) std::printf("rb %d %d %d\n", D, r, T::rb(r));
+    const int stride = 4096;  // elements between consecutive rows
+    for (int w = 0; w < 4; ++w)
+        for (int j = 0; j < T::kBlocks; ++j)
+            for (int lane = 0; lane < 64; ++lane) {
+                const unsigned off = T::lane_offset(j, stride, w, lane) / 2;
+                std::printf("ld %d %d %d %u %u\n", D, w * T::kGs + T::block_base(j) + 16 * lane, lane, off / stride,
+                            (off % stride) / 8);
+            }
+}
+int main() {
+    dump<128>();
+    dump<64>();
+    return 0;
+}
+"""
+
+
+@pytest.fixture(scope="module")
+def layout(tmp_path_factory):
+    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    if not os.path.exists(hipcc) and shutil.which("hipcc") is None:
+        pytest.skip("hipcc not available")
+    d = tmp_path_factory.mktemp("tile")
+    src, exe = d / "dump.cpp", d / "dump"
+    src.write_text(SOURCE)
+    subprocess.run([hipcc if os.path.exists(hipcc) else "hipcc", "-x", "hip", "--offload-arch=gfx950", "-O1",
+                    "-std=c++17", "-I", CSRC, str(src), "-o", str(exe)], check=True, capture_output=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    res = {}
+    for line in out:
+        f = line.split()
+        if not f:
+            continue
+        D = int(f[1])
+        e = res.setdefault(D, {"rb": {}, "ld": {}})
+        if f[0] == "D":
+            e["ps"], e["gs"], e["r8"], e["bytes"], e["blocks"] = map(int, f[2:])
+        elif f[0] == "rb":
+            e["rb"][int(f[2])] = int(f[3])
+        else:
+            e["ld"][int(f[2])] = (int(f[4]), int(f[5]))
+    return res
+
+
+def _degree(addrs, passes):
+    """Largest number of different 4-byte words one bank serves in a pass."""
+    worst = 1
+    for p in passes:
+        banks = {}
+        for lane in p:
+            for a in addrs[lane]:
+                banks.setdefault((a // 4) % 64, set()).add(a // 4)
+        worst = max(worst, max(len(v) for v in banks.values()))
+    return worst
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_loads_and_reads_agree(layout, D):
+    e = layout[D]
+    rb, ps = e["rb"], e["ps"]
+    read = {}
+    for r in range(64):
+        for c in range(D // 8):
+            a = rb[r] + 16 * (c & 1) + ps * (c >> 1)
+            assert a % 16 == 0 and 0 <= a and a + 16 <= e["bytes"]
+            read[a] = (r, c)
+    assert len(read) == 64 * D // 8  # a bijection onto distinct 16-byte slots
+    assert e["ld"] == read  # each load lane fills exactly the slot the reads expect
+    # 8-row and 16-row moves are the constants the kernels add
+    for r in range(64):
+        if r % 16 < 8:
+            assert rb[r + 8] - rb[r] == e["r8"]
+        if r < 48:
+            assert rb[r + 16] - rb[r] == e["gs"]
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_bank_conflicts(layout, D):
+    e = layout[D]
+    rb, ps = e["rb"], e["ps"]
+    b128 = [range(i, i + 16) for i in range(0, 64, 16)]
+    b64 = [range(0, 32), range(32, 64)]
+    deg = {}
+    # 32x32x16 operand rows (lane: row l % 32, chunk 2x + l / 32)
+    deg["row32"] = max(_degree([[rb[l % 32] + 16 * (l // 32) + ps * x + k for k in (0, 4, 8, 12)] for l in range(64)],
+                               b128) for x in range(D // 16))
+    # 16x16x32 operand rows (lane: row l % 16, chunk 4x + l / 16)
+    deg["row16"] = max(_degree([[rb[l % 16] + 16 * ((l // 16) & 1) + ps * (2 * x + l // 32) + k for k in (0, 4, 8, 12)]
+                                for l in range(64)], b128) for x in range(D // 32))
+    # dK/dV transposing reads: group l / 16 takes rows 4 (l / 32) + 8 v + 0..3, chunk pair 2t + (l / 16) % 2
+    deg["tr32"] = max(_degree([[rb[4 * (l // 32) + 8 * v] + ps * (2 * t + ((l >> 4) & 1)) + 8 * (l & 15) + k
+                                for k in (0, 4)] for l in range(64)], b64) for t in range(D // 32) for v in range(2))
+    # dQ transposing reads: group g = l / 16 takes rows 4g + 0..3, chunk pair t
+    deg["tr16"] = max(_degree([[rb[4 * (l // 16)] + ps * t + 8 * (l & 15) + k for k in (0, 4)] for l in range(64)], b64)
+                      for t in range(D // 16))
+    want = {"row32": 1, "row16": 1, "tr32": 1 if D == 128 else 2, "tr16": 1}
+    assert deg == want
