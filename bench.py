@@ -105,9 +105,18 @@ def copy_calibration():
     return 0
 
 
+# device headers every kernel source compiles in
+KERNEL_HEADERS = ("device.h", "mfma.h", "tile.h")
+
+
 def source_sha(name: str) -> str:
-    with open(os.path.join(ROOT, "prefix_tree_attention_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source and the device headers it compiles in: a
+    traffic summary counts only while none of them has changed."""
+    h = hashlib.sha256()
+    for n in (name, *KERNEL_HEADERS):
+        with open(os.path.join(ROOT, "prefix_tree_attention_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload: str, phase: str):
