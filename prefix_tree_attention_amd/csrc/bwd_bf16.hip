@@ -387,13 +387,18 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
                 else
                     asm volatile("; full half" : "+v"(rlane), "+v"(tlane), "+s"(sl));
                 TREEATTN_SCHED();
-                int lo_k[2] = {0, 0}, hi_k[2] = {0, 0};
+                // the lane's visible offsets o form one interval per key,
+                // [key - q0, se[key] - q0]; bit o of vis[kk] is set for
+                // those in 0..31, so a score is kept by one sign-extended
+                // bit extract and an AND (a cleared p is +0)
+                uint32_t vis[2] = {0u, 0u};
                 if constexpr (kMasked) {
                     const int q0 = qbase + 32 * c + 4 * h;
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk) {
-                        lo_k[kk] = key[kk] - q0;
-                        hi_k[kk] = sek[kk] - q0;
+                        const int lo = max(key[kk] - q0, 0), hi = min(sek[kk] - q0, 31);
+                        const int width = hi - lo + 1;
+                        vis[kk] = width >= 32 ? ~0u : width <= 0 ? 0u : ((1u << width) - 1u) << lo;
                     }
                 }
                 auto ex = [&](int e) {
@@ -401,7 +406,14 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
                     float p = fast_exp2(sc[kk][r] * sl);
                     if constexpr (kMasked) {
                         const int o = 8 * (r / 4) + r % 4;
-                        p = (lo_k[kk] <= o && o <= hi_k[kk]) ? p : 0.f;
+                        int32_t keep = __builtin_amdgcn_sbfe(int32_t(vis[kk]), o, 1);
+                        // opaque, so the AND stays an AND instead of a
+                        // compare and select (and stays compiler-visible:
+                        // it reads a transcendental result, which needs a
+                        // wait state the compiler inserts only for its own
+                        // instructions)
+                        asm("" : "+v"(keep));
+                        p = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, p) & uint32_t(keep));
                     }
                     sc[kk][r] = p;
                     if ((e & 7) == 7) pb[kk][(e >> 3) & 1] = cvt8(sc[kk], (e >> 3) & 1);
