@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
     const int32_t* __restrict__ se, const int32_t* __restrict__ g_order, const int32_t* __restrict__ hi64,
     const int32_t* __restrict__ hdr, int L, int Hq, int Hkv, int qb_lo, int qb_hi, float scale_log2,
     float scale, const int32_t* __restrict__ pos, const float* __restrict__ rope_tab) {
-    using T = PairTile<D>;
+    using T = QuadTile<D>;
     constexpr int NX = D / 16;  // k-steps of S = Q K^T and dP = dO V^T
     constexpr int NT = D / 32;  // 32-row d-blocks of dK^T and dV^T
     constexpr int kStage = 2 * T::kBytes + 512;  // Q tile, dO tile, -LSE / scale [64], -Delta [64]
@@ -186,14 +186,14 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(
         T::load_async(ktile + q4 * T::kBytes, K + int64_t(r0) * kv_stride + hkv * D, int(kv_stride), wave, lane);
     }
     // Operand read offsets, one base per lane and pattern: the row-major
-    // read of k-step x (chunk 2 x + h of row j32) is at rlane + PS x; the
+    // read of k-step x (chunk 2 x + h of row j32) is at rlane + px(x); the
     // transposing read of d-block t (rows 4 h + 8 v + 0..3 of a 16-row
-    // k-step, elements 32 t + 16 ((lane / 16) % 2) + ..) at
-    // tlane + R8 v + 2 PS t.  Every other term is an immediate.
+    // k-step, chunk pair 2 t + (lane / 16) % 2) at tlane + R8 v + QS t.
+    // Every other term is an immediate.
     int rlane = T::rb(j32) + 16 * h;
-    int tlane = T::rb(4 * h) + T::kPs * ((lane >> 4) & 1) + 8 * tr_i;
-    auto roff = [&](int x) { return rlane + T::kPs * x; };
-    auto toff = [&](int t, int v) { return tlane + T::kR8 * v + 2 * T::kPs * t; };
+    int tlane = T::rb(4 * h) + 32 * ((lane >> 4) & 1) + T::tr_lane(tr_i);
+    auto roff = [&](int x) { return rlane + T::px(x); };
+    auto toff = [&](int t, int v) { return tlane + T::kR8 * v + T::kQs * t; };
     // dK^T, dV^T accumulators of key block kk: d-block t, register r =
     // d 32 t + 8 (r / 4) + 4 h + r % 4
     f32x16 dk[2][NT], dv[2][NT];
@@ -597,7 +597,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_bf16_kernel(
     const int32_t* __restrict__ q_order, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ row_ent,
     int L, int Hq, int Hkv, float scale_log2, float scale, const int32_t* __restrict__ pos,
     const float* __restrict__ rope_tab) {
-    using T = PairTile<D>;
+    using T = QuadTile<D>;
     constexpr int NS = D / 32, NT = D / 16;
     // K and V tiles and the keys' subtree ends, double-buffered
     __shared__ __attribute__((aligned(1024))) char smem_raw[4 * T::kBytes + 2 * 4 * kStep];
@@ -701,12 +701,12 @@ __global__ __launch_bounds__(kThreads, 2) void dq_bf16_kernel(
     wait_vm_all();
     __syncthreads();
 
-    // LDS offsets of this lane's operand reads (pair-major tiles): K and V
-    // rows 16 b + n, chunk 4 x + g, at rlane + 16-row moves + 2 PS x; K^T
+    // LDS offsets of this lane's operand reads (quad-major tiles): K and V
+    // rows 16 b + n, chunk 4 x + g, at rlane + 16-row moves + QS x; K^T
     // rows 4 g + 0..3 of each 16-row k-half, elements 16 t + 4 (n % 4) ..,
-    // at tlane + 16-row moves + PS t
-    const int rlane = T::rb(n) + 16 * (g & 1) + T::kPs * (g >> 1);
-    const int tlane = T::rb(4 * g) + 8 * n;
+    // at tlane + 16-row moves + px(t)
+    const int rlane = T::rb(n) + 16 * g;
+    const int tlane = T::rb(4 * g) + T::tr_lane(n);
     for (int st = 0; st < nsteps; ++st) {
         const int buf = st & 1;
         const int ent = row_ent[beg + (st >> 1)];
@@ -726,8 +726,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_bf16_kernel(
                 bf16x8 ak[NS], av[NS];
 #pragma unroll
                 for (int x = 0; x < NS; ++x) {
-                    ak[x] = T::frag_at(kt + b * T::kGs, rlane + 2 * T::kPs * x);
-                    av[x] = T::frag_at(vt + b * T::kGs, rlane + 2 * T::kPs * x);
+                    ak[x] = T::frag_at(kt + b * T::kGs, rlane + T::kQs * x);
+                    av[x] = T::frag_at(vt + b * T::kGs, rlane + T::kQs * x);
                 }
 #pragma unroll
                 for (int qs = 0; qs < 2; ++qs) {
@@ -774,8 +774,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_bf16_kernel(
                 elementwise(std::false_type{});
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                const bf16x8 a = join_tr(T::tr_at(kt + 2 * c * T::kGs, tlane + T::kPs * t),
-                                         T::tr_at(kt + (2 * c + 1) * T::kGs, tlane + T::kPs * t));
+                const bf16x8 a = join_tr(T::tr_at(kt + 2 * c * T::kGs, tlane + T::px(t)),
+                                         T::tr_at(kt + (2 * c + 1) * T::kGs, tlane + T::px(t)));
 #pragma unroll
                 for (int qs = 0; qs < 2; ++qs) dq[qs][t] = mfma16x16x32(a, db[qs], dq[qs][t]);
             }

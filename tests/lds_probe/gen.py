@@ -44,6 +44,7 @@ layouts = {
     'pt_1040': mk_pt([0, 1040, 2176, 3216], 4240),
     'pt_plain': mk_pt([0, 1024, 2048, 3072], 4096),
     'pt_new': mk_pt([0, 1152, 2304, 3456], 4496),
+    'quad': lambda r, c: 4208 * (r >> 4) + [0, 1056, 2112, 3168][(r >> 2) & 3] + 256 * (c >> 2) + 64 * (r & 3) + 16 * (c & 3),
 }
 def P1(L):
     return [[L(l % 32, 2 * x + l // 32) for l in range(64)] for x in range(8)]

@@ -1,17 +1,18 @@
-"""The pair-major LDS tile layout of the dK/dV and dQ kernels, from the
+"""The quad-major LDS tile layout of the dK/dV and dQ kernels, from the
 library's own layout functions (a host program built with hipcc evaluates
 them; no GPU needed):
   - the direct loads' lane -> (row, chunk) mapping and the operand reads'
-    (row, chunk) -> LDS offset formula describe the same bijection;
+    (row, chunk) -> LDS offset formula describe the same bijection, and the
+    kernels' per-lane-base-plus-immediate forms (px, tr_lane, the 8- and
+    16-row moves) land on that same formula;
   - a model of the LDS finds no bank conflict in any read pattern of the
     D = 128 kernels.  The model is the one measured on gfx950 with the
     SQ_LDS_BANK_CONFLICT counter by the single-wave probe in tests/lds_probe
-    (lane-pair and stride probes): 64 banks of 4 bytes; a b128 read served in four passes of 16
-    lanes, each the lane quads of one 32-lane half whose quad index has even
-    or odd bit parity; a b64 transposing read in two passes of 32 lanes.
-    Under it the swizzled tile of the other kernels is conflict-free too, as
-    measured, and the earlier pair-major block starts (0, 1152, 2192, 3344)
-    conflict in the row-major reads exactly as measured."""
+    (lane-pair and stride probes): 64 banks of 4 bytes; a b128 read served
+    in four passes of 16 lanes, each the lane quads of one 32-lane half
+    whose quad index has even or odd bit parity; a b64 transposing read in
+    two passes of 32 lanes.  The model reproduces the probe's results for
+    the swizzled tile and for an earlier pair-major layout."""
 
 import os
 import shutil
@@ -26,9 +27,11 @@ SOURCE = r"""
 #include <cstdio>
 #include "tile.h"
 template <int D> void dump() {
-    using T = treeattn::PairTile<D>;
-    std::printf("D %d %d %d %d %d %d\n", D, T::kPs, T::kGs, T::kR8, T::kBytes, T::kBlocks);
+    using T = treeattn::QuadTile<D>;
+    std::printf("D %d %d %d %d %d %d\n", D, T::kQs, T::kGs, T::kR8, T::kBytes, T::kBlocks);
     for (int r = 0; r < 64; ++r) std::printf("rb %d %d %d\n", D, r, T::rb(r));
+    for (int x = 0; x < D / 16; ++x) std::printf("px %d %d %d\n", D, x, T::px(x));
+    for (int i = 0; i < 16; ++i) std::printf("tr %d %d %d\n", D, i, T::tr_lane(i));
     const int stride = 4096;  // elements between consecutive rows
     for (int w = 0; w < 4; ++w)
         for (int j = 0; j < T::kBlocks; ++j)
@@ -44,6 +47,12 @@ int main() {
     return 0;
 }
 """
+
+_QUADS = ([0, 3, 5, 6], [1, 2, 4, 7])
+B128_PASSES = [[4 * q + 32 * half + i for q in quads for i in range(4)] for half in (0, 1) for quads in _QUADS]
+B64_PASSES = [range(0, 32), range(32, 64)]
+# D = 64 is not tuned: dQ's transposing read keeps a 2-way conflict
+D64_EXTRA = {"row32": 0, "row16": 0, "tr32": 0, "tr16": 8}
 
 
 @pytest.fixture(scope="module")
@@ -63,84 +72,100 @@ def layout(tmp_path_factory):
         if not f:
             continue
         D = int(f[1])
-        e = res.setdefault(D, {"rb": {}, "ld": {}})
+        e = res.setdefault(D, {"rb": {}, "px": {}, "tr": {}, "ld": {}})
         if f[0] == "D":
-            e["ps"], e["gs"], e["r8"], e["bytes"], e["blocks"] = map(int, f[2:])
-        elif f[0] == "rb":
-            e["rb"][int(f[2])] = int(f[3])
+            e["qs"], e["gs"], e["r8"], e["bytes"], e["blocks"] = map(int, f[2:])
+        elif f[0] in ("rb", "px", "tr"):
+            e[f[0]][int(f[2])] = int(f[3])
         else:
             e["ld"][int(f[2])] = (int(f[4]), int(f[5]))
     return res
 
 
-_QUADS = ([0, 3, 5, 6], [1, 2, 4, 7])
-B128_PASSES = [[4 * q + 32 * half + i for q in quads for i in range(4)] for half in (0, 1) for quads in _QUADS]
-B64_PASSES = [range(0, 32), range(32, 64)]
-# the D = 64 layout is not tuned: 2-way conflicts in three patterns
-D64_DEGREES = {"row32": 2, "row16": 2, "tr32": 2, "tr16": 1}
+def _cell(e, r, c):
+    """LDS offset of (row, 16-byte chunk) in the quad-major layout."""
+    return e["rb"][r] + 16 * (c & 3) + e["qs"] * (c >> 2)
 
 
-def _degree(addrs, passes):
-    """Largest number of different 4-byte words one bank serves in a pass."""
-    worst = 1
+def _extra(offs, passes, width):
+    """Extra LDS cycles of one read: per pass, the most different 4-byte
+    words one bank serves, minus one."""
+    tot = 0
     for p in passes:
         banks = {}
         for lane in p:
-            for a in addrs[lane]:
-                banks.setdefault((a // 4) % 64, set()).add(a // 4)
-        worst = max(worst, max(len(v) for v in banks.values()))
-    return worst
+            for w in range(width // 4):
+                word = offs[lane] // 4 + w
+                banks.setdefault(word % 64, set()).add(word)
+        tot += max(len(v) for v in banks.values()) - 1
+    return tot
+
+
+def _patterns(L, D):
+    """The kernels' operand reads as per-lane offset lists, by pattern."""
+    def tr(r, e):
+        return L(r, e >> 3) + 2 * (e & 7)
+    return {
+        # 32x32x16 rows (lane: row l % 32, chunk 2x + l / 32)
+        "row32": [[L(l % 32, 2 * x + l // 32) for l in range(64)] for x in range(D // 16)],
+        # 16x16x32 rows (lane: row l % 16, chunk 4x + l / 16)
+        "row16": [[L(16 * b + l % 16, 4 * x + l // 16) for l in range(64)] for b in range(2) for x in range(D // 32)],
+        # dK/dV and forward transposing reads: rows 4 (l / 32) + 8v + (l % 16) / 4, elements 32t + 16 ((l / 16) % 2) + ..
+        "tr32": [[tr(4 * (l // 32) + 8 * v + (l % 16) // 4, 32 * t + 16 * ((l // 16) % 2) + 4 * (l % 4)) for l in range(64)]
+                 for t in range(D // 32) for v in range(2)],
+        # dQ transposing reads: rows 4 (l / 16) + (l % 16) / 4, elements 16t + ..
+        "tr16": [[tr(4 * (l // 16) + (l % 16) // 4, 16 * t + 4 * (l % 4)) for l in range(64)] for t in range(D // 16)],
+    }
+
+
+def _pattern_extra(L, D):
+    return {k: sum(_extra(o, B128_PASSES if k.startswith("row") else B64_PASSES, 16 if k.startswith("row") else 8)
+                   for o in offs) for k, offs in _patterns(L, D).items()}
 
 
 @pytest.mark.parametrize("D", [128, 64])
 def test_loads_and_reads_agree(layout, D):
     e = layout[D]
-    rb, ps = e["rb"], e["ps"]
     read = {}
     for r in range(64):
         for c in range(D // 8):
-            a = rb[r] + 16 * (c & 1) + ps * (c >> 1)
+            a = _cell(e, r, c)
             assert a % 16 == 0 and 0 <= a and a + 16 <= e["bytes"]
             read[a] = (r, c)
     assert len(read) == 64 * D // 8  # a bijection onto distinct 16-byte slots
     assert e["ld"] == read  # each load lane fills exactly the slot the reads expect
-    # 8-row and 16-row moves are the constants the kernels add
+    rb = e["rb"]
     for r in range(64):
         if r % 16 < 8:
             assert rb[r + 8] - rb[r] == e["r8"]
         if r < 48:
             assert rb[r + 16] - rb[r] == e["gs"]
+        for x in range(D // 16):
+            for h in range(2):  # row-major read: base + 16 h + px(x)
+                assert rb[r] + 16 * h + e["px"][x] == _cell(e, r, 2 * x + h)
+    for r0 in range(0, 64, 4):  # transposing read: base + px(x) + tr_lane(i)
+        for x in range(D // 16):
+            for i in range(16):
+                el = 16 * x + 4 * (i % 4)
+                assert rb[r0] + e["px"][x] + e["tr"][i] == _cell(e, r0 + i // 4, el >> 3) + 2 * (el & 7)
 
 
 @pytest.mark.parametrize("D", [128, 64])
 def test_bank_conflicts(layout, D):
     e = layout[D]
-    rb, ps = e["rb"], e["ps"]
-    b128, b64 = B128_PASSES, B64_PASSES
-    deg = {}
-    # 32x32x16 operand rows (lane: row l % 32, chunk 2x + l / 32)
-    deg["row32"] = max(_degree([[rb[l % 32] + 16 * (l // 32) + ps * x + k for k in (0, 4, 8, 12)] for l in range(64)],
-                               b128) for x in range(D // 16))
-    # 16x16x32 operand rows (lane: row l % 16, chunk 4x + l / 16)
-    deg["row16"] = max(_degree([[rb[l % 16] + 16 * ((l // 16) & 1) + ps * (2 * x + l // 32) + k for k in (0, 4, 8, 12)]
-                                for l in range(64)], b128) for x in range(D // 32))
-    # dK/dV transposing reads: group l / 16 takes rows 4 (l / 32) + 8 v + 0..3, chunk pair 2t + (l / 16) % 2
-    deg["tr32"] = max(_degree([[rb[4 * (l // 32) + 8 * v] + ps * (2 * t + ((l >> 4) & 1)) + 8 * (l & 15) + k
-                                for k in (0, 4)] for l in range(64)], b64) for t in range(D // 32) for v in range(2))
-    # dQ transposing reads: group g = l / 16 takes rows 4g + 0..3, chunk pair t
-    deg["tr16"] = max(_degree([[rb[4 * (l // 16)] + ps * t + 8 * (l & 15) + k for k in (0, 4)] for l in range(64)], b64)
-                      for t in range(D // 16))
+    extra = _pattern_extra(lambda r, c: _cell(e, r, c), D)
     if D == 128:
-        assert deg == {"row32": 1, "row16": 1, "tr32": 1, "tr16": 1}
+        assert extra == {"row32": 0, "row16": 0, "tr32": 0, "tr16": 0}
     else:  # not tuned; pinned so that a change is seen
-        assert deg == D64_DEGREES
+        assert extra == D64_EXTRA
 
 
 def test_model_matches_measured_layouts():
-    """The pass model reproduces the probe's measurements: no extra cycles
-    for the swizzled tile; for the earlier pair-major block starts, 4 extra
-    cycles per row-major read (a 2-way conflict in each of its 4 passes, 32
-    over a pattern's 8 reads) and none in the transposing reads."""
+    """The pass model reproduces the probe's measurements
+    (profiles/lds_bank_probe_gfx950.md, conflict cycles over 16 repetitions
+    of a pattern's 8 reads): none for the swizzled tile; for the pair-major
+    blocks at 0/1152/2192/3344 with a 4368-byte group, 512 cycles in each
+    row-major pattern and none in the transposing ones."""
     def swz(r):
         return ((r & 3) << 2 | (r & 4) >> 1) ^ (3 * ((r >> 3) & 1))
 
@@ -151,23 +176,6 @@ def test_model_matches_measured_layouts():
         bb = [0, 1152, 2192, 3344]
         return 4368 * (r >> 4) + bb[(r >> 2) & 3] + 32 * (r & 3) + 16 * (c & 1) + 128 * (c >> 1)
 
-    def extra(offs, passes, width):
-        tot = 0
-        for p in passes:
-            banks = {}
-            for lane in p:
-                for w in range(width // 4):
-                    word = offs[lane] // 4 + w
-                    banks.setdefault(word % 64, set()).add(word)
-            tot += max(len(v) for v in banks.values()) - 1
-        return tot
-
-    def row32(L):
-        return sum(extra([L(l % 32, 2 * x + l // 32) for l in range(64)], B128_PASSES, 16) for x in range(8))
-
-    def tr32(L):
-        return sum(extra([L(4 * (l // 32) + 8 * v + (l % 16) // 4, (32 * t + 16 * ((l // 16) % 2) + 4 * (l % 4)) >> 3)
-                          + 2 * ((4 * (l % 4)) & 7) for l in range(64)], B64_PASSES, 8) for t in range(4) for v in range(2))
-
-    assert (row32(xor_tile), tr32(xor_tile)) == (0, 0)
-    assert (row32(old_pair), tr32(old_pair)) == (32, 0)
+    assert {k: 16 * v for k, v in _pattern_extra(xor_tile, 128).items()} == {"row32": 0, "row16": 0, "tr32": 0, "tr16": 0}
+    assert {k: 16 * v for k, v in _pattern_extra(old_pair, 128).items()} == {"row32": 512, "row16": 512, "tr32": 0,
+                                                                               "tr16": 0}
