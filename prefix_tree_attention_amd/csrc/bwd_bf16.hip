@@ -22,7 +22,7 @@
 //          in LDS.  It walks the group's 64-query steps for each query head
 //          of the key/value head;
 //          Q and dO (and -LSE / scale, -Delta) of a step go HBM -> LDS by
-//          direct loads into double-buffered swizzled tiles.
+//          direct loads into double-buffered quad-major tiles (tile.h).
 //            S = Q K^T, dP = dO V^T      (A = Q / dO rows of the tiles)
 //            dV^T += dO^T P, dK^T += Q^T dS
 //          (A = dO^T / Q^T by transposing LDS reads of the same tiles,

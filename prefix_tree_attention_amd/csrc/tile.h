@@ -1,27 +1,28 @@
 // Internal: 64-row LDS tiles for the gfx950 attention kernels.
 //
-// A tile holds 64 consecutive tokens x D bf16 of one head, in natural row
-// order, as 16-byte chunks (D/8 per row).  It is filled straight from HBM by
-// global_load_lds_dwordx4 (each lane's 16 bytes land at the instruction's
-// LDS base + 16 * lane), so staging costs no registers and no LDS store
-// instructions.  Chunk c of row r sits at slot position c ^ swz(r) within
-// the row.  The kernels read a tile in two patterns:
-//   - row-major operand reads (ds_read_b128): 16 lanes read one chunk
-//     column of 16 consecutive rows, the 4 lane groups 4 adjacent chunks;
+// A tile holds 64 consecutive tokens x D bf16 of one head as 16-byte chunks
+// (D/8 per row).  It is filled straight from HBM by global_load_lds_dwordx4
+// (each lane's 16 bytes land at the instruction's LDS base + 16 * lane), so
+// staging costs no registers and no LDS store instructions; which chunk a
+// lane fetches decides the layout.  The kernels read a tile in two patterns:
+//   - row-major operand reads (ds_read_b128): each lane 16 bytes of its row;
 //   - transposed operand reads (ds_read_b64_tr_b16): a 16-lane group reads
 //     4 consecutive rows x 16 consecutive elements, and lane i of the group
 //     receives element i of each of the 4 rows -- i.e. an MFMA operand
-//     fragment whose k index runs over rows.  32 lanes (8 rows, two
-//     adjacent chunks) are served together by the 64 banks.
-// The swizzle is the GF(2)-linear map of the row's low 4 bits that measured
-// fastest for both patterns together on gfx950 (every invertible map was
-// timed): for D = 128 (16 chunks per 256-byte row)
-//   swz(r) = (4 (r % 4) + 2 ((r / 4) % 2)) ^ 3 ((r / 8) % 2),
-// for D = 64 (8 chunks per 128-byte row)
-//   swz(r) = (r % 8) ^ 2 ((r / 8) % 2).
-// Row-major reads then run at ~208 B/clk/CU (contiguous b128 reads: ~192)
-// and transposed reads at ~114 B/clk/CU, near the b64 instruction-rate
-// ceiling (~123); the LDS issues about one wave-wide read per 4.5 clocks.
+//     fragment whose k index runs over rows.
+// Two layouts:
+//   - Tile (the forward's): natural row order, chunk c of row r at slot
+//     position c ^ swz(r) within the row, with the GF(2)-linear swizzle of
+//     the row's low 4 bits that measured fastest for both patterns together
+//     (every invertible map was timed): for D = 128 (16 chunks per 256-byte
+//     row) swz(r) = (4 (r % 4) + 2 ((r / 4) % 2)) ^ 3 ((r / 8) % 2), for
+//     D = 64 (8 chunks per 128-byte row) swz(r) = (r % 8) ^ 2 ((r / 8) % 2).
+//     Its reads are free of bank conflicts (SQ_LDS_BANK_CONFLICT reads 0);
+//     each lane's offsets are loop-invariant registers.
+//   - QuadTile (dK/dV and dQ, below): quad-major blocks in which every
+//     operand read is one per-lane base plus an immediate, also free of
+//     bank conflicts under the LDS's measured pass structure.
+// The LDS issues about one wave-wide read per 4.5 clocks whatever its width.
 #pragma once
 
 #include <hip/hip_runtime.h>
