@@ -159,10 +159,10 @@ struct Tile {
 // pass the lane quads (4 lanes) of one 32-lane half whose quad index has
 // even (0, 3, 5, 6) or odd (1, 2, 4, 7) bit parity; a ds_read_b64_tr_b16
 // in two passes, lanes 0-31 and 32-63.  For D = 128 the blocks of a 16-row
-// group start at 0, 1056, 2112 and 3168 bytes (4-word offsets 0, 2, 0, 2
-// mod 4 in 16-byte slots) and a group is 4208 bytes (an odd slot count mod
-// 4): under that pass structure the row-major reads of the 32x32x16 and
-// 16x16x32 operand layouts and the transposing reads of both kernels are
+// group start at 0, 1056, 2112 and 3168 bytes (16-byte slots 0, 66, 132,
+// 198: 0, 2, 0, 2 mod 4) and a group is 4208 bytes (263 slots, odd): under
+// that pass structure the row-major reads of the 32x32x16 and 16x16x32
+// operand layouts and the transposing reads of both kernels are
 // conflict-free.  For D = 64 (blocks at 0 and 1056 of a 2096-byte group)
 // only dQ's transposing read keeps a 2-way conflict.
 template <int D>
