@@ -39,6 +39,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -109,13 +110,22 @@ def copy_calibration():
 KERNEL_HEADERS = ("device.h", "mfma.h", "tile.h")
 
 
+def _code_only(text: str) -> str:
+    """C++ source with comments removed and whitespace runs collapsed (string
+    literals in these sources hold no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_sha(name: str) -> str:
-    """Hash of a kernel source and the device headers it compiles in: a
-    traffic summary counts only while none of them has changed."""
+    """Hash of the code of a kernel source and of the device headers it
+    compiles in (comments and layout ignored): a traffic summary counts only
+    while none of them has changed."""
     h = hashlib.sha256()
     for n in (name, *KERNEL_HEADERS):
-        with open(os.path.join(ROOT, "prefix_tree_attention_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "prefix_tree_attention_amd", "csrc", n)) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
