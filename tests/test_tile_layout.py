@@ -179,3 +179,21 @@ def test_model_matches_measured_layouts():
     assert {k: 16 * v for k, v in _pattern_extra(xor_tile, 128).items()} == {"row32": 0, "row16": 0, "tr32": 0, "tr16": 0}
     assert {k: 16 * v for k, v in _pattern_extra(old_pair, 128).items()} == {"row32": 512, "row16": 512, "tr32": 0,
                                                                                "tr16": 0}
+
+
+def test_lds_probe_builds(tmp_path):
+    """The probe whose measurements the model above reproduces stays
+    buildable: its test table generates (every offset in range and aligned,
+    as the generator asserts) and its source compiles for gfx950."""
+    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    if not os.path.exists(hipcc) and shutil.which("hipcc") is None:
+        pytest.skip("hipcc not available")
+    probe = os.path.join(ROOT, "tests", "lds_probe")
+    subprocess.run(["python3", os.path.join(probe, "gen.py"), str(tmp_path / "t.txt"), str(tmp_path / "l.json")],
+                   check=True, capture_output=True)
+    first = (tmp_path / "t.txt").read_text().split("\n", 1)[0]
+    assert int(first) > 100
+    subprocess.run([hipcc if os.path.exists(hipcc) else "hipcc", "-O3", "--offload-arch=gfx950", "-Xclang",
+                    "-target-feature", "-Xclang", "-packed-fp32-ops", "-o", str(tmp_path / "probe"),
+                    os.path.join(probe, "probe.hip")], check=True, capture_output=True)
+    assert (tmp_path / "probe").exists()
